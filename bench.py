@@ -1,0 +1,418 @@
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+
+Headline (one JSON line on stdout): MoE decode tokens/s for batch 1 through
+48 stacked layers shaped like the pages' model (512 experts per layer, top-10
+plus one shared expert, d_model 2048, d_ff 768, every expert resident,
+2-bit scale+min blocks at 3.0 bits per weight).  A step is one token through
+all 48 layers: router top-k, cache lookup and the decode FFN with its
+routing-weighted combine, layer by layer, with fresh router logits for every
+token and layer.  Inputs are seeded synthetic tensors, resident in HBM
+before timing starts.  Steps are replayed from HIP graphs.
+
+Extra objects on the same line: the decode kernel's roofline (HBM), the
+expert-cache workload (94 of 512 experts resident, about 72% hits), the
+1+3-token verify step, the 8,192-token prefill chunk with its GEMMs' MFMA
+roofline, and the CPU oracle timed on a bounded sample of the decode
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+N_LAYERS = 48
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--graphs", type=int, default=16, help="distinct token graphs replayed in turn")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=2)
+    return ap.parse_args()
+
+
+def build_pools(torch, synth, cfg, fmt_of_layer, dev, n_layers=N_LAYERS, resident=None):
+    """Packed pools of n_layers layers on the device; returns list of
+    (pool, slot_of_expert (device int32), shared_slot)."""
+    shape = synth.config_shape(cfg)
+    E = shape.n_experts
+    out = []
+    for l in range(n_layers):
+        fmt = fmt_of_layer(l)
+        table, shared_slot, slot_expert = synth.make_slot_table(cfg, l)
+        pool = synth.make_layer_pool(cfg, l, slot_expert, device=dev, fmt=fmt, batch=64)
+        out.append((pool, torch.tensor(table, dtype=torch.int32, device=dev), shared_slot, fmt))
+    return out
+
+
+class DecodeChain:
+    """48 layers of decode for T tokens, with preallocated buffers, so that a
+    whole step can be captured in a graph."""
+
+    def __init__(self, torch, bf, shape, pools, T, dev):
+        self.torch, self.bf = torch, bf
+        self.T = T
+        self.layers = [bf.MoeLayer(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k, fmt,
+                                   pool, shared_slot) for pool, _, shared_slot, fmt in pools]
+        self.tables = [t for _, t, _, _ in pools]
+        k, E, d = shape.top_k, shape.n_experts, shape.d_model
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.slot = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.miss_e = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        self.miss_p = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        self.n_miss = torch.empty((4,), dtype=torch.int32, device=dev)
+        ws = max(bf.decode_workspace_bytes(L, T) for L in self.layers)
+        self.ws = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        self.x = [torch.empty((T, d), dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def step(self, logits, ffn_events=None):
+        """logits [n_layers, T, E]; result in self.x[n_layers % 2]."""
+        bf = self.bf
+        for l, L in enumerate(self.layers):
+            xin, yout = self.x[l % 2], self.x[(l + 1) % 2]
+            bf.route_topk(logits[l], L.top_k, idx=self.idx, w=self.w)
+            bf.cache_lookup(self.idx, self.tables[l], slot=self.slot, miss_expert=self.miss_e,
+                            miss_pair=self.miss_p, n_miss=self.n_miss)
+            if ffn_events is not None:
+                ffn_events[l][0].record()
+            bf.expert_ffn_decode(L, xin, self.idx, self.slot, self.w, y=yout, ws=self.ws)
+            if ffn_events is not None:
+                ffn_events[l][1].record()
+        return self.x[len(self.layers) % 2]
+
+
+def time_graph_steps(torch, chain, logits_sets, x0, steps, warmup, n_graphs):
+    """Capture n_graphs token steps (each its own logits) and replay them."""
+    graphs = []
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for g in range(min(3, n_graphs)):       # warm the allocator and the code paths
+            chain.x[0].copy_(x0)
+            chain.step(logits_sets[g])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for g in range(n_graphs):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            chain.step(logits_sets[g])
+        graphs.append(graph)
+    torch.cuda.synchronize()
+    chain.x[0].copy_(x0)
+    for i in range(warmup):
+        graphs[i % n_graphs].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % n_graphs].replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    return dt, graphs
+
+
+def time_ffn_kernel(torch, chain, logits_sets, x0, reps):
+    """Average duration of the decode FFN call (its own launches), measured
+    with events on the stream it runs on, eager launches."""
+    n = len(chain.layers)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)] for _ in range(reps)]
+    chain.x[0].copy_(x0)
+    chain.step(logits_sets[0])
+    torch.cuda.synchronize()
+    for r in range(reps):
+        chain.step(logits_sets[r % len(logits_sets)], ffn_events=evs[r])
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for rep in evs for a, b in rep]
+    return sum(ms) / len(ms)
+
+
+def decode_bytes_per_call(synth, shape, fmt, T, n_union):
+    """Algorithmic bytes of one decode FFN call: the packed bytes of every
+    distinct resident expert chosen (plus the shared one) read once, x read,
+    y written."""
+    sb = synth.slot_bytes(fmt, shape.d_model, shape.d_ff)
+    return n_union * sb + 2 * T * shape.d_model * 4
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import bit_expert_ffn_top_amd as bf
+    import synth
+
+    bf.lib()
+    dev = torch.device("cuda:0")
+    shape = synth.config_shape(1)
+    E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
+    t_gen = time.perf_counter()
+    pools = build_pools(torch, synth, 1, lambda l: synth.FMT_Q2SM, dev)
+    torch.cuda.synchronize()
+    log(f"decode pools: {N_LAYERS} layers x {E + 1} experts in {time.perf_counter() - t_gen:.1f} s")
+
+    # ---------------- decode, config 1 (headline) ----------------
+    chain = DecodeChain(torch, bf, shape, pools, 1, dev)
+    n_graphs = args.graphs
+    logits_sets = [torch.stack([synth.make_logits(1, l, 1, E, 1.5, device=dev, step=g)
+                                for l in range(N_LAYERS)]) for g in range(n_graphs)]
+    x0 = synth.make_x(1, 0, 1, d, device=dev)
+    dt, graphs = time_graph_steps(torch, chain, logits_sets, x0, args.steps, args.warmup, n_graphs)
+    tok_s = args.steps / dt
+    ms_step = dt * 1e3 / args.steps
+    log(f"decode: {tok_s:.1f} tok/s, {ms_step * 1e3:.1f} us/token ({ms_step * 1e3 / N_LAYERS:.2f} us/layer)")
+    del graphs
+    ffn_ms = time_ffn_kernel(torch, chain, logits_sets, x0, reps=4)
+    bytes_call = decode_bytes_per_call(synth, shape, synth.FMT_Q2SM, 1, k + 1)
+    ach = bytes_call / (ffn_ms * 1e-3) / 1e9
+    log(f"decode FFN call: {ffn_ms * 1e3:.2f} us avg, {ach:.0f} GB/s algorithmic")
+    token_bytes = N_LAYERS * bytes_call
+    result = {
+        "metric": "MoE decode tok/s (48 layers, bs=1)",
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (2-bit scale+min weight blocks)",
+        "data": "synthetic (seeded; weights ~N(0,0.02) block-quantized, x ~N(0,1), logits ~N(0,1.5) fresh per token and layer)",
+        "config": {
+            "workload": "decode, batch 1, 48 stacked MoE layers: E=512 routed (top-10) + 1 shared expert, "
+                        "d_model=2048, d_ff=768, all experts resident under a seeded slot permutation, "
+                        "Q2SM blocks (3.0 bits/weight)",
+            "tokens_per_step": 1, "layers": N_LAYERS, "experts_per_layer": E, "top_k": k,
+            "shared_experts": 1, "d_model": d, "d_ff": f, "format": "Q2SM",
+        },
+        "token_hbm_bytes_algorithmic": token_bytes,
+        "token_hbm_GBps_algorithmic": round(token_bytes * tok_s / 1e9, 1),
+        "token_frac_of_hbm_peak": round(token_bytes * tok_s / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "kernel": "moe_expert_ffn_decode (one call per layer)",
+            "bound": "hbm",
+            "achieved": round(ach, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_call_us": round(ffn_ms * 1e3, 3),
+            "bytes_per_call": bytes_call,
+        },
+    }
+
+    extra = {}
+    if not args.no_extra:
+        extra.update(run_extras(torch, np, bf, synth, pools, dev, args))
+    result.update(extra)
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(np, synth, pools, shape)
+    print(json.dumps(result), flush=True)
+
+
+def run_extras(torch, np, bf, synth, pools, dev, args):
+    out = {}
+    shape = synth.config_shape(1)
+    E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
+
+    # ---------------- expert-cache workload, config 2 ----------------
+    t0 = time.perf_counter()
+    c2 = synth.CONFIGS[2]
+    pools2 = build_pools(torch, synth, 2, lambda l: synth.FMT_Q2SM, dev)
+    chain2 = DecodeChain(torch, bf, shape, pools2, 1, dev)
+    n_graphs = min(args.graphs, 8)
+    logits2 = [torch.stack([synth.zipf_gumbel_logits(2, l, 1, E, c2["zipf_s"], device=dev, step=g)
+                            for l in range(N_LAYERS)]) for g in range(n_graphs)]
+    x0 = synth.make_x(2, 0, 1, d, device=dev)
+    steps2 = max(20, args.steps // 2)
+    dt, graphs = time_graph_steps(torch, chain2, logits2, x0, steps2, 5, n_graphs)
+    del graphs
+    hits = tot = 0
+    for g in range(n_graphs):
+        for l in range(N_LAYERS):
+            idx = np.argsort(-logits2[g][l].cpu().numpy(), axis=1, kind="stable")[:, :k]
+            tab = pools2[l][1].cpu().numpy()
+            hits += int((tab[idx] >= 0).sum())
+            tot += idx.size
+    out["expert_cache"] = {
+        "workload": "decode batch 1, 48 stacked layers, 94 of 512 experts + shared resident per layer, "
+                    "Zipf(1.1) routing; GPU computes the resident part and emits the miss list",
+        "tok_s": round(steps2 / dt, 2), "ms_per_step": round(dt * 1e3 / steps2, 5),
+        "hit_rate": round(hits / tot, 4),
+    }
+    log(f"expert cache: {steps2 / dt:.1f} tok/s, hit rate {hits / tot:.3f} ({time.perf_counter() - t0:.1f} s)")
+    del pools2, chain2, logits2
+    torch.cuda.empty_cache()
+
+    # ---------------- verify step, config 3 ----------------
+    t0 = time.perf_counter()
+    pools3 = []
+    for l in range(N_LAYERS):
+        if l % 2 == 0:
+            pools3.append(pools[l])       # Q2SM layers shared with the decode workload
+        else:
+            table, shared_slot, slot_expert = synth.make_slot_table(3, l)
+            pool = synth.make_layer_pool(3, l, slot_expert, device=dev, fmt=synth.FMT_Q3G, batch=64)
+            pools3.append((pool, torch.tensor(table, dtype=torch.int32, device=dev), shared_slot,
+                           synth.FMT_Q3G))
+    chain3 = DecodeChain(torch, bf, shape, pools3, 4, dev)
+    logits3 = [torch.stack([synth.make_logits(3, l, 4, E, 1.5, device=dev, step=g)
+                            for l in range(N_LAYERS)]) for g in range(n_graphs)]
+    x0 = synth.make_x(3, 0, 4, d, device=dev)
+    steps3 = max(20, args.steps // 2)
+    dt, graphs = time_graph_steps(torch, chain3, logits3, x0, steps3, 5, n_graphs)
+    del graphs
+    union = []
+    for g in range(n_graphs):
+        for l in range(N_LAYERS):
+            idx = np.argsort(-logits3[g][l].cpu().numpy(), axis=1, kind="stable")[:, :k]
+            union.append(len(set(idx.reshape(-1).tolist())) + 1)
+    sb2 = synth.slot_bytes(synth.FMT_Q2SM, d, f)
+    sb3 = synth.slot_bytes(synth.FMT_Q3G, d, f)
+    mean_u = float(np.mean(union))
+    step_bytes = sum(mean_u * (sb2 if l % 2 == 0 else sb3) for l in range(N_LAYERS))
+    sps = steps3 / dt
+    out["verify"] = {
+        "workload": "verify step: 1 real + 3 draft tokens routed independently through 48 layers "
+                    "alternating Q2SM / Q3G; each distinct chosen expert read once per step",
+        "steps_per_s": round(sps, 2), "token_positions_per_s": round(4 * sps, 2),
+        "ms_per_step": round(dt * 1e3 / steps3, 5), "mean_union_experts": round(mean_u, 2),
+        "hbm_GBps_algorithmic": round(step_bytes * sps / 1e9, 1),
+        "frac_of_hbm_peak": round(step_bytes * sps / 1e9 / HBM_PEAK_GBS, 4),
+    }
+    log(f"verify: {sps:.1f} steps/s, union {mean_u:.2f} ({time.perf_counter() - t0:.1f} s)")
+    del pools3, chain3, logits3
+    torch.cuda.empty_cache()
+
+    # ---------------- prefill chunk, config 4 ----------------
+    out["prefill"] = run_prefill(torch, np, bf, synth, pools, dev, args)
+    return out
+
+
+def run_prefill(torch, np, bf, synth, pools, dev, args):
+    shape = synth.config_shape(4)
+    E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
+    T = synth.CONFIGS[4]["T"]
+    layers = [bf.MoeLayer(d, f, E, k, fmt, pool, shared_slot)
+              for pool, _, shared_slot, fmt in pools]
+    tables = [t for _, t, _, _ in pools]
+    xs = [synth.make_x(4, l, T, d, device=dev, dtype=torch.bfloat16) for l in range(N_LAYERS)]
+    logits = [synth.make_logits(4, l, T, E, 1.5, device=dev) for l in range(N_LAYERS)]
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    slot = torch.empty((T, k), dtype=torch.int32, device=dev)
+    me = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    n_miss = torch.empty((4,), dtype=torch.int32, device=dev)
+    lws = torch.empty((max(bf.lookup_workspace_bytes(T, k, E), 256),), dtype=torch.uint8, device=dev)
+    out_pairs = torch.empty((T * k, d), dtype=torch.float32, device=dev)
+    pair_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
+    offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    out_sh = torch.empty((T, d), dtype=torch.float32, device=dev)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    pws = torch.empty((bf.prefill_workspace_bytes(layers[0], T),), dtype=torch.uint8, device=dev)
+
+    def one_step(events=None):
+        for l, L in enumerate(layers):
+            bf.route_topk(logits[l], k, idx=idx, w=w)
+            bf.cache_lookup(idx, tables[l], slot=slot, miss_expert=me, n_miss=n_miss, ws=lws,
+                            want_pairs=False)
+            if events is not None:
+                events[l][0].record()
+            bf.expert_ffn_prefill(L, xs[l], idx, slot, out_pairs=out_pairs, pair_pos=pair_pos,
+                                  expert_offsets=offs, out_shared=out_sh, ws=pws)
+            if events is not None:
+                events[l][1].record()
+            bf.combine(xs[l], out_pairs, pair_pos, w, out_sh, y=y)
+
+    one_step()
+    torch.cuda.synchronize()
+    steps = args.prefill_steps
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(N_LAYERS)]
+    one_step(evs)
+    torch.cuda.synchronize()
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flops = 2 * 3 * d * f * T * (k + 1)
+    tflops = flops / (call_ms * 1e-3) / 1e12
+    toks = steps * T / dt
+    log(f"prefill: {toks:.0f} tok/s (48 layers), prefill call {call_ms:.3f} ms, {tflops:.1f} TFLOP/s")
+    return {
+        "workload": "prefill chunk: 8,192 bf16 tokens, top-10 + shared, 48 independent layers of the decode shape (Q2SM)",
+        "tok_s": round(toks, 1),
+        "ms_per_layer": round(dt * 1e3 / steps / N_LAYERS, 4),
+        "roofline": {
+            "kernel": "moe_expert_ffn_prefill (grouping + gate/up + down GEMMs)",
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "avg_call_ms": round(call_ms, 4), "flops_per_call": flops,
+        },
+    }
+
+
+def cpu_baseline(np, synth, pools, shape):
+    """The oracle on this host's cores: decode of one token through a sample
+    of the layers, scaled to the 48-layer token."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
+    n_sample = 3
+    x = synth.make_x(1, 0, 1, d).double().numpy()
+    inputs = []
+    for l in range(n_sample):          # device -> host copies stay outside the timing
+        pool, table_dev, shared_slot, fmt = pools[l]
+        table = table_dev.cpu().numpy()
+        logits = synth.make_logits(1, l, 1, E, 1.5).numpy()
+        host = {s: pool[s].cpu().numpy() for s in range(pool.shape[0])
+                if s == shared_slot or s in set(table[np.argsort(-logits[0])[:k]].tolist())}
+        inputs.append((logits, table, host, shared_slot, fmt))
+    t0 = time.perf_counter()
+    for logits, table, host, shared_slot, fmt in inputs:
+        idx, w = oracle.route_topk(logits, k)
+        slot, _, _, _ = oracle.cache_lookup(idx, table)
+        x = oracle.layer_decode(x, idx, slot, w,
+                                lambda s: oracle.unpack_expert(host[s], fmt, d, f), shared_slot)
+    dt = time.perf_counter() - t0
+    per_token = dt / n_sample * N_LAYERS
+    return {"value": round(1.0 / per_token, 5), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, {n_sample} of the 48 decode layers for one token "
+                      f"(unpack of the 11 chosen slots + FFN + combine), scaled x{N_LAYERS // n_sample}",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

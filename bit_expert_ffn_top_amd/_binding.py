@@ -1,0 +1,250 @@
+"""ctypes binding of libbitffn_moe.so (include/bitffn_moe.h).
+
+Argument marshalling only: tensors are checked for device, dtype and shape,
+their data pointers and the current HIP stream are passed to the C ABI, and
+any output tensor the caller did not supply is allocated with torch.  Every
+step of the computation runs in the library's kernels.  There is no fallback:
+if the library cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+LIB_NAME = "libbitffn_moe.so"
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EFORMAT, MOE_ENOSPC, MOE_EHIP = 0, -1, -2, -3, -4, -5
+FMT_Q2S, FMT_Q2SM, FMT_Q3G = 1, 2, 3
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+# every symbol the header declares, with its ctypes signature
+_c_int, _c_i64, _c_sz, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+
+class MoeLayerC(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("fmt", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+        ("shared_slot", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("slot_bytes", ctypes.c_int64), ("pool", ctypes.c_void_p),
+    ]
+
+
+_LP = ctypes.POINTER(MoeLayerC)
+SIGNATURES = {
+    "moe_abi_version": (_c_int, []),
+    "moe_status_str": (ctypes.c_char_p, [_c_int]),
+    "moe_last_hip_error": (_c_int, []),
+    "moe_slot_bytes": (_c_i64, [_c_int, _c_int, _c_int]),
+    "moe_route_topk": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
+    "moe_lookup_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
+    "moe_cache_lookup": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
+                                  _c_sz, _vp]),
+    "moe_decode_workspace_bytes": (_c_sz, [_LP, _c_int]),
+    "moe_expert_ffn_decode": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
+    "moe_prefill_workspace_bytes": (_c_sz, [_LP, _c_int]),
+    "moe_expert_ffn_prefill": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _c_sz, _vp]),
+    "moe_combine": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp]),
+}
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_NAME} is not built; run `python -m bit_expert_ffn_top_amd.build`")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = lib().moe_status_str(status).decode()
+        if status == MOE_EHIP:
+            msg += f" (hip error {lib().moe_last_hip_error()})"
+        super().__init__(f"{what}: {msg} [{status}]")
+        self.status = status
+
+
+def _check(status: int, what: str):
+    if status != MOE_OK:
+        raise MoeError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+@dataclasses.dataclass
+class MoeLayer:
+    """One layer's packed expert pool in device memory."""
+    d_model: int
+    d_ff: int
+    n_experts: int
+    top_k: int
+    fmt: int
+    pool: torch.Tensor            # uint8 [n_slots, slot_bytes] on the device
+    shared_slot: int = -1
+
+    def c_struct(self) -> MoeLayerC:
+        _dev(self.pool, torch.uint8, "pool")
+        n_slots, sb = self.pool.shape
+        return MoeLayerC(self.d_model, self.d_ff, self.n_experts, self.top_k, self.fmt,
+                         n_slots, self.shared_slot, 0, sb, self.pool.data_ptr())
+
+
+def abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def slot_bytes(fmt: int, d_model: int, d_ff: int) -> int:
+    v = lib().moe_slot_bytes(fmt, d_model, d_ff)
+    _check(int(v) if v < 0 else 0, "moe_slot_bytes")
+    return int(v)
+
+
+def route_topk(logits: torch.Tensor, k: int, idx=None, w=None, stream=None):
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    if idx is None:
+        idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_route_topk(_ptr(logits), T, E, k, _ptr(idx), _ptr(w), _stream(stream)),
+           "moe_route_topk")
+    return idx, w
+
+
+def lookup_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(lib().moe_lookup_workspace_bytes(T, k, E))
+
+
+def cache_lookup(idx: torch.Tensor, slot_of_expert: torch.Tensor, slot=None, miss_expert=None,
+                 miss_pair=None, n_miss=None, ws=None, want_pairs=True, stream=None):
+    _dev(idx, torch.int32, "idx")
+    _dev(slot_of_expert, torch.int32, "slot_of_expert")
+    T, k = idx.shape
+    E = slot_of_expert.shape[0]
+    dev = idx.device
+    n = T * k
+    slot = torch.empty((T, k), dtype=torch.int32, device=dev) if slot is None else slot
+    miss_expert = torch.full((max(n, 1),), -1, dtype=torch.int32, device=dev) if miss_expert is None else miss_expert
+    if want_pairs and miss_pair is None:
+        miss_pair = torch.full((max(n, 1),), -1, dtype=torch.int32, device=dev)
+    n_miss = torch.zeros((4,), dtype=torch.int32, device=dev) if n_miss is None else n_miss
+    need = lookup_workspace_bytes(T, k, E)
+    if need and ws is None:
+        ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().moe_cache_lookup(_ptr(idx), T, k, _ptr(slot_of_expert), E, _ptr(slot),
+                                  _ptr(miss_expert), _ptr(miss_pair), _ptr(n_miss), _ptr(ws),
+                                  ws_bytes, _stream(stream)), "moe_cache_lookup")
+    return slot, miss_expert, miss_pair, n_miss
+
+
+def decode_workspace_bytes(layer: MoeLayer, T: int) -> int:
+    L = layer.c_struct()
+    return int(lib().moe_decode_workspace_bytes(ctypes.byref(L), T))
+
+
+def expert_ffn_decode(layer: MoeLayer, x, idx, slot, w, y=None, ws=None, stream=None):
+    _dev(x, torch.float32, "x")
+    for name, t, dt in (("idx", idx, torch.int32), ("slot", slot, torch.int32),
+                        ("w", w, torch.float32)):
+        _dev(t, dt, name)
+    T = x.shape[0]
+    L = layer.c_struct()
+    if y is None:
+        y = torch.empty_like(x)
+    if ws is None:
+        ws = torch.empty((decode_workspace_bytes(layer, T),), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_expert_ffn_decode(ctypes.byref(L), _ptr(x), T, _ptr(idx), _ptr(slot),
+                                       _ptr(w), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_expert_ffn_decode")
+    return y
+
+
+def prefill_workspace_bytes(layer: MoeLayer, T: int) -> int:
+    L = layer.c_struct()
+    return int(lib().moe_prefill_workspace_bytes(ctypes.byref(L), T))
+
+
+def expert_ffn_prefill(layer: MoeLayer, x_bf16, idx, slot, out_pairs=None, pair_pos=None,
+                       expert_offsets=None, out_shared=None, with_shared=True, ws=None,
+                       stream=None):
+    _dev(x_bf16, torch.bfloat16, "x_bf16")
+    _dev(idx, torch.int32, "idx")
+    _dev(slot, torch.int32, "slot")
+    T, d = x_bf16.shape
+    k = idx.shape[1]
+    dev = x_bf16.device
+    if out_pairs is None:
+        out_pairs = torch.empty((T * k, d), dtype=torch.float32, device=dev)
+    if pair_pos is None:
+        pair_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if expert_offsets is None:
+        expert_offsets = torch.empty((layer.n_experts + 1,), dtype=torch.int32, device=dev)
+    if with_shared and layer.shared_slot >= 0 and out_shared is None:
+        out_shared = torch.empty((T, d), dtype=torch.float32, device=dev)
+    if not with_shared:
+        out_shared = None
+    if ws is None:
+        ws = torch.empty((prefill_workspace_bytes(layer, T),), dtype=torch.uint8, device=dev)
+    L = layer.c_struct()
+    _check(lib().moe_expert_ffn_prefill(ctypes.byref(L), _ptr(x_bf16), T, _ptr(idx), _ptr(slot),
+                                        _ptr(out_pairs), _ptr(pair_pos), _ptr(expert_offsets),
+                                        _ptr(out_shared), _ptr(ws), ws.numel(),
+                                        _stream(stream)), "moe_expert_ffn_prefill")
+    return out_pairs, pair_pos, expert_offsets, out_shared
+
+
+def combine(x, rows, pair_pos, w, shared=None, y=None, stream=None):
+    if x.dtype == torch.float32:
+        x_dtype = DTYPE_F32
+    elif x.dtype == torch.bfloat16:
+        x_dtype = DTYPE_BF16
+    else:
+        raise ValueError("x must be float32 or bfloat16")
+    _dev(x, x.dtype, "x")
+    T, d = x.shape
+    k = pair_pos.shape[1] if pair_pos is not None else 0
+    if y is None:
+        y = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    _check(lib().moe_combine(_ptr(x), x_dtype, T, d, k, _ptr(rows), _ptr(pair_pos), _ptr(w),
+                             _ptr(shared), _ptr(y), _stream(stream)), "moe_combine")
+    return y

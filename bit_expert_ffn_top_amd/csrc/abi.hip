@@ -1,0 +1,181 @@
+// C ABI entry points: host-side argument checks, workspace sizing, dispatch.
+// Nothing here allocates; every check runs before the first HIP call.
+#include <stdint.h>
+
+#include "bitffn_moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return MOE_EHIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+bool valid_dims(int fmt, int d, int f) {
+  (void)fmt;
+  if (d < 64 || d > 2048 || !is_pow2(d)) return false;
+  if (f < 32 || f % 32 != 0) return false;
+  int nb = f / 32;
+  if (nb % 3 == 0) nb /= 3;
+  return is_pow2(nb) && f / 32 <= 64;
+}
+
+bool valid_fmt(int fmt) {
+  return fmt == MOE_FMT_Q2S || fmt == MOE_FMT_Q2SM || fmt == MOE_FMT_Q3G;
+}
+
+int check_layer(const moe_layer* L) {
+  if (!L) return MOE_EINVAL;
+  if (!valid_fmt(L->fmt)) return MOE_EFORMAT;
+  if (!valid_dims(L->fmt, L->d_model, L->d_ff)) return MOE_EINVAL;
+  if (L->n_experts < 1 || L->n_experts > MOE_MAX_EXPERTS) return MOE_EINVAL;
+  if (L->top_k < 1 || L->top_k > MOE_MAX_TOPK || L->top_k > L->n_experts) return MOE_EINVAL;
+  if (L->n_slots < 1) return MOE_EINVAL;
+  if (L->shared_slot < -1 || L->shared_slot >= L->n_slots) return MOE_EINVAL;
+  if (L->reserved != 0) return MOE_EINVAL;
+  if (L->slot_bytes != bitffn::slot_layout(L->fmt, L->d_model, L->d_ff).total) return MOE_EFORMAT;
+  if (!L->pool) return MOE_EINVAL;
+  if (!aligned256(L->pool)) return MOE_EALIGN;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EALIGN: return "misaligned device pointer";
+    case MOE_EFORMAT: return "unknown block format or slot size mismatch";
+    case MOE_ENOSPC: return "workspace too small";
+    case MOE_EHIP: return "HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip_error; }
+
+int64_t moe_slot_bytes(int fmt, int d_model, int d_ff) {
+  if (!valid_fmt(fmt)) return MOE_EFORMAT;
+  if (!valid_dims(fmt, d_model, d_ff)) return MOE_EINVAL;
+  return bitffn::slot_layout(fmt, d_model, d_ff).total;
+}
+
+int moe_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                   hipStream_t stream) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E) return MOE_EINVAL;
+  if (T < 0 || T >= (1 << 24)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!logits || !idx || !w) return MOE_EINVAL;
+  if (!aligned16(logits) || !aligned16(idx) || !aligned16(w)) return MOE_EALIGN;
+  return hip_status(bitffn::launch_route_topk(logits, T, E, k, idx, w, stream));
+}
+
+size_t moe_lookup_workspace_bytes(int T, int k, int E) {
+  if (T < 0 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+  if (static_cast<int64_t>(T) * k <= bitffn::kSmallLookupPairs) return 0;
+  return bitffn::group_workspace_bytes(T, E);
+}
+
+int moe_cache_lookup(const int32_t* idx, int T, int k, const int32_t* slot_of_expert, int E,
+                     int32_t* slot, int32_t* miss_expert, int32_t* miss_pair, int32_t* n_miss,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK) return MOE_EINVAL;
+  if (T < 0 || T > 65536) return MOE_EINVAL;
+  if (!idx || !slot_of_expert || !slot || !miss_expert || !n_miss) return MOE_EINVAL;
+  if (!aligned16(idx) || !aligned16(slot_of_expert) || !aligned16(slot) ||
+      !aligned16(miss_expert) || !aligned16(n_miss) || (miss_pair && !aligned16(miss_pair)))
+    return MOE_EALIGN;
+  const int64_t n = static_cast<int64_t>(T) * k;
+  if (n <= bitffn::kSmallLookupPairs)
+    return hip_status(bitffn::launch_lookup_small(idx, T, k, slot_of_expert, E, slot,
+                                                  miss_expert, miss_pair, n_miss, stream));
+  if (!ws) return MOE_EINVAL;
+  if (!aligned256(ws)) return MOE_EALIGN;
+  if (ws_bytes < bitffn::group_workspace_bytes(T, E)) return MOE_ENOSPC;
+  // slot for every pair, then the grouping of the missed pairs
+  hipError_t e = bitffn::launch_lookup_slots(idx, T, k, slot_of_expert, slot, stream);
+  if (e != hipSuccess) return hip_status(e);
+  const bitffn::GroupWorkspace gws = bitffn::group_workspace(ws, T, E);
+  return hip_status(bitffn::launch_group_pairs(idx, slot, nullptr, T, k, E, false, gws, nullptr,
+                                               miss_pair, nullptr, miss_expert, n_miss, nullptr,
+                                               0, stream));
+}
+
+size_t moe_decode_workspace_bytes(const moe_layer* L, int T) {
+  if (check_layer(L) != MOE_OK || T < 1 || T > MOE_MAX_DECODE_T) return 0;
+  return bitffn::decode_workspace_bytes(L->d_model, L->d_ff, T, L->top_k);
+}
+
+int moe_expert_ffn_decode(const moe_layer* L, const float* x, int T, const int32_t* idx,
+                          const int32_t* slot, const float* w, float* y, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  const int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 1 || T > MOE_MAX_DECODE_T || T * L->top_k > MOE_MAX_DECODE_PAIRS) return MOE_EINVAL;
+  if (!x || !idx || !slot || !w || !y || !ws) return MOE_EINVAL;
+  if (static_cast<const void*>(x) == static_cast<const void*>(y)) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(idx) || !aligned16(slot) || !aligned16(w) || !aligned16(y))
+    return MOE_EALIGN;
+  if (!aligned256(ws)) return MOE_EALIGN;
+  if (ws_bytes < bitffn::decode_workspace_bytes(L->d_model, L->d_ff, T, L->top_k))
+    return MOE_ENOSPC;
+  return hip_status(bitffn::launch_decode(*L, x, T, idx, slot, w, y, ws, stream));
+}
+
+size_t moe_prefill_workspace_bytes(const moe_layer* L, int T) {
+  if (check_layer(L) != MOE_OK || T < 1 || T > 65536) return 0;
+  return bitffn::prefill_workspace_bytes(L->d_model, L->d_ff, T, L->top_k, L->n_experts);
+}
+
+int moe_expert_ffn_prefill(const moe_layer* L, const uint16_t* x_bf16, int T, const int32_t* idx,
+                           const int32_t* slot, float* out_pairs, int32_t* pair_pos,
+                           int32_t* expert_offsets, float* out_shared, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  const int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 1 || T > 65536) return MOE_EINVAL;
+  if (L->d_model % 128 != 0 || L->d_ff % 64 != 0) return MOE_EINVAL;
+  if (!x_bf16 || !idx || !slot || !out_pairs || !pair_pos || !expert_offsets || !ws)
+    return MOE_EINVAL;
+  if (out_shared && L->shared_slot < 0) return MOE_EINVAL;
+  if (!aligned16(x_bf16) || !aligned16(idx) || !aligned16(slot) || !aligned16(out_pairs) ||
+      !aligned16(pair_pos) || !aligned16(expert_offsets) || (out_shared && !aligned16(out_shared)))
+    return MOE_EALIGN;
+  if (!aligned256(ws)) return MOE_EALIGN;
+  if (ws_bytes < bitffn::prefill_workspace_bytes(L->d_model, L->d_ff, T, L->top_k, L->n_experts))
+    return MOE_ENOSPC;
+  return hip_status(bitffn::launch_prefill(*L, x_bf16, T, idx, slot, out_pairs, pair_pos,
+                                           expert_offsets, out_shared, ws, stream));
+}
+
+int moe_combine(const void* x, int x_dtype, int T, int d, int k, const float* rows,
+                const int32_t* pair_pos, const float* w, const float* shared, float* y,
+                hipStream_t stream) {
+  if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_EINVAL;
+  if (T < 0 || d < 4 || d % 4 != 0 || k < 0 || k > MOE_MAX_TOPK) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  if (!x || !y) return MOE_EINVAL;
+  if (k > 0 && (!rows || !pair_pos || !w)) return MOE_EINVAL;
+  if (x_dtype == MOE_DTYPE_BF16 && static_cast<const void*>(y) == x) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || (rows && !aligned16(rows)) ||
+      (pair_pos && !aligned16(pair_pos)) || (w && !aligned16(w)) || (shared && !aligned16(shared)))
+    return MOE_EALIGN;
+  return hip_status(
+      bitffn::launch_combine(x, x_dtype, T, d, k, rows, pair_pos, w, shared, y, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,245 @@
+// Expert-cache lookup and the grouping of (token, k-slot) pairs by expert.
+//
+// Small inputs (T*k <= 1024, the decode and verify steps): one workgroup.
+//   slot = table[idx]; a bitmap of missed experts in LDS gives the ascending
+//   distinct miss list by prefix popcount; each missed pair's position in the
+//   (expert, t, i) order is the count of missed pairs that sort before it.
+// Large inputs (prefill chunks): a three-pass counting sort that is stable in
+// (t, i) order and needs no sort of keys:
+//   1. per chunk of 32 tokens, a histogram of the selected pairs per expert;
+//   2. one workgroup turns the histograms into per-(chunk, expert) start
+//      positions (exclusive scan over chunks, then over experts);
+//   3. per chunk, one wavefront walks its tokens in order; the k pairs of a
+//      token name distinct experts, so the lanes bump distinct LDS cursors.
+#include "moe_internal.h"
+
+namespace bitffn {
+namespace {
+
+constexpr int kMaxE = MOE_MAX_EXPERTS;
+
+__global__ __launch_bounds__(1024) void lookup_small_kernel(
+    const int32_t* __restrict__ idx, int n, const int32_t* __restrict__ table, int E,
+    int32_t* __restrict__ slot, int32_t* __restrict__ miss_expert,
+    int32_t* __restrict__ miss_pair, int32_t* __restrict__ n_miss) {
+  __shared__ uint32_t bitmap[kMaxE / 32];
+  __shared__ int32_t s_exp[kSmallLookupPairs];
+  __shared__ int32_t s_cnt;
+  const int tid = threadIdx.x;
+  if (tid < kMaxE / 32) bitmap[tid] = 0;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  int e = -1;
+  bool miss = false;
+  if (tid < n) {
+    e = idx[tid];
+    const int s = table[e];
+    slot[tid] = s;
+    miss = s < 0;
+    if (miss) {
+      atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+      atomicAdd(&s_cnt, 1);
+    }
+    s_exp[tid] = miss ? e : -1;
+  }
+  __syncthreads();
+  // ascending distinct missed experts
+  if (tid < E) {
+    const uint32_t word = bitmap[tid >> 5];
+    if ((word >> (tid & 31)) & 1u) {
+      int pos = __popc(word & ((1u << (tid & 31)) - 1u));
+      for (int w = 0; w < (tid >> 5); ++w) pos += __popc(bitmap[w]);
+      miss_expert[pos] = tid;
+    }
+  }
+  // missed pairs ordered by (expert, pair id)
+  if (miss && miss_pair != nullptr) {
+    int pos = 0;
+    for (int q = 0; q < n; ++q) {
+      const int eq = s_exp[q];
+      pos += (eq >= 0) && (eq < e || (eq == e && q < tid));
+    }
+    miss_pair[pos] = tid;
+  }
+  if (tid == 0) {
+    int distinct = 0;
+    for (int w = 0; w < kMaxE / 32; ++w) distinct += __popc(bitmap[w]);
+    n_miss[0] = distinct;
+    n_miss[1] = s_cnt;
+  }
+}
+
+__device__ __forceinline__ bool selected(int s, bool select_hits) {
+  return select_hits ? (s >= 0) : (s < 0);
+}
+
+// pass 1: per-chunk histograms
+__global__ __launch_bounds__(256) void group_count_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ slot_of_pair,
+    const int32_t* __restrict__ table, int T, int k, int E, bool select_hits,
+    int32_t* __restrict__ chunk_counts) {
+  __shared__ int32_t hist[kMaxE];
+  const int chunk = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int t0 = chunk * kGroupChunkTokens;
+  const int t1 = min(T, t0 + kGroupChunkTokens);
+  for (int p = t0 * k + threadIdx.x; p < t1 * k; p += blockDim.x) {
+    const int e = idx[p];
+    const int s = slot_of_pair ? slot_of_pair[p] : table[e];
+    if (selected(s, select_hits)) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    chunk_counts[static_cast<int64_t>(chunk) * E + e] = hist[e];
+}
+
+// pass 2: start positions, offsets, distinct list, tile bases
+__global__ __launch_bounds__(1024) void group_scan_kernel(
+    int n_chunks, int E, int T, int32_t* __restrict__ chunk_counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ distinct,
+    int32_t* __restrict__ counts_out, int32_t* __restrict__ tile_base, int tile_m) {
+  __shared__ int32_t s_tot[kMaxE];
+  __shared__ int32_t s_nz[kMaxE];
+  __shared__ int32_t s_tiles[kMaxE];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E) {
+    for (int c = 0; c < n_chunks; ++c) {
+      int32_t* p = chunk_counts + static_cast<int64_t>(c) * E + e;
+      const int v = *p;
+      *p = tot;  // exclusive within the expert, over chunks
+      tot += v;
+    }
+  }
+  if (e < kMaxE) {
+    s_tot[e] = e < E ? tot : 0;
+    s_nz[e] = (e < E && tot > 0) ? 1 : 0;
+    s_tiles[e] = (e < E) ? (tot + tile_m - 1) / tile_m : 0;
+  }
+  __syncthreads();
+  // Hillis-Steele inclusive scans over the E entries (fixed order)
+  for (int off = 1; off < kMaxE; off <<= 1) {
+    int a = 0, b = 0, c = 0;
+    if (e < kMaxE && e >= off) {
+      a = s_tot[e - off];
+      b = s_nz[e - off];
+      c = s_tiles[e - off];
+    }
+    __syncthreads();
+    if (e < kMaxE && e >= off) {
+      s_tot[e] += a;
+      s_nz[e] += b;
+      s_tiles[e] += c;
+    }
+    __syncthreads();
+  }
+  if (e < E) {
+    const int start = s_tot[e] - tot;  // exclusive
+    for (int c = 0; c < n_chunks; ++c) chunk_counts[static_cast<int64_t>(c) * E + e] += start;
+    if (offsets) offsets[e] = start;
+    if (distinct && tot > 0) distinct[s_nz[e] - 1] = e;
+    if (tile_base) tile_base[e] = s_tiles[e] - (tot + tile_m - 1) / tile_m;
+  }
+  if (e == 0) {
+    const int total = s_tot[E - 1];
+    if (offsets) offsets[E] = total;
+    if (counts_out) {
+      counts_out[0] = s_nz[E - 1];
+      counts_out[1] = total;
+    }
+    if (tile_base) {
+      const int base = s_tiles[E - 1];
+      tile_base[E] = base;
+      tile_base[E + 1] = base + (T + tile_m - 1) / tile_m;
+    }
+  }
+}
+
+// pass 3: stable scatter, one wavefront per chunk of tokens
+__global__ __launch_bounds__(64) void group_scatter_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ slot_of_pair,
+    const int32_t* __restrict__ table, int T, int k, int E, bool select_hits,
+    const int32_t* __restrict__ chunk_start, int32_t* __restrict__ perm,
+    int32_t* __restrict__ pos) {
+  __shared__ int32_t cursor[kMaxE];
+  const int chunk = blockIdx.x;
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) cursor[e] = chunk_start[static_cast<int64_t>(chunk) * E + e];
+  __syncthreads();
+  const int t0 = chunk * kGroupChunkTokens;
+  const int t1 = min(T, t0 + kGroupChunkTokens);
+  for (int t = t0; t < t1; ++t) {
+    for (int i0 = 0; i0 < k; i0 += 64) {
+      const int i = i0 + lane;
+      if (i < k) {
+        const int p = t * k + i;
+        const int e = idx[p];
+        const int s = slot_of_pair ? slot_of_pair[p] : table[e];
+        int at = -1;
+        if (selected(s, select_hits)) {
+          at = atomicAdd(&cursor[e], 1);
+          if (perm) perm[at] = p;
+        }
+        if (pos) pos[p] = at;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void lookup_slots_kernel(const int32_t* __restrict__ idx, int n,
+                                                           const int32_t* __restrict__ table,
+                                                           int32_t* __restrict__ slot) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p < n) slot[p] = table[idx[p]];
+}
+
+}  // namespace
+
+hipError_t launch_lookup_slots(const int32_t* idx, int T, int k, const int32_t* table,
+                               int32_t* slot, hipStream_t s) {
+  const int n = T * k;
+  if (n == 0) return hipSuccess;
+  lookup_slots_kernel<<<(n + 255) / 256, 256, 0, s>>>(idx, n, table, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_lookup_small(const int32_t* idx, int T, int k, const int32_t* table, int E,
+                               int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
+                               int32_t* n_miss, hipStream_t s) {
+  lookup_small_kernel<<<1, 1024, 0, s>>>(idx, T * k, table, E, slot, miss_expert, miss_pair,
+                                         n_miss);
+  return hipGetLastError();
+}
+
+size_t group_workspace_bytes(int T, int E) {
+  const int64_t n_chunks = (T + kGroupChunkTokens - 1) / kGroupChunkTokens;
+  return static_cast<size_t>(align256(n_chunks * E * 4) + align256((E + 1) * 4));
+}
+
+GroupWorkspace group_workspace(void* ws, int T, int E) {
+  const int64_t n_chunks = (T + kGroupChunkTokens - 1) / kGroupChunkTokens;
+  char* p = static_cast<char*>(ws);
+  GroupWorkspace g;
+  g.chunk_counts = reinterpret_cast<int32_t*>(p);
+  g.totals = reinterpret_cast<int32_t*>(p + align256(n_chunks * E * 4));
+  return g;
+}
+
+hipError_t launch_group_pairs(const int32_t* idx, const int32_t* slot_of_pair,
+                              const int32_t* table, int T, int k, int E, bool select_hits,
+                              GroupWorkspace gws, int32_t* offsets, int32_t* perm,
+                              int32_t* pos, int32_t* distinct, int32_t* counts_out,
+                              int32_t* tile_base, int tile_m, hipStream_t s) {
+  const int n_chunks = (T + kGroupChunkTokens - 1) / kGroupChunkTokens;
+  group_count_kernel<<<n_chunks, 256, 0, s>>>(idx, slot_of_pair, table, T, k, E, select_hits,
+                                              gws.chunk_counts);
+  group_scan_kernel<<<1, 1024, 0, s>>>(n_chunks, E, T, gws.chunk_counts, offsets, distinct,
+                                       counts_out, tile_base, tile_m > 0 ? tile_m : 1);
+  group_scatter_kernel<<<n_chunks, 64, 0, s>>>(idx, slot_of_pair, table, T, k, E, select_hits,
+                                               gws.chunk_counts, perm, pos);
+  return hipGetLastError();
+}
+
+}  // namespace bitffn

@@ -1,0 +1,71 @@
+// Routing-weighted combine into the residual:
+//   y[t] = x[t] + sum_i w[t,i] * rows[pair_pos[t,i]] + shared[t]
+// One thread per 4 consecutive columns of one token; the k terms are added in
+// i order with fused multiply-adds, the shared row last.
+#include "moe_internal.h"
+
+namespace bitffn {
+namespace {
+
+template <bool XBF16>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ x, int T, int d,
+                                                      int k, const float* __restrict__ rows,
+                                                      const int32_t* __restrict__ pair_pos,
+                                                      const float* __restrict__ w,
+                                                      const float* __restrict__ shared,
+                                                      float* __restrict__ y) {
+  const int d4 = d >> 2;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= static_cast<int64_t>(T) * d4) return;
+  const int t = static_cast<int>(gid / d4);
+  const int c = static_cast<int>(gid - static_cast<int64_t>(t) * d4) * 4;
+  float4 acc;
+  if (XBF16) {
+    const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) +
+                                                    static_cast<int64_t>(t) * d + c);
+    acc.x = bf16_bits_to_float(b.x & 0xFFFFu);
+    acc.y = bf16_bits_to_float(b.x >> 16);
+    acc.z = bf16_bits_to_float(b.y & 0xFFFFu);
+    acc.w = bf16_bits_to_float(b.y >> 16);
+  } else {
+    acc = *reinterpret_cast<const float4*>(static_cast<const float*>(x) +
+                                           static_cast<int64_t>(t) * d + c);
+  }
+  for (int i = 0; i < k; ++i) {
+    const int p = pair_pos[static_cast<int64_t>(t) * k + i];
+    if (p < 0) continue;
+    const float wi = w[static_cast<int64_t>(t) * k + i];
+    const float4 r = *reinterpret_cast<const float4*>(rows + static_cast<int64_t>(p) * d + c);
+    acc.x = fmaf(wi, r.x, acc.x);
+    acc.y = fmaf(wi, r.y, acc.y);
+    acc.z = fmaf(wi, r.z, acc.z);
+    acc.w = fmaf(wi, r.w, acc.w);
+  }
+  if (shared) {
+    const float4 r = *reinterpret_cast<const float4*>(shared + static_cast<int64_t>(t) * d + c);
+    acc.x += r.x;
+    acc.y += r.y;
+    acc.z += r.z;
+    acc.w += r.w;
+  }
+  *reinterpret_cast<float4*>(y + static_cast<int64_t>(t) * d + c) = acc;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* x, int x_dtype, int T, int d, int k, const float* rows,
+                          const int32_t* pair_pos, const float* w, const float* shared,
+                          float* y, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(T) * (d / 4);
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  if (x_dtype == MOE_DTYPE_BF16)
+    combine_kernel<true><<<static_cast<unsigned>(blocks), 256, 0, s>>>(x, T, d, k, rows, pair_pos,
+                                                                      w, shared, y);
+  else
+    combine_kernel<false><<<static_cast<unsigned>(blocks), 256, 0, s>>>(x, T, d, k, rows,
+                                                                       pair_pos, w, shared, y);
+  return hipGetLastError();
+}
+
+}  // namespace bitffn

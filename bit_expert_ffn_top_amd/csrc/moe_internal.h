@@ -1,0 +1,62 @@
+// Host-side launchers shared between the translation units of the library.
+// Every launcher assumes its arguments were validated by the C ABI layer and
+// returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bitffn_moe.h"
+#include "moe_common.h"
+
+namespace bitffn {
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx,
+                             float* w, hipStream_t s);
+
+hipError_t launch_lookup_slots(const int32_t* idx, int T, int k, const int32_t* table,
+                               int32_t* slot, hipStream_t s);
+
+// Small lookup: one workgroup, T*k <= kSmallLookupPairs.
+constexpr int kSmallLookupPairs = 1024;
+hipError_t launch_lookup_small(const int32_t* idx, int T, int k, const int32_t* table, int E,
+                               int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
+                               int32_t* n_miss, hipStream_t s);
+
+// Grouping of (t, i) pairs by expert id, stable in (t, i) order, for the pairs
+// whose slot satisfies the predicate (hits: slot >= 0, misses: slot < 0).
+// Outputs: offsets[E+1] (may be null), perm (pair ids in group order),
+// pos[T*k] (position of each pair, -1 if not selected; may be null),
+// distinct[E] (ascending ids of non-empty groups; may be null),
+// counts_out[2] = {non-empty groups, selected pairs} (may be null),
+// tile_base[E+2] (may be null): prefix sums of ceil(group size / tile_m) for
+// the E groups plus one extra group of T rows (the shared expert).
+struct GroupWorkspace {
+  int32_t* chunk_counts;  // [n_chunks * E]
+  int32_t* totals;        // [E + 1]
+};
+constexpr int kGroupChunkTokens = 32;
+size_t group_workspace_bytes(int T, int E);
+GroupWorkspace group_workspace(void* ws, int T, int E);
+hipError_t launch_group_pairs(const int32_t* idx, const int32_t* slot_of_pair,
+                              const int32_t* table, int T, int k, int E, bool select_hits,
+                              GroupWorkspace gws, int32_t* offsets, int32_t* perm,
+                              int32_t* pos, int32_t* distinct, int32_t* counts_out,
+                              int32_t* tile_base, int tile_m, hipStream_t s);
+
+size_t decode_workspace_bytes(int d, int f, int T, int k);
+hipError_t launch_decode(const moe_layer& L, const float* x, int T, const int32_t* idx,
+                         const int32_t* slot, const float* w, float* y, void* ws,
+                         hipStream_t s);
+
+size_t prefill_workspace_bytes(int d, int f, int T, int k, int E);
+hipError_t launch_prefill(const moe_layer& L, const uint16_t* x_bf16, int T,
+                          const int32_t* idx, const int32_t* slot, float* out_pairs,
+                          int32_t* pair_pos, int32_t* expert_offsets, float* out_shared,
+                          void* ws, hipStream_t s);
+
+hipError_t launch_combine(const void* x, int x_dtype, int T, int d, int k, const float* rows,
+                          const int32_t* pair_pos, const float* w, const float* shared,
+                          float* y, hipStream_t s);
+
+}  // namespace bitffn

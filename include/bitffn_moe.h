@@ -1,0 +1,210 @@
+/*
+ * bitffn_moe.h -- C ABI of the routed-expert MoE layer library (gfx950).
+ *
+ * One MoE layer of a 2-3-bit block-quantized mixture-of-experts model: the
+ * router's top-k choice, the split of the chosen experts into those resident
+ * in the GPU expert cache and those that are not, the fused
+ * dequantize + gate/up + SiLU-gating + down expert FFN, and the
+ * routing-weighted sum into the residual.
+ *
+ * Sources: the pages on the "Strata" engine.
+ *   - "Strata" (news.blueqat.app post 3262), section "Strataとは": 48 layers,
+ *     512 experts per layer, 10 chosen per token plus one shared expert.
+ *   - same page, section "GPU・CPU・RAM・SSDの分担": router, shared expert and a
+ *     cache of the most used experts live on the GPU; long inputs are taken
+ *     8,192 tokens at a time.
+ *   - same page, section "投機的デコード" and "Strataとは？VRAM 12GBのGPUで
+ *     Qwen3.8-Flash-Nextを動かす方法" (vramglass.com), section "その3": up to
+ *     3 drafted tokens are verified in one pass over the layers; the weights
+ *     are read once however many tokens are verified.
+ *   - vramglass.com page, sections "その1" and "その2": about 72% of a
+ *     token's experts are found in the GPU cache; the others are computed
+ *     from host memory at the same time instead of being copied over.
+ *   - "FreeToken vs Strata" (geekoyaji.com), section "共通の仕組み": the GPU
+ *     part and the host part of a layer are joined before the next layer.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers unless marked (host).  The caller owns
+ *     every buffer; the library allocates nothing and keeps no state between
+ *     calls except what a caller-provided workspace holds.
+ *   - Work is enqueued asynchronously on `stream`; results are ready when
+ *     the stream reaches that point.  Calls on one stream are ordered.
+ *   - Arguments are checked on the host before any HIP call; a check that
+ *     fails returns a negative status and enqueues nothing.  MOE_EHIP means
+ *     a HIP launch failed; moe_last_hip_error() gives the HIP code (kept per
+ *     calling thread).
+ *   - Device pointers must be 16-byte aligned (MOE_EALIGN otherwise).
+ *   - Results never depend on timing: every reduction has a fixed order, so
+ *     two runs on the same inputs are bitwise equal.
+ */
+#ifndef BITFFN_MOE_H
+#define BITFFN_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)   /* null pointer, size or count out of range     */
+#define MOE_EALIGN (-2)   /* device pointer not 16-byte aligned           */
+#define MOE_EFORMAT (-3)  /* unknown block format or slot size mismatch  */
+#define MOE_ENOSPC (-4)   /* workspace smaller than the query returned   */
+#define MOE_EHIP (-5)     /* a HIP call failed                           */
+
+/* Block formats: 32 consecutive weights of a row share one block.
+ *   MOE_FMT_Q2S : 2-bit code q, fp16 scale s:          w = s * (q - 1.5)
+ *   MOE_FMT_Q2SM: 2-bit code q, fp16 scale s, min m:   w = m + s * q
+ *   MOE_FMT_Q3G : 3-bit code q, fp16 scale s:          w = s * (2q - 7) / 7
+ *                 (the grid -3.5..3.5 in steps of 1, times s / 3.5)
+ * Slot layout (bytes of one expert): matrix G = 2*d_ff rows x d_model
+ * columns (row 2j = gate row j, row 2j+1 = up row j), then matrix
+ * D = d_model rows x d_ff columns (down projection).  Each matrix is
+ * row-major in blocks and stored as planes, each starting 256-byte aligned
+ * from the slot start, in this order:
+ *   codes (8 B/block: code i at bits [2i,2i+2) of the little-endian 64-bit
+ *          word; for Q3G the low two bits),
+ *   hi    (Q3G only, 4 B/block: bit i = bit 2 of code i),
+ *   scale (fp16, 2 B/block),
+ *   min   (Q2SM only, fp16, 2 B/block).
+ * The slot size is rounded up to 256 bytes; moe_slot_bytes() returns it. */
+#define MOE_FMT_Q2S 1
+#define MOE_FMT_Q2SM 2
+#define MOE_FMT_Q3G 3
+
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+
+/* Limits checked on the host. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 64
+#define MOE_MAX_DECODE_T 4
+#define MOE_MAX_DECODE_PAIRS 64
+
+/* One MoE layer as it sits in device memory (host struct, read during the
+ * call only). */
+typedef struct moe_layer {
+  int32_t d_model;     /* multiple of 64, a power of two in 64..2048        */
+  int32_t d_ff;        /* multiple of 32; d_ff/32 = 2^n or 3 * 2^n, <= 64   */
+  int32_t n_experts;   /* 1..MOE_MAX_EXPERTS routed experts                  */
+  int32_t top_k;       /* 1..min(n_experts, MOE_MAX_TOPK)                    */
+  int32_t fmt;         /* MOE_FMT_*                                          */
+  int32_t n_slots;     /* slots in the pool                                  */
+  int32_t shared_slot; /* slot of the always-used shared expert, -1 = none   */
+  int32_t reserved;    /* must be 0                                          */
+  int64_t slot_bytes;  /* must equal moe_slot_bytes(fmt, d_model, d_ff)      */
+  const void* pool;    /* device: n_slots * slot_bytes packed experts, 256-B
+                          aligned                                            */
+} moe_layer;
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* (host) Static text for a status code. */
+const char* moe_status_str(int status);
+
+/* (host) HIP error code of this thread's last MOE_EHIP. */
+int moe_last_hip_error(void);
+
+/* (host) Bytes of one packed expert slot; MOE_EFORMAT / MOE_EINVAL (as a
+ * negative value) for an unknown format or unsupported sizes. */
+int64_t moe_slot_bytes(int fmt, int d_model, int d_ff);
+
+/* Router top-k ("Strata" page, "Strataとは": 10 of 512 per token).
+ * logits fp32 [T][E] row-major.  Per token the experts are ranked by
+ * (logit descending, expert id ascending); NaN ranks as -inf and -0.0 as
+ * +0.0.  idx int32 [T][k] receives the first k ids in rank order, w fp32
+ * [T][k] the softmax over those k logits, exp(l_i - l_0) / sum_j
+ * exp(l_j - l_0) with l_0 the largest (the difference of two equal values,
+ * infinities included, is taken as 0).
+ * Limits: 1 <= E <= 1024, 1 <= k <= min(E, 64), 0 <= T < 2^24 (T = 0 is a
+ * no-op). */
+int moe_route_topk(const float* logits, int T, int E, int k,
+                   int32_t* idx, float* w, hipStream_t stream);
+
+/* Expert-cache lookup (vramglass.com page, "その1"/"その2": the GPU caches
+ * the most used experts; the others are computed elsewhere).
+ * slot_of_expert int32 [E]: slot holding expert e, or -1.
+ * slot int32 [T*k] = slot_of_expert[idx]; miss_expert int32 [T*k] receives
+ * the distinct missed expert ids in ascending order; miss_pair int32 [T*k]
+ * (may be NULL) receives t*k+i of every missed pair, ordered by
+ * (expert, t, i); n_miss int32 [2] = {distinct missed experts, missed
+ * pairs}.  Entries past the counts are left as they were.
+ * Expert ids in idx must be in [0, E) and distinct within a token (as
+ * moe_route_topk returns them); neither is checked.
+ * ws: device workspace of moe_lookup_workspace_bytes(T, k, E) bytes (0 for
+ * T*k <= 1024, then ws may be NULL), 256-byte aligned. */
+size_t moe_lookup_workspace_bytes(int T, int k, int E);
+int moe_cache_lookup(const int32_t* idx, int T, int k,
+                     const int32_t* slot_of_expert, int E,
+                     int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
+                     int32_t* n_miss, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* (host) Workspace bytes that moe_expert_ffn_decode needs for T tokens. */
+size_t moe_decode_workspace_bytes(const moe_layer* L, int T);
+
+/* Decode / verify layer for T = 1..4 tokens routed independently
+ * ("Strata" page "投機的デコード": one real and up to 3 drafted tokens).
+ *   y[t] = x[t] + sum_{i: slot[t*k+i] >= 0} w[t*k+i] * FFN_{slot}(x[t])
+ *               + FFN_{shared_slot}(x[t])          (if shared_slot >= 0)
+ * with FFN(x) = D (silu(G_gate x) * (G_up x)), silu(z) = z / (1 + e^-z),
+ * summed for each token in k-slot order, shared expert last.  Misses
+ * (slot < 0) are skipped: the caller adds them (moe_combine can).
+ * Each distinct resident expert chosen by any of the T tokens is streamed
+ * from memory once for all tokens that chose it.  x, y fp32 [T][d_model]
+ * (y may not alias x); idx, slot int32 [T][k]; w fp32 [T][k].
+ * Requires T * top_k <= 64.  ws: device workspace of at least
+ * moe_decode_workspace_bytes(L, T) bytes, 256-byte aligned; its contents on
+ * entry do not matter. */
+int moe_expert_ffn_decode(const moe_layer* L, const float* x, int T,
+                          const int32_t* idx, const int32_t* slot,
+                          const float* w, float* y, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* (host) Workspace bytes that moe_expert_ffn_prefill needs for T tokens. */
+size_t moe_prefill_workspace_bytes(const moe_layer* L, int T);
+
+/* Prefill chunk ("Strata" page, "GPU・CPU・RAM・SSDの分担": up to 8,192
+ * tokens at a time).  x_bf16 [T][d_model] bfloat16 bits.  Pairs (t,i) with
+ * slot[t*k+i] >= 0 are grouped by expert id (groups ascending, inside a
+ * group by t then i); expert_offsets int32 [E+1] receives the group bounds,
+ * pair_pos int32 [T*k] each pair's row in out_pairs (-1 for a miss).  For
+ * every pair the expert FFN runs with bf16 inputs and weights (weights
+ * dequantized to bf16 round-to-nearest-even), fp32 accumulation, and
+ * h = silu(g) * u rounded to bf16 before the down product:
+ *   out_pairs fp32 [T*k][d_model] (rows past the pair count untouched),
+ *   out_shared fp32 [T][d_model] = FFN_shared(x[t]) (NULL if no shared
+ *   expert is wanted; must be NULL when shared_slot < 0).
+ * moe_combine then forms y.  Limits: 1 <= T <= 65536, d_model a multiple
+ * of 128, d_ff a multiple of 64.
+ * ws: at least moe_prefill_workspace_bytes(L, T) bytes, 256-byte aligned. */
+int moe_expert_ffn_prefill(const moe_layer* L, const uint16_t* x_bf16, int T,
+                           const int32_t* idx, const int32_t* slot,
+                           float* out_pairs, int32_t* pair_pos,
+                           int32_t* expert_offsets, float* out_shared,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Routing-weighted combine into the residual ("FreeToken vs Strata",
+ * "共通の仕組み": a layer's parts are joined before the next layer).
+ *   y[t] = x[t] + sum_{i: pair_pos[t*k+i] >= 0} w[t*k+i] * rows[pair_pos[t*k+i]]
+ *               + shared[t]                       (if shared != NULL)
+ * summed in i order, shared last, in fp32.  x is fp32 or bf16 bits
+ * (x_dtype), [T][d]; rows fp32 [*][d]; y fp32 [T][d] and may alias x only
+ * when x is fp32.  d must be a multiple of 4. */
+int moe_combine(const void* x, int x_dtype, int T, int d, int k,
+                const float* rows, const int32_t* pair_pos, const float* w,
+                const float* shared, float* y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITFFN_MOE_H */

@@ -226,10 +226,11 @@ def _interleave_gate_up(Wg: torch.Tensor, Wu: torch.Tensor) -> torch.Tensor:
 
 
 def make_layer_pool(cfg: int, layer: int, experts, device="cpu", fmt=None,
-                    batch: int = 32) -> torch.Tensor:
+                    batch: int = 32, shape: LayerShape | None = None) -> torch.Tensor:
     """Packed slots for the listed expert ids (n_experts = shared expert),
-    in list order: uint8 [len(experts), slot_bytes]."""
-    shape = config_shape(cfg)
+    in list order: uint8 [len(experts), slot_bytes].  `shape` overrides the
+    configuration's layer shape (the seeds still come from `cfg`)."""
+    shape = config_shape(cfg) if shape is None else shape
     fmt = layer_format(cfg, layer) if fmt is None else fmt
     sb = slot_bytes(fmt, shape.d_model, shape.d_ff)
     out = torch.empty((len(experts), sb), dtype=torch.uint8, device=device)
@@ -276,7 +277,7 @@ def zipf_gumbel_logits(cfg: int, layer: int, T: int, E: int, s: float,
     g = torch_gen(seed_of(cfg, layer, -1, TAG_LOGITS, step), device)
     u = torch.rand((T, E), generator=g, dtype=torch.float32, device=device)
     u = u.clamp_(min=1e-12)
-    gumbel = -torch.log(-torch.log(u).clamp_(min=1e-30))
+    gumbel = -torch.log((-torch.log(u)).clamp_(min=1e-30))
     return base.unsqueeze(0) + gumbel
 
 

@@ -1,0 +1,91 @@
+"""Shared helpers of the GPU parity tests (not a test module)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+# fp32 outputs: max|err| <= 2e-3 * max|ref| and sum|err| / sum|ref| <= 1e-4,
+# on the layer output y and on its update y - x.
+MAX_REL = 2e-3
+MEAN_REL = 1e-4
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def check_close(got, ref, x=None, what="y", max_rel=MAX_REL, mean_rel=MEAN_REL):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    pairs = [(what, got, ref)]
+    if x is not None:
+        x = np.asarray(x, dtype=np.float64)
+        pairs.append((what + "-x", got - x, ref - x))
+    for name, g, r in pairs:
+        err = np.abs(g - r)
+        scale = np.abs(r).max()
+        if scale == 0:
+            assert err.max() == 0, f"{name}: expected zeros, max err {err.max()}"
+            continue
+        assert err.max() <= max_rel * scale, f"{name}: max err {err.max():.3e} > {max_rel}*{scale:.3e}"
+        mr = err.sum() / np.abs(r).sum()
+        assert mr <= mean_rel, f"{name}: mean relative error {mr:.3e} > {mean_rel}"
+
+
+class GpuLayer:
+    """A layer's packed pool on the device plus the oracle's view of it."""
+
+    def __init__(self, cfg, layer, shape, fmt, dev, resident=None, shared=True, seed_slots=True,
+                 only_experts=None):
+        self.cfg, self.layer, self.shape, self.fmt = cfg, layer, shape, fmt
+        E = shape.n_experts
+        self.E = E
+        resident = np.arange(E) if resident is None else np.asarray(resident)
+        ids = [int(e) for e in resident] + ([E] if shared else [])
+        rng = np.random.default_rng(1000 + 7 * layer + cfg)
+        order = rng.permutation(len(ids)) if seed_slots else np.arange(len(ids))
+        self.slot_expert = [0] * len(ids)
+        for i, s in enumerate(order):
+            self.slot_expert[int(s)] = ids[i]
+        self.table = np.full(E, -1, dtype=np.int32)
+        self.shared_slot = -1
+        for s, e in enumerate(self.slot_expert):
+            if e == E:
+                self.shared_slot = s
+            else:
+                self.table[e] = s
+        sb = synth.slot_bytes(fmt, shape.d_model, shape.d_ff)
+        self.pool = torch.zeros((len(ids), sb), dtype=torch.uint8, device=dev)
+        want = set(ids) if only_experts is None else set(only_experts) | ({E} if shared else set())
+        fill = [s for s, e in enumerate(self.slot_expert) if e in want]
+        self._bytes = {}
+        if fill:
+            experts = [self.slot_expert[s] for s in fill]
+            packed = synth.make_layer_pool(cfg, layer, experts, device=dev, fmt=fmt, shape=shape)
+            self.pool[fill] = packed
+            host = packed.cpu().numpy()
+            for j, s in enumerate(fill):
+                self._bytes[s] = host[j]
+        self._w = {}
+        import bit_expert_ffn_top_amd as bf
+        self.layer_obj = bf.MoeLayer(shape.d_model, shape.d_ff, E, shape.top_k, fmt, self.pool,
+                                     self.shared_slot)
+
+    def weights_of_slot(self, s):
+        if s not in self._w:
+            self._w[s] = oracle.unpack_expert(self._bytes[s], self.fmt, self.shape.d_model,
+                                              self.shape.d_ff)
+        return self._w[s]
+
+    def weights_of_expert(self, e):
+        s = self.shared_slot if e == self.E else int(self.table[e])
+        return self.weights_of_slot(s)
+
+    def table_dev(self, dev):
+        return torch.tensor(self.table, dtype=torch.int32, device=dev)

@@ -1,0 +1,156 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+the header declares, computes slot sizes like the two independent layout
+implementations, and rejects bad arguments on the host before any HIP call
+(so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitffn_moe.h")
+
+bf = pytest.importorskip("bit_expert_ffn_top_amd")
+
+
+def _lib():
+    try:
+        return bf.lib()
+    except RuntimeError as e:
+        pytest.skip(str(e))
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    lib = _lib()
+    names = _declared_functions()
+    assert len(names) >= 12, names
+    for n in names:
+        assert hasattr(lib, n), n
+    from bit_expert_ffn_top_amd import _binding
+    assert set(names) == set(_binding.SIGNATURES), set(names) ^ set(_binding.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    lib = _lib()
+    assert lib.moe_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.moe_status_str(st)
+    assert lib.moe_status_str(-99) == b"unknown status"
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("d,f", [(64, 32), (256, 128), (2048, 768), (512, 96), (1024, 2048)])
+def test_slot_bytes_matches_layouts(fmt, d, f):
+    lib = _lib()
+    got = lib.moe_slot_bytes(fmt, d, f)
+    assert got == synth.slot_bytes(fmt, d, f) == oracle.slot_size(fmt, d, f)
+
+
+def test_slot_bytes_rejects():
+    lib = _lib()
+    assert lib.moe_slot_bytes(4, 256, 128) == -3
+    assert lib.moe_slot_bytes(2, 96, 128) == -1       # d not a power of two
+    assert lib.moe_slot_bytes(2, 4096, 128) == -1     # d too large
+    assert lib.moe_slot_bytes(2, 256, 160) == -1      # 5 blocks per row
+    assert lib.moe_slot_bytes(2, 256, 4096) == -1     # d_ff too large
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails its host checks
+
+
+def _p(off=0):
+    return ctypes.c_void_p(FAKE + off)
+
+
+def test_route_topk_host_checks():
+    lib = _lib()
+    s = ctypes.c_void_p(0)
+    assert lib.moe_route_topk(_p(), 1, 0, 1, _p(), _p(), s) == -1          # E = 0
+    assert lib.moe_route_topk(_p(), 1, 2000, 4, _p(), _p(), s) == -1       # E > 1024
+    assert lib.moe_route_topk(_p(), 1, 64, 65, _p(), _p(), s) == -1        # k > 64
+    assert lib.moe_route_topk(_p(), 1, 8, 9, _p(), _p(), s) == -1          # k > E
+    assert lib.moe_route_topk(_p(), -1, 64, 4, _p(), _p(), s) == -1
+    assert lib.moe_route_topk(None, 1, 64, 4, _p(), _p(), s) == -1
+    assert lib.moe_route_topk(_p(4), 1, 64, 4, _p(), _p(), s) == -2        # misaligned
+    assert lib.moe_route_topk(None, 0, 64, 4, None, None, s) == 0          # T = 0: no-op
+
+
+def test_lookup_host_checks():
+    lib = _lib()
+    s = ctypes.c_void_p(0)
+    assert lib.moe_cache_lookup(_p(), 1, 0, _p(), 64, _p(), _p(), _p(), _p(), None, 0, s) == -1
+    assert lib.moe_cache_lookup(None, 1, 4, _p(), 64, _p(), _p(), _p(), _p(), None, 0, s) == -1
+    assert lib.moe_cache_lookup(_p(8), 1, 4, _p(), 64, _p(), _p(), _p(), _p(), None, 0, s) == -2
+    # large inputs need a workspace
+    need = lib.moe_lookup_workspace_bytes(8192, 10, 512)
+    assert need > 0 and lib.moe_lookup_workspace_bytes(4, 10, 512) == 0
+    assert lib.moe_cache_lookup(_p(), 8192, 10, _p(), 512, _p(), _p(), _p(), _p(), None, 0, s) == -1
+    assert lib.moe_cache_lookup(_p(), 8192, 10, _p(), 512, _p(), _p(), _p(), _p(), _p(),
+                                need - 1, s) == -4
+
+
+def _layer(**kw):
+    v = dict(d_model=2048, d_ff=768, n_experts=512, top_k=10, fmt=2, n_slots=513,
+             shared_slot=512, reserved=0, slot_bytes=synth.slot_bytes(2, 2048, 768), pool=FAKE)
+    v.update(kw)
+    from bit_expert_ffn_top_amd._binding import MoeLayerC
+    return MoeLayerC(**v)
+
+
+def test_decode_host_checks():
+    lib = _lib()
+    s = ctypes.c_void_p(0)
+    L = _layer()
+    need = lib.moe_decode_workspace_bytes(ctypes.byref(L), 1)
+    assert need > 0
+    args = lambda L, T=1, ws=need, y=_p(1 << 20): (ctypes.byref(L), _p(), T, _p(), _p(), _p(), y, _p(), ws, s)
+    assert lib.moe_expert_ffn_decode(*args(L, ws=need - 1)) == -4
+    assert lib.moe_expert_ffn_decode(*args(L, T=5)) == -1
+    assert lib.moe_expert_ffn_decode(*args(_layer(top_k=20), T=4)) == -1   # T*k > 64
+    assert lib.moe_expert_ffn_decode(*args(L, y=_p())) == -1               # y aliases x
+    assert lib.moe_expert_ffn_decode(*args(_layer(fmt=7))) == -3
+    assert lib.moe_expert_ffn_decode(*args(_layer(slot_bytes=12345))) == -3
+    assert lib.moe_expert_ffn_decode(*args(_layer(pool=FAKE + 16))) == -2
+    assert lib.moe_expert_ffn_decode(*args(_layer(shared_slot=513))) == -1
+    assert lib.moe_expert_ffn_decode(*args(_layer(reserved=1))) == -1
+    assert lib.moe_expert_ffn_decode(*args(_layer(top_k=0))) == -1
+    assert lib.moe_expert_ffn_decode(*args(_layer(d_model=3000))) == -1
+    assert lib.moe_decode_workspace_bytes(ctypes.byref(L), 5) == 0
+
+
+def test_prefill_host_checks():
+    lib = _lib()
+    s = ctypes.c_void_p(0)
+    L = _layer()
+    need = lib.moe_prefill_workspace_bytes(ctypes.byref(L), 8192)
+    assert need > 0
+    def call(L, T=8192, ws=need, shared=_p()):
+        return lib.moe_expert_ffn_prefill(ctypes.byref(L), _p(), T, _p(), _p(), _p(), _p(), _p(),
+                                          shared, _p(), ws, s)
+    assert call(L, ws=need - 1) == -4
+    assert call(L, T=0) == -1
+    assert call(L, T=70000) == -1
+    assert call(_layer(shared_slot=-1)) == -1                               # shared out, no shared
+    L64 = _layer(d_model=64, slot_bytes=synth.slot_bytes(2, 64, 768))
+    assert call(L64, ws=1 << 40) == -1                                      # d not a multiple of 128
+
+
+def test_combine_host_checks():
+    lib = _lib()
+    s = ctypes.c_void_p(0)
+    assert lib.moe_combine(_p(), 3, 1, 64, 4, _p(), _p(), _p(), None, _p(), s) == -1
+    assert lib.moe_combine(_p(), 0, 1, 66, 4, _p(), _p(), _p(), None, _p(), s) == -1
+    assert lib.moe_combine(_p(), 0, 1, 64, 4, None, _p(), _p(), None, _p(), s) == -1
+    assert lib.moe_combine(_p(), 1, 1, 64, 4, _p(), _p(), _p(), None, _p(), s) == -1   # bf16 alias
+    assert lib.moe_combine(_p(4), 0, 1, 64, 4, _p(), _p(), _p(), None, _p(1 << 12), s) == -2
+    assert lib.moe_combine(None, 0, 0, 64, 4, None, None, None, None, None, s) == 0

@@ -1,0 +1,156 @@
+"""GPU parity: prefill chunk (grouping, two grouped bf16 MFMA GEMMs, combine)
+and the standalone combine, against the oracle.
+
+expert_offsets and pair_pos must match bit for bit; out_pairs, out_shared
+and y within max|err| <= 2e-3 max|ref| and normwise 1e-4 (on y and y - x).
+The oracle rounds x, the dequantized weights and h = silu(g) * u to bf16 as
+the kernels do."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import GpuLayer, check_close, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill(L, x_bf16, logits, k, dev, table=None, with_shared=True):
+    import bit_expert_ffn_top_amd as bf
+    idx, w = bf.route_topk(logits.to(dev), k)
+    tab = L.table_dev(dev) if table is None else torch.tensor(table, dtype=torch.int32, device=dev)
+    slot, _, _, _ = bf.cache_lookup(idx, tab)
+    out_pairs, pair_pos, offs, out_sh = bf.expert_ffn_prefill(L.layer_obj, x_bf16.to(dev), idx,
+                                                              slot, with_shared=with_shared)
+    y = bf.combine(x_bf16.to(dev), out_pairs, pair_pos, w, out_sh)
+    torch.cuda.synchronize()
+    return (out_pairs.cpu(), pair_pos.cpu().numpy(), offs.cpu().numpy(),
+            None if out_sh is None else out_sh.cpu(), y.cpu(), idx.cpu().numpy(),
+            slot.cpu().numpy(), w.cpu().numpy())
+
+
+def _oracle_groups(idx, slot, E):
+    """Oracle grouping of the hit pairs only (misses get position -1)."""
+    T, k = idx.shape
+    hit = slot >= 0
+    order = sorted((p for p in range(T * k) if hit.reshape(-1)[p]),
+                   key=lambda p: (idx.reshape(-1)[p], p))
+    counts = np.zeros(E, np.int64)
+    for p in order:
+        counts[idx.reshape(-1)[p]] += 1
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    pos = np.full(T * k, -1, np.int32)
+    pos[np.array(order, dtype=np.int64)] = np.arange(len(order), dtype=np.int32)
+    return offs, pos.reshape(T, k), order
+
+
+CASES = [
+    ("q2sm_T16", synth.LayerShape(64, 4, 256, 128, True), synth.FMT_Q2SM, 16),
+    ("q2sm_T300", synth.LayerShape(64, 4, 256, 128, True), synth.FMT_Q2SM, 300),
+    ("q2s_T130_noshared", synth.LayerShape(64, 4, 256, 128, False), synth.FMT_Q2S, 130),
+    ("q3g_T77", synth.LayerShape(32, 6, 256, 192, True), synth.FMT_Q3G, 77),
+    ("q2sm_T1", synth.LayerShape(64, 4, 256, 128, True), synth.FMT_Q2SM, 1),
+]
+
+
+@pytest.mark.parametrize("name,shape,fmt,T", CASES, ids=[c[0] for c in CASES])
+def test_prefill_small(name, shape, fmt, T):
+    dev = need_gpu()
+    L = GpuLayer(4, 1, shape, fmt, dev, shared=shape.shared)
+    x = synth.make_x(4, 1, T, shape.d_model, dtype=torch.bfloat16)
+    logits = synth.make_logits(4, 1, T, shape.n_experts, 1.5)
+    out_pairs, pair_pos, offs, out_sh, y, idx, slot, w = _prefill(L, x, logits, shape.top_k, dev)
+    ridx, rw = oracle.route_topk(logits.numpy(), shape.top_k)
+    np.testing.assert_array_equal(idx, ridx)
+    roffs, rpos, _ = _oracle_groups(ridx, slot, shape.n_experts)
+    np.testing.assert_array_equal(offs, roffs)
+    np.testing.assert_array_equal(pair_pos, rpos)
+    xd = x.double().numpy()
+    shared_w = L.weights_of_slot(L.shared_slot) if shape.shared else None
+    ro, rsh, ry = oracle.prefill_layer(xd, ridx, rw, L.weights_of_expert, shared_w, shape.n_experts)
+    n = int(roffs[-1])
+    check_close(out_pairs.numpy()[:n], ro[:n], what="out_pairs")
+    if shape.shared:
+        check_close(out_sh.numpy(), rsh, what="out_shared")
+    check_close(y.numpy(), ry, xd)
+
+
+def test_prefill_with_misses():
+    dev = need_gpu()
+    shape = synth.LayerShape(64, 4, 256, 128, True)
+    rng = np.random.default_rng(3)
+    resident = np.sort(rng.choice(64, 40, replace=False))
+    L = GpuLayer(4, 2, shape, synth.FMT_Q2SM, dev, resident=resident)
+    T = 200
+    x = synth.make_x(4, 2, T, 256, dtype=torch.bfloat16)
+    logits = synth.make_logits(4, 2, T, 64, 1.5)
+    out_pairs, pair_pos, offs, out_sh, y, idx, slot, w = _prefill(L, x, logits, 4, dev)
+    assert (slot < 0).any()
+    roffs, rpos, _ = _oracle_groups(idx, slot, 64)
+    np.testing.assert_array_equal(offs, roffs)
+    np.testing.assert_array_equal(pair_pos, rpos)
+    # reference: per token, resident experts only, bf16 rounding points
+    xd = x.double().numpy()
+    ref = xd.copy()
+    for t in range(T):
+        for i in range(4):
+            if slot[t, i] >= 0:
+                ref[t] += w[t, i].astype(np.float64) * oracle.expert_ffn_bf16(
+                    xd[t:t + 1], *L.weights_of_slot(int(slot[t, i])))[0]
+        ref[t] += oracle.expert_ffn_bf16(xd[t:t + 1], *L.weights_of_slot(L.shared_slot))[0]
+    check_close(y.numpy(), ref, xd)
+
+
+def test_prefill_full_chunk_sampled():
+    """The prefill chunk at full size: T=8192, E=512, top-10 + shared,
+    d=2048, d_ff=768, Q2SM.  Grouping is checked in full; outputs on a sample
+    of tokens the oracle evaluates one by one."""
+    dev = need_gpu()
+    shape = synth.config_shape(4)
+    T = 8192
+    L = GpuLayer(4, 0, shape, synth.FMT_Q2SM, dev)
+    x = synth.make_x(4, 0, T, shape.d_model, dtype=torch.bfloat16)
+    logits = synth.make_logits(4, 0, T, shape.n_experts, 1.5)
+    out_pairs, pair_pos, offs, out_sh, y, idx, slot, w = _prefill(L, x, logits, 10, dev)
+    ref_idx = np.argsort(-logits.numpy(), axis=1, kind="stable")[:, :10]
+    np.testing.assert_array_equal(idx, ref_idx)
+    roffs, rpos, order = _oracle_groups(idx, slot, shape.n_experts)
+    np.testing.assert_array_equal(offs, roffs)
+    np.testing.assert_array_equal(pair_pos, rpos)
+    sample = np.random.default_rng(1).choice(T, 6, replace=False)
+    xd = x.double().numpy()
+    rows_got, rows_ref = [], []
+    for t in sample:
+        ridx, rw = oracle.route_topk(logits.numpy()[t:t + 1], 10)
+        ref = xd[t].copy()
+        for i in range(10):
+            o = oracle.expert_ffn_bf16(xd[t:t + 1], *L.weights_of_expert(int(ridx[0, i])))[0]
+            rows_ref.append(o)
+            rows_got.append(out_pairs.numpy()[pair_pos[t, i]])
+            ref += rw[0, i] * o
+        osh = oracle.expert_ffn_bf16(xd[t:t + 1], *L.weights_of_slot(L.shared_slot))[0]
+        check_close(out_sh.numpy()[t], osh, what="out_shared")
+        ref += osh
+        check_close(y.numpy()[t], ref, xd[t])
+    check_close(np.array(rows_got), np.array(rows_ref), what="out_pairs")
+
+
+def test_combine_parity():
+    dev = need_gpu()
+    import bit_expert_ffn_top_amd as bf
+    rng = np.random.default_rng(7)
+    T, d, k, R = 33, 512, 5, 200
+    x = torch.tensor(rng.normal(size=(T, d)), dtype=torch.float32)
+    rows = torch.tensor(rng.normal(size=(R, d)), dtype=torch.float32)
+    pos = rng.choice(R, T * k, replace=False).reshape(T, k).astype(np.int32)
+    pos[rng.random((T, k)) < 0.2] = -1
+    w = torch.tensor(rng.random((T, k)), dtype=torch.float32)
+    sh = torch.tensor(rng.normal(size=(T, d)), dtype=torch.float32)
+    for xx in (x, x.to(torch.bfloat16)):
+        for s in (sh, None):
+            y = bf.combine(xx.to(dev), rows.to(dev), torch.tensor(pos, device=dev), w.to(dev),
+                           None if s is None else s.to(dev))
+            ref = oracle.combine(xx.double().numpy(), rows.double().numpy(), pos,
+                                 w.double().numpy(), None if s is None else s.double().numpy())
+            np.testing.assert_allclose(y.cpu().double().numpy(), ref, rtol=1e-5, atol=1e-5)
