@@ -18,15 +18,11 @@ int hip_status(hipError_t e) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
-bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
-
 bool valid_dims(int fmt, int d, int f) {
   (void)fmt;
-  if (d < 64 || d > 2048 || !is_pow2(d)) return false;
-  if (f < 32 || f % 32 != 0) return false;
-  int nb = f / 32;
-  if (nb % 3 == 0) nb /= 3;
-  return is_pow2(nb) && f / 32 <= 64;
+  if (d < 64 || d > 2048 || d % 64 != 0) return false;
+  if (f < 32 || f > 4096 || f % 32 != 0) return false;
+  return true;
 }
 
 bool valid_fmt(int fmt) {

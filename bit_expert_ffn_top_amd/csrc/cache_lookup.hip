@@ -1,6 +1,7 @@
 // Expert-cache lookup and the grouping of (token, k-slot) pairs by expert.
 //
-// Small inputs (T*k <= 1024, the decode and verify steps): one workgroup.
+// T*k <= 64 (the decode and verify steps): one wavefront, see below.
+// Small inputs (T*k <= 1024): one workgroup.
 //   slot = table[idx]; a bitmap of missed experts in LDS gives the ascending
 //   distinct miss list by prefix popcount; each missed pair's position in the
 //   (expert, t, i) order is the count of missed pairs that sort before it.
@@ -66,6 +67,46 @@ __global__ __launch_bounds__(1024) void lookup_small_kernel(
     for (int w = 0; w < kMaxE / 32; ++w) distinct += __popc(bitmap[w]);
     n_miss[0] = distinct;
     n_miss[1] = s_cnt;
+  }
+}
+
+// T*k <= 64: one wavefront, lane p = pair p; pairs are compared through lane
+// reads (uniform values), so there is no LDS traffic and no barrier.
+__global__ __launch_bounds__(64) void lookup_wave_kernel(
+    const int32_t* __restrict__ idx, int n, const int32_t* __restrict__ table,
+    int32_t* __restrict__ slot, int32_t* __restrict__ miss_expert,
+    int32_t* __restrict__ miss_pair, int32_t* __restrict__ n_miss) {
+  const int p = threadIdx.x;
+  int e = 0x7FFFFFFF;
+  bool miss = false;
+  if (p < n) {
+    e = idx[p];
+    const int s = table[e];
+    slot[p] = s;
+    miss = s < 0;
+  }
+  const int key = miss ? e : 0x7FFFFFFF;   // only missed pairs take part
+  int pos = 0;          // missed pairs before this one in (expert, pair) order
+  int dpos = 0;         // distinct missed experts with a smaller id
+  bool first = miss;    // first missed pair naming this expert
+  for (int q = 0; q < n; ++q) {
+    const int kq = __builtin_amdgcn_readlane(key, q);
+    if (kq == 0x7FFFFFFF) continue;
+    pos += (kq < key || (kq == key && q < p)) ? 1 : 0;
+    if (kq == key && q < p) first = false;
+  }
+  const uint64_t firsts = __ballot(first);
+  for (int q = 0; q < n; ++q) {
+    if (!((firsts >> q) & 1ull)) continue;
+    const int kq = __builtin_amdgcn_readlane(key, q);
+    dpos += kq < key ? 1 : 0;
+  }
+  const uint64_t misses = __ballot(miss);   // taken by the whole wavefront
+  if (miss && miss_pair) miss_pair[pos] = p;
+  if (first) miss_expert[dpos] = e;
+  if (p == 0) {
+    n_miss[0] = __popcll(firsts);
+    n_miss[1] = __popcll(misses);
   }
 }
 
@@ -208,6 +249,10 @@ hipError_t launch_lookup_slots(const int32_t* idx, int T, int k, const int32_t* 
 hipError_t launch_lookup_small(const int32_t* idx, int T, int k, const int32_t* table, int E,
                                int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
                                int32_t* n_miss, hipStream_t s) {
+  if (T * k <= 64) {
+    lookup_wave_kernel<<<1, 64, 0, s>>>(idx, T * k, table, slot, miss_expert, miss_pair, n_miss);
+    return hipGetLastError();
+  }
   lookup_small_kernel<<<1, 1024, 0, s>>>(idx, T * k, table, E, slot, miss_expert, miss_pair,
                                          n_miss);
   return hipGetLastError();

@@ -1,360 +1,341 @@
-// Decode / verify layer for T <= 4 tokens.
+// Decode / verify layer for T <= 4 tokens: two kernels, no waiting between
+// workgroups inside a kernel.
 //
-// 1. plan (one wavefront): the distinct resident experts chosen by the T
-//    tokens, in order of first appearance over (t, i), each with the mask of
-//    tokens that chose it; pair_pos[t*k+i] = u*T + t for a hit, -1 for a miss.
-//    The shared expert takes the fixed union index T*k.
-// 2. gate/up (one wavefront per (union expert, 8 rows of h)): each lane owns
-//    64 consecutive columns of G, i.e. two 32-weight blocks, so a row of
-//    d_model columns is spread over d_model/64 lanes and one 16-byte load per
-//    lane per row fetches the codes.  All the workgroup's weight bytes are
-//    loaded before any arithmetic; each token that chose the expert then
-//    reuses them from registers.  Row sums are reduced across the lanes of
-//    the row; gate and up rows of the same h index sit in neighbouring lane
-//    groups, so h = silu(g) * u needs one more exchange.
-// 3. down (one wavefront per (union expert, 64 output rows)): each lane owns
-//    BD consecutive blocks of a D row (d_ff / (32 BD) lanes per row) and
-//    keeps its slice of h in registers for all the rows it visits.
-// 4. combine: y = x + sum_i w * o_i + o_shared in k-slot order.
-// Every weight byte of a chosen expert is read once per call, however many
-// of the T tokens chose it.
+// Union of experts.  Union member u < T*k is pair u = t*k+i if its slot is a
+// hit and no earlier pair names the same slot; it serves every token that
+// chose that slot.  Member T*k is the shared expert (all tokens).  Every
+// member's packed bytes are read once per call.
+//
+// 1. ffn kernel, one workgroup of 16 wavefronts per (member u, slice js of 32
+//    h indices).  Gate/up: the slice owns G rows 64js..64js+63 (gate and up
+//    rows of h indices 32js..32js+31); lane l streams row 64js+l, so every
+//    load of a wavefront reads one 1 KiB unit of 64 consecutive rows, and the
+//    activation x is the same for all lanes (scalar operands).  The 16
+//    wavefronts split the d_model columns in interleaved 64-column units;
+//    their row sums meet in LDS in a fixed order, and h = silu(g) * u is
+//    formed for the 32 h indices.
+//    Down, split over d_ff: the same workgroup multiplies its 32 h values into
+//    block column js of D (all d_model rows) and stores that partial product.
+//    Weight bytes of both parts are loaded before any arithmetic.
+// 2. combine kernel: y[t] = x[t] + sum_i w[t,i] * (sum over slices of the
+//    partials of member u(t,i)) + (same for the shared member), slices summed
+//    in a fixed tree, terms in k-slot order, shared last.
+// Arithmetic per block: codes become fp16 pairs (c + q) by mask-and-OR with
+// an exponent, each multiplied into fp32 by v_fma_mix; the block's offset sum
+// and scale/min are applied once per block.
 #include "moe_internal.h"
 
 namespace bitffn {
 namespace {
 
-constexpr int kPlanUSlot = 1;
-constexpr int kPlanUMask = 1 + MOE_MAX_DECODE_PAIRS;
-constexpr int kPlanPairPos = 1 + 2 * MOE_MAX_DECODE_PAIRS;
-constexpr int kPlanInts = 1 + 3 * MOE_MAX_DECODE_PAIRS;
+// x is read-only for the whole kernel: reading it through the constant address
+// space lets its wavefront-uniform loads become scalar loads.
+typedef const __attribute__((address_space(4))) float cfloat;
 
-__global__ __launch_bounds__(64) void decode_plan_kernel(const int32_t* __restrict__ slot, int T,
-                                                         int k, int32_t* __restrict__ plan) {
-  const int p = threadIdx.x;
+constexpr int KA_THREADS = 1024;
+constexpr int KA_WAVES = KA_THREADS / 64;
+constexpr int SLICE = 32;          // h indices per workgroup
+constexpr int MAX_DROWS = 2;       // D rows per thread: d_model <= 2048
+
+struct FfnArgs {
+  const uint8_t* pool;
+  int64_t slot_bytes;
+  Planes G, D;
+  int d, f, T, k, shared_slot;
+  const int32_t* slot;
+  float* part;  // [(T*k+1) * T][f/32][d]
+};
+
+// Union member u: its slot and the mask of tokens it serves.
+__device__ __forceinline__ bool union_member(const int32_t* __restrict__ slot, int T, int k,
+                                             int shared_slot, int u, int& s, uint32_t& mask) {
   const int n = T * k;
-  const int s = p < n ? slot[p] : -1;
-  const bool hit = s >= 0;
-  bool first = hit;
-  for (int q = 0; q < n; ++q) {
-    const int sq = __shfl(s, q, 64);
-    if (q < p && sq == s) first = false;
-  }
-  const uint64_t fm = __ballot(first);
-  const int u_first = __popcll(fm & ((1ull << p) - 1ull));
-  int my_u = -1;
-  uint32_t mask = 0;
-  for (int q = 0; q < n; ++q) {
-    const int sq = __shfl(s, q, 64);
-    const int uq = __shfl(u_first, q, 64);
-    const bool fq = (fm >> q) & 1ull;
-    if (hit && sq == s) {
-      mask |= 1u << (q / k);
-      if (fq) my_u = uq;
-    }
-  }
-  if (first) {
-    plan[kPlanUSlot + u_first] = s;
-    plan[kPlanUMask + u_first] = static_cast<int32_t>(mask);
-  }
-  if (p < n) plan[kPlanPairPos + p] = hit ? my_u * T + p / k : -1;
-  if (p == 0) plan[0] = __popcll(fm);
-}
-
-__device__ __forceinline__ bool decode_union_member(const int32_t* plan, int u, int T, int k,
-                                                    int shared_slot, int& slot, uint32_t& mask) {
-  if (u == T * k) {
+  if (u == n) {
     if (shared_slot < 0) return false;
-    slot = shared_slot;
+    s = shared_slot;
     mask = (1u << T) - 1u;
     return true;
   }
-  if (u >= plan[0]) return false;
-  slot = plan[kPlanUSlot + u];
-  mask = static_cast<uint32_t>(plan[kPlanUMask + u]);
+  s = slot[u];
+  if (s < 0) return false;
+  for (int p = 0; p < u; ++p)
+    if (slot[p] == s) return false;
+  mask = 0;
+  for (int p = u; p < n; ++p)
+    if (slot[p] == s) mask |= 1u << (p / k);
   return true;
 }
 
-// NLPR: lanes per G row (= d_model / 64).
-template <int FMT, int NLPR>
-__global__ __launch_bounds__(64) void decode_gateup_kernel(
-    const uint8_t* __restrict__ pool, int64_t slot_bytes, Planes GP, int d, int f, int T, int k,
-    int shared_slot, const float* __restrict__ x, const int32_t* __restrict__ plan,
-    float* __restrict__ hbuf) {
-  constexpr int RPW = 64 / NLPR;                 // rows per wave iteration
-  constexpr int J = RPW <= 16 ? 8 : RPW / 2;     // h indices per workgroup
-  constexpr int NIT = 2 * J / RPW;               // iterations
-  int sl;
-  uint32_t mask;
-  const int u = blockIdx.y;
-  if (!decode_union_member(plan, u, T, k, shared_slot, sl, mask)) return;
-  const uint8_t* base = pool + static_cast<int64_t>(sl) * slot_bytes;
-  const int lane = threadIdx.x;
-  const int c = lane % NLPR;
-  const int rr = lane / NLPR;
-  const int nb = d / 32;
-  const int j0 = blockIdx.x * J;
-
-  uint4 cw[NIT];
-  uint32_t sc[NIT], mn[NIT];
-  uint2 hw[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int64_t r = 2 * j0 + it * RPW + rr;
-    const int64_t blk = r * nb + 2 * c;
-    cw[it] = *reinterpret_cast<const uint4*>(base + GP.codes + blk * 8);
-    sc[it] = *reinterpret_cast<const uint32_t*>(base + GP.scale + blk * 2);
-    if (FMT == MOE_FMT_Q2SM) mn[it] = *reinterpret_cast<const uint32_t*>(base + GP.min + blk * 2);
-    if (FMT == MOE_FMT_Q3G) hw[it] = *reinterpret_cast<const uint2*>(base + GP.hi + blk * 4);
-  }
-
-  for (int t = 0; t < T; ++t) {
-    if (!((mask >> t) & 1u)) continue;
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      opaque(cw[it]);
-      opaque(sc[it]);
-      if (FMT == MOE_FMT_Q2SM) opaque(mn[it]);
-      if (FMT == MOE_FMT_Q3G) opaque(hw[it]);
-    }
-    float xv[64];
-    const float4* xp = reinterpret_cast<const float4*>(x + static_cast<int64_t>(t) * d + 64 * c);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const float4 v = xp[q];
-      xv[4 * q] = v.x;
-      xv[4 * q + 1] = v.y;
-      xv[4 * q + 2] = v.z;
-      xv[4 * q + 3] = v.w;
-    }
-    float xs0 = 0.0f, xs1 = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      xs0 += xv[q];
-      xs1 += xv[32 + q];
-    }
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const float s0 = half_bits_to_float(sc[it] & 0xFFFFu);
-      const float s1 = half_bits_to_float(sc[it] >> 16);
-      float m0 = 0.0f, m1 = 0.0f;
-      if (FMT == MOE_FMT_Q2SM) {
-        m0 = half_bits_to_float(mn[it] & 0xFFFFu);
-        m1 = half_bits_to_float(mn[it] >> 16);
-      }
-      const uint32_t h0 = FMT == MOE_FMT_Q3G ? hw[it].x : 0u;
-      const uint32_t h1 = FMT == MOE_FMT_Q3G ? hw[it].y : 0u;
-      float part = block_dot<FMT>(cw[it].x, cw[it].y, h0, s0, m0, xv, xs0);
-      part += block_dot<FMT>(cw[it].z, cw[it].w, h1, s1, m1, xv + 32, xs1);
-#pragma unroll
-      for (int o = NLPR / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
-      const float other = __shfl_xor(part, NLPR, 64);
-      if ((rr & 1) == 0 && c == 0) {
-        const int j = j0 + (it * RPW + rr) / 2;
-        hbuf[(static_cast<int64_t>(u) * T + t) * f + j] = silu(part) * other;
-      }
-    }
-  }
+// value of v in lane `src` (uniform result)
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
 }
 
-// BD: blocks per lane, LD: lanes per D row (BD * LD = d_ff / 32).
-template <int FMT, int BD, int LD>
-__global__ __launch_bounds__(64) void decode_down_kernel(
-    const uint8_t* __restrict__ pool, int64_t slot_bytes, Planes DP, int d, int f, int T, int k,
-    int shared_slot, const int32_t* __restrict__ plan, const float* __restrict__ hbuf,
-    float* __restrict__ obuf) {
-  constexpr int RPI = 64 / LD;   // rows per iteration
-  constexpr int ROWS = 64;       // rows per workgroup
-  constexpr int NIT = ROWS / RPI;
-  int sl;
-  uint32_t mask;
-  const int u = blockIdx.y;
-  if (!decode_union_member(plan, u, T, k, shared_slot, sl, mask)) return;
-  const uint8_t* base = pool + static_cast<int64_t>(sl) * slot_bytes;
-  const int lane = threadIdx.x;
-  const int c = lane % LD;
-  const int rr = lane / LD;
-  const int nb = f / 32;
-  const int r0 = blockIdx.x * ROWS;
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
 
-  uint2 cw[NIT][BD];
-  uint32_t sc[NIT][BD], mn[NIT][BD], hw[NIT][BD];
+// UPW: G units (2 blocks) per wavefront, ceil(d_model / 64 / KA_WAVES); wavefront
+// w takes units w, w + KA_WAVES, ...  d_model <= 2048.
+template <int FMT, int UPW>
+__global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
+                                                                const float* __restrict__ x) {
+  const int js = blockIdx.x;
+  const int u = blockIdx.y;
+  int s;
+  uint32_t mask;
+  if (!union_member(a.slot, a.T, a.k, a.shared_slot, u, s, mask)) return;
+  const uint8_t* __restrict__ base = a.pool + static_cast<int64_t>(s) * a.slot_bytes;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
+  const int d = a.d;
+  const int64_t R = 2 * static_cast<int64_t>(a.f);   // G rows
+  const int64_t grow = 2 * SLICE * js + lane;        // this lane's G row
+  const int nu = d / 64;
+
+  // ---- loads: G units of this wavefront, then D block column js ----
+  uint4 gc[UPW];
+  uint32_t gs[UPW], gm[UPW];
+  uint2 gh[UPW];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int64_t r = r0 + it * RPI + rr;
+  for (int i = 0; i < UPW; ++i) {
+    if (wave + KA_WAVES * i < nu) {
+      const int64_t unit = static_cast<int64_t>(wave + KA_WAVES * i) * R + grow;
+      gc[i] = *reinterpret_cast<const uint4*>(base + a.G.codes + unit * 16);
+      gs[i] = *reinterpret_cast<const uint32_t*>(base + a.G.scale + unit * 4);
+      if (FMT == MOE_FMT_Q2SM) gm[i] = *reinterpret_cast<const uint32_t*>(base + a.G.min + unit * 4);
+      if (FMT == MOE_FMT_Q3G) gh[i] = *reinterpret_cast<const uint2*>(base + a.G.hi + unit * 8);
+    }
+  }
+  const int ndr = (d - tid + KA_THREADS - 1) / KA_THREADS;   // D rows of this thread
+  uint2 dc[MAX_DROWS];
+  uint32_t ds[MAX_DROWS], dm[MAX_DROWS], dh[MAX_DROWS];
 #pragma unroll
-    for (int b = 0; b < BD; ++b) {
-      const int64_t blk = r * nb + c * BD + b;
-      cw[it][b] = *reinterpret_cast<const uint2*>(base + DP.codes + blk * 8);
-      sc[it][b] = *reinterpret_cast<const uint16_t*>(base + DP.scale + blk * 2);
-      if (FMT == MOE_FMT_Q2SM) mn[it][b] = *reinterpret_cast<const uint16_t*>(base + DP.min + blk * 2);
-      if (FMT == MOE_FMT_Q3G) hw[it][b] = *reinterpret_cast<const uint32_t*>(base + DP.hi + blk * 4);
+  for (int i = 0; i < MAX_DROWS; ++i) {
+    if (i < ndr) {
+      const int64_t unit = static_cast<int64_t>(js) * d + tid + KA_THREADS * i;
+      dc[i] = *reinterpret_cast<const uint2*>(base + a.D.codes + unit * 8);
+      ds[i] = *reinterpret_cast<const uint16_t*>(base + a.D.scale + unit * 2);
+      if (FMT == MOE_FMT_Q2SM) dm[i] = *reinterpret_cast<const uint16_t*>(base + a.D.min + unit * 2);
+      if (FMT == MOE_FMT_Q3G) dh[i] = *reinterpret_cast<const uint32_t*>(base + a.D.hi + unit * 4);
     }
   }
 
-  for (int t = 0; t < T; ++t) {
+  __shared__ float red[KA_WAVES][64];
+  __shared__ float2 bsum[2048 / 32];   // per block of x: (sum, offset constant)
+  __shared__ __attribute__((aligned(16))) float hsh[SLICE];
+  __shared__ float hsum[2];
+
+  const int nslices = a.f / SLICE;
+  for (int t = 0; t < a.T; ++t) {
     if (!((mask >> t) & 1u)) continue;
+    // weights stay in registers across tokens
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
+    for (int i = 0; i < UPW; ++i) {
+      opaque(gc[i]);
+      opaque(gs[i]);
+      if (FMT == MOE_FMT_Q2SM) opaque(gm[i]);
+      if (FMT == MOE_FMT_Q3G) opaque(gh[i]);
+    }
 #pragma unroll
-      for (int b = 0; b < BD; ++b) {
-        opaque(cw[it][b]);
-        opaque(sc[it][b]);
-        if (FMT == MOE_FMT_Q2SM) opaque(mn[it][b]);
-        if (FMT == MOE_FMT_Q3G) opaque(hw[it][b]);
+    for (int i = 0; i < MAX_DROWS; ++i) {
+      opaque(dc[i]);
+      opaque(ds[i]);
+      if (FMT == MOE_FMT_Q2SM) opaque(dm[i]);
+      if (FMT == MOE_FMT_Q3G) opaque(dh[i]);
+    }
+    const float* __restrict__ xt = x + static_cast<int64_t>(t) * d;
+
+    // per-block sums of x: thread b < d/32 sums block b (fixed order), LDS
+    for (int b = tid; b < d / 32; b += KA_THREADS) {
+      const float4* p = reinterpret_cast<const float4*>(xt + 32 * b);
+      float sx = 0.0f, sc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = p[q];
+        const float xv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sx += xv[j];
+          sc = fmaf(block_offset_weight<FMT>(4 * q + j), xv[j], sc);
+        }
+      }
+      bsum[b] = make_float2(sx, block_const<FMT>(sx, sc));
+    }
+    __syncthreads();
+
+    // gate/up rows: partial sums over this wavefront's units (x as scalar
+    // operands)
+    float row = 0.0f;
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      const int c = wave + KA_WAVES * i;
+      if (c < nu) {
+        const cfloat* xw = (const cfloat*)(xt + 64 * c);
+        const float2 s0 = bsum[2 * c], s1 = bsum[2 * c + 1];
+        const uint32_t hw0 = FMT == MOE_FMT_Q3G ? gh[i].x : 0u;
+        const uint32_t hw1 = FMT == MOE_FMT_Q3G ? gh[i].y : 0u;
+        const uint32_t m = FMT == MOE_FMT_Q2SM ? gm[i] : 0u;
+        const float acc0 = block_acc<FMT>(gc[i].x, gc[i].y, hw0, xw, 0);
+        row = block_finish<FMT>(row, acc0, s0.y, s0.x, gs[i], m);
+        const float acc1 = block_acc<FMT>(gc[i].z, gc[i].w, hw1, xw, 32);
+        row = block_finish<FMT>(row, acc1, s1.y, s1.x, gs[i] >> 16, m >> 16);
       }
     }
-    float hv[BD * 32];
-    const float4* hp = reinterpret_cast<const float4*>(
-        hbuf + (static_cast<int64_t>(u) * T + t) * f + c * BD * 32);
+    red[wave][lane] = row;
+    __syncthreads();
+    if (wave == 0) {
+      float rs = red[0][lane];
 #pragma unroll
-    for (int q = 0; q < BD * 8; ++q) {
-      const float4 v = hp[q];
+      for (int w = 1; w < KA_WAVES; ++w) rs += red[w][lane];
+      const float up = __shfl_xor(rs, 1, 64);
+      const float hv = silu(rs) * up;                       // valid in even lanes
+      const int j = lane >> 1;
+      const bool even = (lane & 1) == 0;
+      if (even) hsh[j] = hv;
+      const float hx = wave_sum(even ? hv : 0.0f);
+      const float hc = wave_sum(even ? block_offset_weight<FMT>(j) * hv : 0.0f);
+      if (lane == 0) {
+        hsum[0] = hx;
+        hsum[1] = block_const<FMT>(hx, hc);
+      }
+    }
+    __syncthreads();
+
+    // down: this slice's block column of D, all rows
+    float hv[SLICE];
+#pragma unroll
+    for (int q = 0; q < SLICE / 4; ++q) {
+      const float4 v = reinterpret_cast<const float4*>(hsh)[q];
       hv[4 * q] = v.x;
       hv[4 * q + 1] = v.y;
       hv[4 * q + 2] = v.z;
       hv[4 * q + 3] = v.w;
     }
-    float hs[BD];
+    const float HX = hsum[0], HK = hsum[1];
+    float* __restrict__ out = a.part + ((static_cast<int64_t>(u) * a.T + t) * nslices + js) * d;
 #pragma unroll
-    for (int b = 0; b < BD; ++b) {
-      float a = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 32; ++q) a += hv[32 * b + q];
-      hs[b] = a;
-    }
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      float part = 0.0f;
-#pragma unroll
-      for (int b = 0; b < BD; ++b) {
-        const float s = half_bits_to_float(sc[it][b]);
-        const float m = FMT == MOE_FMT_Q2SM ? half_bits_to_float(mn[it][b]) : 0.0f;
-        part += block_dot<FMT>(cw[it][b].x, cw[it][b].y, FMT == MOE_FMT_Q3G ? hw[it][b] : 0u, s, m,
-                               hv + 32 * b, hs[b]);
-      }
-#pragma unroll
-      for (int o = LD / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
-      if (c == 0) {
-        const int64_t r = r0 + it * RPI + rr;
-        obuf[(static_cast<int64_t>(u) * T + t) * d + r] = part;
+    for (int i = 0; i < MAX_DROWS; ++i) {
+      if (i < ndr) {
+        const float acc = block_acc<FMT>(dc[i].x, dc[i].y, FMT == MOE_FMT_Q3G ? dh[i] : 0u, hv, 0);
+        out[tid + KA_THREADS * i] =
+            block_finish<FMT>(0.0f, acc, HK, HX, ds[i], FMT == MOE_FMT_Q2SM ? dm[i] : 0u);
       }
     }
+    __syncthreads();
   }
 }
 
-struct DecodeWs {
-  int32_t* plan;
-  float* h;
-  float* o;
-};
+// y = x + sum_i w_i * P(u(t,i)) + P(shared), P(u) = sum over slices of u's
+// partials.  Workgroup: 64 rows x 16 term lanes; a thread sums the slices of
+// terms g, g+16, ... for its row (all loads of a term issued together), the
+// row's 64 threads of lane 0 then add the terms in k-slot order.
+constexpr int KB_ROWS = 64;
+constexpr int KB_TERMS = 16;
 
-DecodeWs decode_ws(void* ws, int d, int f, int T, int k) {
-  char* p = static_cast<char*>(ws);
-  DecodeWs w;
-  w.plan = reinterpret_cast<int32_t*>(p);
-  p += align256(kPlanInts * 4);
-  w.h = reinterpret_cast<float*>(p);
-  p += align256(static_cast<int64_t>(T * k + 1) * T * f * 4);
-  w.o = reinterpret_cast<float*>(p);
-  return w;
+__global__ __launch_bounds__(KB_ROWS * KB_TERMS) void decode_combine_kernel(
+    const float* __restrict__ x, const int32_t* __restrict__ slot, const float* __restrict__ w,
+    int T, int k, int d, int nslices, int has_shared, const float* __restrict__ part,
+    float* __restrict__ y) {
+  extern __shared__ float red[];  // [k+1][KB_ROWS]
+  const int t = blockIdx.y;
+  const int rr = threadIdx.x % KB_ROWS;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / KB_ROWS);
+  const int r = blockIdx.x * KB_ROWS + rr;
+  const int n = T * k;
+  const int nterms = k + 1;
+  for (int i = g; i < nterms; i += KB_TERMS) {
+    int uu = -1;
+    if (i < k) {
+      const int sl = slot[t * k + i];
+      if (sl >= 0) {
+        uu = t * k + i;
+        for (int p = 0; p < t * k + i; ++p)
+          if (slot[p] == sl) {
+            uu = p;
+            break;
+          }
+      }
+    } else if (has_shared) {
+      uu = n;
+    }
+    float acc = 0.0f;
+    if (uu >= 0) {
+      const float* src = part + (static_cast<int64_t>(uu) * T + t) * nslices * d + r;
+      int js = 0;
+      for (; js + 8 <= nslices; js += 8) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = src[static_cast<int64_t>(js + q) * d];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc += v[q];
+      }
+      for (; js < nslices; ++js) acc += src[static_cast<int64_t>(js) * d];
+    }
+    red[i * KB_ROWS + rr] = acc;
+  }
+  __syncthreads();
+  if (g != 0) return;
+  float acc = x[static_cast<int64_t>(t) * d + r];
+  for (int i = 0; i < k; ++i)
+    if (slot[t * k + i] >= 0) acc = fmaf(w[t * k + i], red[i * KB_ROWS + rr], acc);
+  if (has_shared) acc += red[k * KB_ROWS + rr];
+  y[static_cast<int64_t>(t) * d + r] = acc;
 }
 
-template <int FMT, int NLPR>
-hipError_t launch_gateup_f(const moe_layer& L, const SlotLayout& lay, int T, const float* x,
-                           const DecodeWs& w, hipStream_t s) {
-  constexpr int RPW = 64 / NLPR;
-  constexpr int J = RPW <= 16 ? 8 : RPW / 2;
-  const dim3 grid(L.d_ff / J, L.top_k * T + 1);
-  decode_gateup_kernel<FMT, NLPR><<<grid, 64, 0, s>>>(
-      static_cast<const uint8_t*>(L.pool), L.slot_bytes, lay.G, L.d_model, L.d_ff, T, L.top_k,
-      L.shared_slot, x, w.plan, w.h);
+size_t part_bytes(int d, int f, int T, int k) {
+  return static_cast<size_t>(static_cast<int64_t>(T * k + 1) * T * (f / SLICE) * d * 4);
+}
+
+template <int FMT>
+hipError_t launch_ffn(const FfnArgs& a, const float* x, hipStream_t s) {
+  const dim3 grid(a.f / SLICE, a.T * a.k + 1);
+  const int nu = a.d / 64;
+  if (nu <= KA_WAVES)
+    decode_ffn_kernel<FMT, 1><<<grid, KA_THREADS, 0, s>>>(a, x);
+  else
+    decode_ffn_kernel<FMT, 2><<<grid, KA_THREADS, 0, s>>>(a, x);
   return hipGetLastError();
-}
-
-template <int FMT>
-hipError_t launch_gateup(const moe_layer& L, const SlotLayout& lay, int T, const float* x,
-                         const DecodeWs& w, hipStream_t s) {
-  switch (L.d_model / 64) {
-    case 1: return launch_gateup_f<FMT, 1>(L, lay, T, x, w, s);
-    case 2: return launch_gateup_f<FMT, 2>(L, lay, T, x, w, s);
-    case 4: return launch_gateup_f<FMT, 4>(L, lay, T, x, w, s);
-    case 8: return launch_gateup_f<FMT, 8>(L, lay, T, x, w, s);
-    case 16: return launch_gateup_f<FMT, 16>(L, lay, T, x, w, s);
-    case 32: return launch_gateup_f<FMT, 32>(L, lay, T, x, w, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <int FMT, int BD, int LD>
-hipError_t launch_down_f(const moe_layer& L, const SlotLayout& lay, int T, const DecodeWs& w,
-                         hipStream_t s) {
-  const dim3 grid(L.d_model / 64, L.top_k * T + 1);
-  decode_down_kernel<FMT, BD, LD><<<grid, 64, 0, s>>>(
-      static_cast<const uint8_t*>(L.pool), L.slot_bytes, lay.D, L.d_model, L.d_ff, T, L.top_k,
-      L.shared_slot, w.plan, w.h, w.o);
-  return hipGetLastError();
-}
-
-template <int FMT, int BD>
-hipError_t launch_down_bd(const moe_layer& L, const SlotLayout& lay, int T, const DecodeWs& w,
-                          hipStream_t s) {
-  switch (L.d_ff / 32 / BD) {
-    case 1: return launch_down_f<FMT, BD, 1>(L, lay, T, w, s);
-    case 2: return launch_down_f<FMT, BD, 2>(L, lay, T, w, s);
-    case 4: return launch_down_f<FMT, BD, 4>(L, lay, T, w, s);
-    case 8: return launch_down_f<FMT, BD, 8>(L, lay, T, w, s);
-    case 16: return launch_down_f<FMT, BD, 16>(L, lay, T, w, s);
-    case 32: return launch_down_f<FMT, BD, 32>(L, lay, T, w, s);
-    case 64: return launch_down_f<FMT, BD, 64>(L, lay, T, w, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <int FMT>
-hipError_t launch_down(const moe_layer& L, const SlotLayout& lay, int T, const DecodeWs& w,
-                       hipStream_t s) {
-  const int nb = L.d_ff / 32;
-  if (nb % 3 == 0) return launch_down_bd<FMT, 3>(L, lay, T, w, s);
-  return launch_down_bd<FMT, 1>(L, lay, T, w, s);
-}
-
-template <int FMT>
-hipError_t launch_decode_fmt(const moe_layer& L, const float* x, int T, const float* wts,
-                             float* y, const DecodeWs& w, hipStream_t s) {
-  const SlotLayout lay = slot_layout(L.fmt, L.d_model, L.d_ff);
-  hipError_t e = launch_gateup<FMT>(L, lay, T, x, w, s);
-  if (e != hipSuccess) return e;
-  e = launch_down<FMT>(L, lay, T, w, s);
-  if (e != hipSuccess) return e;
-  const float* shared = L.shared_slot >= 0
-                            ? w.o + static_cast<int64_t>(T) * L.top_k * T * L.d_model
-                            : nullptr;
-  return launch_combine(x, MOE_DTYPE_F32, T, L.d_model, L.top_k, w.o, w.plan + kPlanPairPos,
-                        wts, shared, y, s);
 }
 
 }  // namespace
 
 size_t decode_workspace_bytes(int d, int f, int T, int k) {
-  return static_cast<size_t>(align256(kPlanInts * 4) +
-                             align256(static_cast<int64_t>(T * k + 1) * T * f * 4) +
-                             align256(static_cast<int64_t>(T * k + 1) * T * d * 4));
+  return static_cast<size_t>(align256(static_cast<int64_t>(part_bytes(d, f, T, k))));
 }
 
 hipError_t launch_decode(const moe_layer& L, const float* x, int T, const int32_t* idx,
                          const int32_t* slot, const float* w, float* y, void* ws,
                          hipStream_t s) {
   (void)idx;
-  const DecodeWs dw = decode_ws(ws, L.d_model, L.d_ff, T, L.top_k);
-  decode_plan_kernel<<<1, 64, 0, s>>>(slot, T, L.top_k, dw.plan);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const SlotLayout lay = slot_layout(L.fmt, L.d_model, L.d_ff);
+  FfnArgs a;
+  a.pool = static_cast<const uint8_t*>(L.pool);
+  a.slot_bytes = L.slot_bytes;
+  a.G = lay.G;
+  a.D = lay.D;
+  a.d = L.d_model;
+  a.f = L.d_ff;
+  a.T = T;
+  a.k = L.top_k;
+  a.shared_slot = L.shared_slot;
+  a.slot = slot;
+  a.part = static_cast<float*>(ws);
+  hipError_t e;
   switch (L.fmt) {
-    case MOE_FMT_Q2S: return launch_decode_fmt<MOE_FMT_Q2S>(L, x, T, w, y, dw, s);
-    case MOE_FMT_Q2SM: return launch_decode_fmt<MOE_FMT_Q2SM>(L, x, T, w, y, dw, s);
-    case MOE_FMT_Q3G: return launch_decode_fmt<MOE_FMT_Q3G>(L, x, T, w, y, dw, s);
+    case MOE_FMT_Q2S: e = launch_ffn<MOE_FMT_Q2S>(a, x, s); break;
+    case MOE_FMT_Q2SM: e = launch_ffn<MOE_FMT_Q2SM>(a, x, s); break;
+    case MOE_FMT_Q3G: e = launch_ffn<MOE_FMT_Q3G>(a, x, s); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess) return e;
+  const dim3 grid(L.d_model / KB_ROWS, T);
+  const size_t lds = static_cast<size_t>(L.top_k + 1) * KB_ROWS * 4;
+  decode_combine_kernel<<<grid, KB_ROWS * KB_TERMS, lds, s>>>(
+      x, slot, w, T, L.top_k, L.d_model, L.d_ff / SLICE, L.shared_slot >= 0 ? 1 : 0, a.part, y);
+  return hipGetLastError();
 }
 
 }  // namespace bitffn

@@ -74,15 +74,20 @@ __device__ __forceinline__ int tile_token(const GroupInfo& g, const TileInfo& ti
   return m;
 }
 
+// Bit of a block's 32-bit hi word that holds bit 2 of code j.
+__device__ __forceinline__ int hi_bit(int j) { return j < 16 ? 2 * j + 1 : 2 * (j - 16); }
+
+// Dequantize one 32-weight block (codes at byte offset oc, scale at os, min at
+// om, hi word at oh, all from `base`) to bf16 and store 64 bytes at dst.
 template <int FMT>
-__device__ __forceinline__ void dequant_block_to_lds(const uint8_t* base, const Planes& P,
-                                                     int64_t blk, __bf16* dst) {
-  const uint2 cw = *reinterpret_cast<const uint2*>(base + P.codes + blk * 8);
-  const float s = half_bits_to_float(*reinterpret_cast<const uint16_t*>(base + P.scale + blk * 2));
+__device__ __forceinline__ void dequant_block_to_lds(const uint8_t* base, int64_t oc, int64_t os,
+                                                     int64_t om, int64_t oh, __bf16* dst) {
+  const uint2 cw = *reinterpret_cast<const uint2*>(base + oc);
+  const float s = half_bits_to_float(*reinterpret_cast<const uint16_t*>(base + os));
   float m = 0.0f;
   uint32_t hi = 0;
-  if (FMT == MOE_FMT_Q2SM) m = half_bits_to_float(*reinterpret_cast<const uint16_t*>(base + P.min + blk * 2));
-  if (FMT == MOE_FMT_Q3G) hi = *reinterpret_cast<const uint32_t*>(base + P.hi + blk * 4);
+  if (FMT == MOE_FMT_Q2SM) m = half_bits_to_float(*reinterpret_cast<const uint16_t*>(base + om));
+  if (FMT == MOE_FMT_Q3G) hi = *reinterpret_cast<const uint32_t*>(base + oh);
   uint32_t packed[16];
 #pragma unroll
   for (int j = 0; j < 32; j += 2) {
@@ -91,8 +96,8 @@ __device__ __forceinline__ void dequant_block_to_lds(const uint8_t* base, const 
     uint32_t q0 = (word >> sh) & 3u;
     uint32_t q1 = (word >> (sh + 2)) & 3u;
     if (FMT == MOE_FMT_Q3G) {
-      q0 |= ((hi >> j) & 1u) << 2;
-      q1 |= ((hi >> (j + 1)) & 1u) << 2;
+      q0 |= ((hi >> hi_bit(j)) & 1u) << 2;
+      q1 |= ((hi >> hi_bit(j + 1)) & 1u) << 2;
     }
     const uint32_t b0 = float_to_bf16_rne(dequant_one<FMT>(q0, s, m));
     const uint32_t b1 = float_to_bf16_rne(dequant_one<FMT>(q1, s, m));
@@ -122,7 +127,6 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int nb = K / 32;                     // blocks per weight row
 
   for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
     const int mt = tile / n_tiles;
@@ -176,9 +180,25 @@ __global__ __launch_bounds__(256) void prefill_gemm_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) dst[q] = v[q];
       }
-      // B tile: 128 rows x 2 blocks, one block per thread
-      dequant_block_to_lds<FMT>(base, P, b_row * nb + k0 / 32 + b_blk,
-                                Bs + b_n * LDS_STRIDE + 32 * b_blk);
+      // B tile: 128 rows x 2 blocks, one block per thread.  G is stored in
+      // units of 2 blocks, D in units of 1 block; unit c of row r at c*rows + r.
+      {
+        int64_t oc, os, om, oh;
+        if (GATEUP) {
+          const int64_t unit = static_cast<int64_t>(k0 / 64) * (2 * static_cast<int64_t>(f)) + b_row;
+          oc = P.codes + unit * 16 + 8 * b_blk;
+          os = P.scale + unit * 4 + 2 * b_blk;
+          om = P.min + unit * 4 + 2 * b_blk;
+          oh = P.hi + unit * 8 + 4 * b_blk;
+        } else {
+          const int64_t unit = static_cast<int64_t>(k0 / 32 + b_blk) * d + b_row;
+          oc = P.codes + unit * 8;
+          os = P.scale + unit * 2;
+          om = P.min + unit * 2;
+          oh = P.hi + unit * 4;
+        }
+        dequant_block_to_lds<FMT>(base, oc, os, om, oh, Bs + b_n * LDS_STRIDE + 32 * b_blk);
+      }
       __syncthreads();
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {

@@ -1,11 +1,11 @@
 // Router top-k: one 64-wide wavefront per token.
 //
-// Each lane keeps NPL candidate keys (expert e = lane + 64*j).  A key packs
-// the logit into an order-preserving 32-bit integer (high word) and the
-// complement of the expert id (low word), so the unsigned 64-bit maximum is
-// the largest logit with the smallest id.  k rounds of a wavefront max-reduce
-// pick the experts in rank order; the winner's lane retires the key.  The
-// softmax over the k chosen logits is then taken across lanes 0..k-1.
+// Each lane keeps NPL logits (expert e = lane + 64*j) as order-preserving
+// 32-bit keys.  Each of the k rounds takes the wavefront maximum key with DPP
+// row rotations plus four lane reads (no LDS traffic), then finds the
+// smallest expert id holding that key with one ballot per register (ids grow
+// with j first, then with the lane), and retires that entry.  The softmax
+// over the k chosen logits is then taken across lanes 0..k-1.
 #include "moe_internal.h"
 
 namespace bitffn {
@@ -23,15 +23,23 @@ __device__ __forceinline__ float from_orderable(uint32_t u) {
   return __builtin_bit_cast(float, b);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, 64);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, 64);
-    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_dpp(uint32_t v) {
+  const uint32_t o = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+  return o > v ? o : v;
+}
+
+// maximum over the wavefront, returned uniform
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max_dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = max_dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = max_dpp<0x124>(v);   // row_ror:4
+  v = max_dpp<0x128>(v);   // row_ror:8
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -49,29 +57,33 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;  // uniform per wavefront
   const float* row = logits + static_cast<int64_t>(t) * E;
 
-  uint64_t key[NPL];
+  // key 0 marks an empty entry: every real key is >= orderable(-inf) > 0
+  uint32_t key[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int e = lane + 64 * j;
-    key[j] = 0;
-    if (e < E) {
-      key[j] = (static_cast<uint64_t>(orderable(row[e])) << 32) | static_cast<uint32_t>(~e);
-    }
+    key[j] = e < E ? orderable(row[e]) : 0u;
   }
 
   float my_val = 0.0f;
   int my_idx = 0;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = key[0];
+    uint32_t best = key[0];
 #pragma unroll
     for (int j = 1; j < NPL; ++j) best = key[j] > best ? key[j] : best;
-    best = wave_max_u64(best);
+    best = wave_max_u32(best);
+    int winner = 0;
+#pragma unroll
+    for (int j = NPL - 1; j >= 0; --j) {  // smallest id: lowest j, then lowest lane
+      const uint64_t bal = __ballot(key[j] == best);
+      if (bal) winner = 64 * j + __builtin_ctzll(bal);
+    }
 #pragma unroll
     for (int j = 0; j < NPL; ++j)
-      if (key[j] == best) key[j] = 0;
+      if (lane + 64 * j == winner) key[j] = 0u;
     if (lane == r) {
-      my_idx = static_cast<int>(~static_cast<uint32_t>(best));
-      my_val = from_orderable(static_cast<uint32_t>(best >> 32));
+      my_idx = winner;
+      my_val = from_orderable(best);
     }
   }
 

@@ -66,12 +66,17 @@ extern "C" {
  *                 (the grid -3.5..3.5 in steps of 1, times s / 3.5)
  * Slot layout (bytes of one expert): matrix G = 2*d_ff rows x d_model
  * columns (row 2j = gate row j, row 2j+1 = up row j), then matrix
- * D = d_model rows x d_ff columns (down projection).  Each matrix is
- * row-major in blocks and stored as planes, each starting 256-byte aligned
- * from the slot start, in this order:
+ * D = d_model rows x d_ff columns (down projection).  Rows are cut into
+ * 32-weight blocks.  A matrix is stored in units of U consecutive blocks of
+ * one row (U = 2 for G, U = 1 for D); with R rows, unit c of row r has index
+ * c*R + r, so one unit of consecutive rows is contiguous.  Each matrix is a
+ * sequence of planes, each starting 256-byte aligned from the slot start and
+ * holding its units in index order (inside a unit the U blocks follow each
+ * other):
  *   codes (8 B/block: code i at bits [2i,2i+2) of the little-endian 64-bit
  *          word; for Q3G the low two bits),
- *   hi    (Q3G only, 4 B/block: bit i = bit 2 of code i),
+ *   hi    (Q3G only, 4 B/block: bit 2i+1 holds bit 2 of code i for i < 16,
+ *          bit 2(i-16) holds it for i >= 16),
  *   scale (fp16, 2 B/block),
  *   min   (Q2SM only, fp16, 2 B/block).
  * The slot size is rounded up to 256 bytes; moe_slot_bytes() returns it. */
@@ -91,8 +96,8 @@ extern "C" {
 /* One MoE layer as it sits in device memory (host struct, read during the
  * call only). */
 typedef struct moe_layer {
-  int32_t d_model;     /* multiple of 64, a power of two in 64..2048        */
-  int32_t d_ff;        /* multiple of 32; d_ff/32 = 2^n or 3 * 2^n, <= 64   */
+  int32_t d_model;     /* multiple of 64 in 64..2048                        */
+  int32_t d_ff;        /* multiple of 32 in 32..4096                        */
   int32_t n_experts;   /* 1..MOE_MAX_EXPERTS routed experts                  */
   int32_t top_k;       /* 1..min(n_experts, MOE_MAX_TOPK)                    */
   int32_t fmt;         /* MOE_FMT_*                                          */

@@ -50,7 +50,8 @@ def plane_offsets(fmt, d_model, d_ff):
     """Byte offset of every plane of the two matrices inside one slot.
 
     G (2*d_ff x d_model, gate row j at 2j, up row j at 2j+1) comes first,
-    then D (d_model x d_ff).  Planes are 256-byte aligned from the slot start.
+    then D (d_model x d_ff).  Planes are 256-byte aligned from the slot start;
+    a plane holds per-block data (codes 8 B, hi 4 B, scale 2 B, min 2 B).
     """
     offs = {}
     pos = 0
@@ -73,6 +74,11 @@ def _grid_q3g():
     return np.array([-3.5, -2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 3.5], dtype=np.float64)
 
 
+def _hi_position(i):
+    """Bit of the 32-bit hi word that holds bit 2 of code i of a block."""
+    return 2 * i + 1 if i < 16 else 2 * (i - 16)
+
+
 def unpack_matrix(slot, fmt, d_model, d_ff, which):
     """Dequantize matrix `which` ('G' or 'D') of one packed slot to float64.
 
@@ -84,24 +90,30 @@ def unpack_matrix(slot, fmt, d_model, d_ff, which):
       Q3G : w = s * grid[q] / 3.5          q = lo2 + 4 * hi1, grid above
     s, m are IEEE fp16 read exactly; every product and sum here is exact
     in float64 except the Q3G division by 3.5.
+
+    Storage order: units of U blocks of one row (U = 2 for G, 1 for D);
+    unit c of row r is the (c * rows + r)-th unit of every plane.
     """
     slot = np.asarray(slot, dtype=np.uint8).reshape(-1)
     rows, cols = (2 * d_ff, d_model) if which == "G" else (d_model, d_ff)
     nb = cols // _BLK
+    U = 2 if which == "G" else 1
     nblocks = rows * nb
     offs = plane_offsets(fmt, d_model, d_ff)
 
     def plane(name, per):
         o = offs[(which, name)]
-        return slot[o:o + nblocks * per]
+        raw = slot[o:o + nblocks * per].reshape(nb // U, rows, U, per)
+        # -> blocks in row-major order: [row][block in row][bytes]
+        return np.ascontiguousarray(raw.transpose(1, 0, 2, 3)).reshape(-1)
 
     word = plane("codes", 8).view("<u8").astype(np.uint64)          # [nblocks]
     shifts = (2 * np.arange(_BLK)).astype(np.uint64)
     q = ((word[:, None] >> shifts[None, :]) & np.uint64(3)).astype(np.int64)
     if fmt == FMT_Q3G:
         hiw = plane("hi", 4).view("<u4").astype(np.uint64)
-        bits = ((hiw[:, None] >> np.arange(_BLK, dtype=np.uint64)[None, :])
-                & np.uint64(1)).astype(np.int64)
+        hpos = np.array([_hi_position(i) for i in range(_BLK)], dtype=np.uint64)
+        bits = ((hiw[:, None] >> hpos[None, :]) & np.uint64(1)).astype(np.int64)
         q = q + 4 * bits
     s = plane("scale", 2).view("<f2").astype(np.float64)[:, None]
     if fmt == FMT_Q2S:

@@ -14,15 +14,20 @@ each implements its own reader):
   - G has 2*d_ff rows and d_model columns; row 2j is the gate row j and row
     2j+1 is the up row j.
   - D has d_model rows and d_ff columns (the down projection).
-* Each matrix is row-major and cut into blocks of 32 consecutive weights
-  along a row.  Its bytes are a sequence of planes, each starting on a
-  256-byte boundary measured from the slot start:
+* Rows are cut into blocks of 32 consecutive weights.  A matrix is stored in
+  units of U consecutive blocks of one row (U = 2 for G, U = 1 for D); with R
+  rows, unit c of row r has index c*R + r, so one unit of 64 consecutive rows
+  is contiguous.  Each matrix is a sequence of planes, each starting on a
+  256-byte boundary measured from the slot start, each holding the units in
+  index order:
   - codes: 8 bytes per block; code i of the block sits at bits [2i, 2i+2) of
     the little-endian 64-bit word (for the 3-bit format: the low two bits).
-  - hi (3-bit format only): 4 bytes per block; bit i of the little-endian
-    32-bit word is bit 2 of code i.
+  - hi (3-bit format only): 4 bytes per block, a little-endian 32-bit word in
+    which bit 2i+1 is bit 2 of code i for i < 16 and bit 2(i-16) is bit 2 of
+    code i for i >= 16.
   - scale: one IEEE fp16 per block.
   - min (2-bit scale+min format only): one IEEE fp16 per block.
+  Inside a unit the U blocks follow each other in every plane.
 * The slot size is rounded up to 256 bytes.
 
 Formats and how a code decodes (the quantizer below only has to produce codes
@@ -117,6 +122,9 @@ def _planes(fmt: int):
     raise ValueError(f"unknown format {fmt}")
 
 
+UNIT_BLOCKS = {"G": 2, "D": 1}
+
+
 def slot_layout(fmt: int, d_model: int, d_ff: int) -> dict:
     """{('G'|'D', plane): (offset, bytes)} plus 'total'."""
     out = {}
@@ -165,21 +173,30 @@ def quantize_blocks(w: torch.Tensor, fmt: int):
     raise ValueError(f"unknown format {fmt}")
 
 
+def _hi_bit_positions():
+    pos = torch.empty(32, dtype=torch.int64)
+    for i in range(32):
+        pos[i] = 2 * i + 1 if i < 16 else 2 * (i - 16)
+    return pos
+
+
 def pack_matrix_planes(codes: torch.Tensor, s16: torch.Tensor, m16, fmt: int) -> dict:
-    """codes uint8 [..., nb, 32] -> {plane: uint8 tensor [..., nb*per]}."""
+    """codes uint8 [..., nb, 32] -> {plane: uint8 tensor [..., nb, per]}
+    in the order of the leading dimensions (no unit reordering here)."""
     lead = codes.shape[:-1]  # [..., nb]
     c = codes.to(torch.int32)
     sh2 = torch.tensor([0, 2, 4, 6], dtype=torch.int32, device=codes.device)
     lo = (c & 3).reshape(*lead, 8, 4)
-    code_bytes = (lo << sh2).sum(-1).to(torch.uint8)            # [..., nb, 8]
-    out = {"codes": code_bytes.reshape(*lead[:-1], -1)}
+    out = {"codes": (lo << sh2).sum(-1).to(torch.uint8)}                # [..., nb, 8]
     if fmt == FMT_Q3G:
-        sh1 = torch.arange(8, dtype=torch.int32, device=codes.device)
-        hi = ((c >> 2) & 1).reshape(*lead, 4, 8)
-        out["hi"] = (hi << sh1).sum(-1).to(torch.uint8).reshape(*lead[:-1], -1)
-    out["scale"] = s16.contiguous().view(torch.uint8).reshape(*lead[:-1], -1)
+        bit = ((c >> 2) & 1).to(torch.int64)                             # [..., nb, 32]
+        pos = _hi_bit_positions().to(codes.device)
+        word = (bit << pos).sum(-1)                                      # [..., nb]
+        sh = torch.tensor([0, 8, 16, 24], dtype=torch.int64, device=codes.device)
+        out["hi"] = ((word.unsqueeze(-1) >> sh) & 255).to(torch.uint8)   # [..., nb, 4]
+    out["scale"] = s16.contiguous().view(torch.uint8).reshape(*lead, 2)
     if fmt == FMT_Q2SM:
-        out["min"] = m16.contiguous().view(torch.uint8).reshape(*lead[:-1], -1)
+        out["min"] = m16.contiguous().view(torch.uint8).reshape(*lead, 2)
     return out
 
 
@@ -193,13 +210,16 @@ def pack_expert_slots(G: torch.Tensor, D: torch.Tensor, fmt: int) -> torch.Tenso
     out = torch.zeros((n, lay["total"]), dtype=torch.uint8, device=G.device)
     for mat, W in (("G", G), ("D", D)):
         rows, cols = W.shape[1], W.shape[2]
-        codes, s16, m16 = quantize_blocks(W.reshape(n, rows, cols // BLOCK, BLOCK), fmt)
-        planes = pack_matrix_planes(codes.reshape(n, rows * (cols // BLOCK), BLOCK),
-                                    s16.reshape(n, -1),
-                                    None if m16 is None else m16.reshape(n, -1), fmt)
+        nb = cols // BLOCK
+        U = UNIT_BLOCKS[mat]
+        codes, s16, m16 = quantize_blocks(W.reshape(n, rows, nb, BLOCK), fmt)
+        planes = pack_matrix_planes(codes, s16, m16, fmt)            # [n, rows, nb, per]
         for name, data in planes.items():
+            per = data.shape[-1]
+            # [n, rows, nb/U, U, per] -> [n, nb/U, rows, U, per]: unit c of row r at c*rows + r
+            unit = data.reshape(n, rows, nb // U, U, per).permute(0, 2, 1, 3, 4)
             off, nbytes = lay[(mat, name)]
-            flat = data.reshape(n, -1)
+            flat = unit.reshape(n, -1)
             assert flat.shape[1] == nbytes, (mat, name, flat.shape, nbytes)
             out[:, off:off + nbytes] = flat
     return out

@@ -49,7 +49,8 @@ def test_version_and_status_strings():
 
 
 @pytest.mark.parametrize("fmt", [1, 2, 3])
-@pytest.mark.parametrize("d,f", [(64, 32), (256, 128), (2048, 768), (512, 96), (1024, 2048)])
+@pytest.mark.parametrize("d,f", [(64, 32), (256, 128), (2048, 768), (512, 96), (1024, 2048),
+                                 (192, 160)])
 def test_slot_bytes_matches_layouts(fmt, d, f):
     lib = _lib()
     got = lib.moe_slot_bytes(fmt, d, f)
@@ -59,10 +60,10 @@ def test_slot_bytes_matches_layouts(fmt, d, f):
 def test_slot_bytes_rejects():
     lib = _lib()
     assert lib.moe_slot_bytes(4, 256, 128) == -3
-    assert lib.moe_slot_bytes(2, 96, 128) == -1       # d not a power of two
+    assert lib.moe_slot_bytes(2, 96, 128) == -1       # d not a multiple of 64
     assert lib.moe_slot_bytes(2, 4096, 128) == -1     # d too large
-    assert lib.moe_slot_bytes(2, 256, 160) == -1      # 5 blocks per row
-    assert lib.moe_slot_bytes(2, 256, 4096) == -1     # d_ff too large
+    assert lib.moe_slot_bytes(2, 256, 80) == -1       # d_ff not a multiple of 32
+    assert lib.moe_slot_bytes(2, 256, 8192) == -1     # d_ff too large
 
 
 FAKE = 0x7F0000000000  # never dereferenced: every call below fails its host checks

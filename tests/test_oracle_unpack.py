@@ -30,17 +30,18 @@ def _parse(path):
             spec["size"] = int(tok[1])
         elif tok[0] == "write":
             spec["writes"].append((int(tok[1]), bytes.fromhex(tok[2])))
-        elif tok[0] == "expect":
+        elif tok[0] == "expect_block_rl":
             vals = []
-            rest = tok[3:]
+            rest = tok[4:]
             for j in range(0, len(rest), 2):
                 vals += [float(rest[j])] * int(rest[j + 1].lstrip("x"))
             assert len(vals) == 32, path
-            spec["expect"].append((tok[1], int(tok[2]), np.array(vals)))
-        elif tok[0] == "expect_pattern":
-            pat = [float(v) for v in tok[3:]]
+            spec["expect"].append((tok[1], int(tok[2]), int(tok[3]), np.array(vals)))
+        elif tok[0] == "expect_block":
+            pat = [float(v) for v in tok[4:]]
             assert 32 % len(pat) == 0
-            spec["expect"].append((tok[1], int(tok[2]), np.array(pat * (32 // len(pat)))))
+            spec["expect"].append((tok[1], int(tok[2]), int(tok[3]),
+                                   np.array(pat * (32 // len(pat)))))
         else:
             raise ValueError(line)
     return spec
@@ -52,26 +53,27 @@ GOLDEN = sorted(glob.glob(os.path.join(os.path.dirname(__file__), "golden", "*.t
 @pytest.mark.parametrize("path", GOLDEN, ids=[os.path.basename(p) for p in GOLDEN])
 def test_hand_built_blocks(path):
     spec = _parse(path)
-    d = f = 32
+    d = f = 64
     assert oracle.slot_size(spec["fmt"], d, f) == spec["size"]
     slot = np.zeros(spec["size"], dtype=np.uint8)
     for off, data in spec["writes"]:
         slot[off:off + len(data)] = np.frombuffer(data, dtype=np.uint8)
     mats = {m: oracle.unpack_matrix(slot, spec["fmt"], d, f, m) for m in "GD"}
     named = set()
-    for m, row, vals in spec["expect"]:
-        np.testing.assert_array_equal(mats[m][row], vals)
-        named.add((m, row))
+    for m, row, blk, vals in spec["expect"]:
+        np.testing.assert_array_equal(mats[m][row, 32 * blk:32 * blk + 32], vals)
+        named.add((m, row, blk))
     for m in "GD":
         for r in range(mats[m].shape[0]):
-            if (m, r) not in named:
-                assert not mats[m][r].any(), (m, r)
+            for b in range(2):
+                if (m, r, b) not in named:
+                    assert not mats[m][r, 32 * b:32 * b + 32].any(), (m, r, b)
 
 
 def test_plane_offsets_against_generator_layout():
     # two independent layout implementations must agree
     for fmt in FMTS.values():
-        for d, f in ((32, 32), (256, 128), (2048, 768), (64, 96)):
+        for d, f in ((64, 64), (256, 128), (2048, 768), (64, 96)):
             lay = synth.slot_layout(fmt, d, f)
             offs = oracle.plane_offsets(fmt, d, f)
             assert lay["total"] == offs["end"]
@@ -83,7 +85,7 @@ def test_plane_offsets_against_generator_layout():
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 def test_quantizer_roundtrip(fmt):
     """synth quantize+pack -> oracle unpack stays within half a step."""
-    d, f = 256, 128
+    d, f = 256, 96
     gen = torch.Generator().manual_seed(1234 + fmt)
     G = torch.randn(2, 2 * f, d, generator=gen) * 0.02
     D = torch.randn(2, d, f, generator=gen) * 0.02
