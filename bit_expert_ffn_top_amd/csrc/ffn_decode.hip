@@ -35,7 +35,8 @@ typedef const __attribute__((address_space(4))) float cfloat;
 constexpr int KA_THREADS = 1024;
 constexpr int KA_WAVES = KA_THREADS / 64;
 constexpr int SLICE = 32;          // h indices per workgroup
-constexpr int MAX_DROWS = 2;       // D rows per thread: d_model <= 2048
+constexpr int MAX_DROWS = 2048 / KA_THREADS;   // D rows per thread: d_model <= 2048
+static_assert(2048 / 64 <= 4 * KA_WAVES, "G units per wavefront above 4");
 
 struct FfnArgs {
   const uint8_t* pool;
@@ -46,9 +47,11 @@ struct FfnArgs {
   float* part;  // [(T*k+1) * T][f/32][d]
 };
 
-// Union member u: its slot and the mask of tokens it serves.
-__device__ __forceinline__ bool union_member(const int32_t* __restrict__ slot, int T, int k,
-                                             int shared_slot, int u, int& s, uint32_t& mask) {
+// Union member u: its slot and the mask of tokens it serves.  `sp` is the
+// slot of pair `lane` (-1 for lanes >= T*k; T*k <= 64), so the test is a
+// lane read and a ballot; the result is uniform across the wavefront.
+__device__ __forceinline__ bool union_member(int sp, int T, int k, int shared_slot, int u,
+                                             int& s, uint32_t& mask) {
   const int n = T * k;
   if (u == n) {
     if (shared_slot < 0) return false;
@@ -56,19 +59,34 @@ __device__ __forceinline__ bool union_member(const int32_t* __restrict__ slot, i
     mask = (1u << T) - 1u;
     return true;
   }
-  s = slot[u];
+  s = __builtin_amdgcn_readlane(sp, u);
   if (s < 0) return false;
-  for (int p = 0; p < u; ++p)
-    if (slot[p] == s) return false;
+  const uint64_t same = __ballot(sp == s);
+  if (same & ((1ull << u) - 1ull)) return false;   // an earlier pair names this slot
+  const uint64_t kmask = k >= 64 ? ~0ull : (1ull << k) - 1ull;
   mask = 0;
-  for (int p = u; p < n; ++p)
-    if (slot[p] == s) mask |= 1u << (p / k);
+  for (int t = 0; t < T; ++t)
+    if ((same >> (t * k)) & kmask) mask |= 1u << t;
   return true;
 }
 
 // value of v in lane `src` (uniform result)
 __device__ __forceinline__ float lane_value(float v, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                 0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// sum over each row of 16 lanes, complete in every lane of the row
+__device__ __forceinline__ float row16_sum(float v) {
+  v = add_dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = add_dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = add_dpp<0x124>(v);   // row_ror:4
+  return add_dpp<0x128>(v);   // row_ror:8
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -84,13 +102,28 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
                                                                 const float* __restrict__ x) {
   const int js = blockIdx.x;
   const int u = blockIdx.y;
-  int s;
-  uint32_t mask;
-  if (!union_member(a.slot, a.T, a.k, a.shared_slot, u, s, mask)) return;
-  const uint8_t* __restrict__ base = a.pool + static_cast<int64_t>(s) * a.slot_bytes;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int d = a.d;
+  const int sp = lane < a.T * a.k ? a.slot[lane] : -1;
+
+  // Every load below is unconditional, with indices clamped into range (the
+  // surplus values are never used), so the compiler can count outstanding
+  // loads and wait for each group alone.  Order: the pair slots, x (needed
+  // first, by the block sums), G units in the order they are used, then D.
+  float2 xv[MOE_MAX_DECODE_T];
+  const int ex = min(2 * tid, d - 2);
+#pragma unroll
+  for (int t = 0; t < MOE_MAX_DECODE_T; ++t) {
+    const int tt = min(t, a.T - 1);
+    xv[t] = *reinterpret_cast<const float2*>(x + static_cast<int64_t>(tt) * d + ex);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep the issue order
+
+  int s;
+  uint32_t mask;
+  if (!union_member(sp, a.T, a.k, a.shared_slot, u, s, mask)) return;
+  const uint8_t* __restrict__ base = a.pool + static_cast<int64_t>(s) * a.slot_bytes;
   const int64_t R = 2 * static_cast<int64_t>(a.f);   // G rows
   const int64_t grow = 2 * SLICE * js + lane;        // this lane's G row
   const int nu = d / 64;
@@ -101,70 +134,49 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
   uint2 gh[UPW];
 #pragma unroll
   for (int i = 0; i < UPW; ++i) {
-    if (wave + KA_WAVES * i < nu) {
-      const int64_t unit = static_cast<int64_t>(wave + KA_WAVES * i) * R + grow;
-      gc[i] = *reinterpret_cast<const uint4*>(base + a.G.codes + unit * 16);
-      gs[i] = *reinterpret_cast<const uint32_t*>(base + a.G.scale + unit * 4);
-      if (FMT == MOE_FMT_Q2SM) gm[i] = *reinterpret_cast<const uint32_t*>(base + a.G.min + unit * 4);
-      if (FMT == MOE_FMT_Q3G) gh[i] = *reinterpret_cast<const uint2*>(base + a.G.hi + unit * 8);
-    }
+    const int64_t unit = static_cast<int64_t>(min(wave + KA_WAVES * i, nu - 1)) * R + grow;
+    gc[i] = *reinterpret_cast<const uint4*>(base + a.G.codes + unit * 16);
+    gs[i] = *reinterpret_cast<const uint32_t*>(base + a.G.scale + unit * 4);
+    if (FMT == MOE_FMT_Q2SM) gm[i] = *reinterpret_cast<const uint32_t*>(base + a.G.min + unit * 4);
+    if (FMT == MOE_FMT_Q3G) gh[i] = *reinterpret_cast<const uint2*>(base + a.G.hi + unit * 8);
   }
+  __builtin_amdgcn_sched_barrier(0);
   const int ndr = (d - tid + KA_THREADS - 1) / KA_THREADS;   // D rows of this thread
   uint2 dc[MAX_DROWS];
   uint32_t ds[MAX_DROWS], dm[MAX_DROWS], dh[MAX_DROWS];
 #pragma unroll
   for (int i = 0; i < MAX_DROWS; ++i) {
-    if (i < ndr) {
-      const int64_t unit = static_cast<int64_t>(js) * d + tid + KA_THREADS * i;
-      dc[i] = *reinterpret_cast<const uint2*>(base + a.D.codes + unit * 8);
-      ds[i] = *reinterpret_cast<const uint16_t*>(base + a.D.scale + unit * 2);
-      if (FMT == MOE_FMT_Q2SM) dm[i] = *reinterpret_cast<const uint16_t*>(base + a.D.min + unit * 2);
-      if (FMT == MOE_FMT_Q3G) dh[i] = *reinterpret_cast<const uint32_t*>(base + a.D.hi + unit * 4);
-    }
+    const int64_t unit = static_cast<int64_t>(js) * d + min(tid + KA_THREADS * i, d - 1);
+    dc[i] = *reinterpret_cast<const uint2*>(base + a.D.codes + unit * 8);
+    ds[i] = *reinterpret_cast<const uint16_t*>(base + a.D.scale + unit * 2);
+    if (FMT == MOE_FMT_Q2SM) dm[i] = *reinterpret_cast<const uint16_t*>(base + a.D.min + unit * 2);
+    if (FMT == MOE_FMT_Q3G) dh[i] = *reinterpret_cast<const uint32_t*>(base + a.D.hi + unit * 4);
   }
 
   __shared__ float red[KA_WAVES][64];
-  __shared__ float2 bsum[2048 / 32];   // per block of x: (sum, offset constant)
+  __shared__ float2 bsum[MOE_MAX_DECODE_T][2048 / 32];   // per block of x: (sum, offset constant)
   __shared__ __attribute__((aligned(16))) float hsh[SLICE];
   __shared__ float hsum[2];
 
-  const int nslices = a.f / SLICE;
-  for (int t = 0; t < a.T; ++t) {
-    if (!((mask >> t) & 1u)) continue;
-    // weights stay in registers across tokens
+  // per-block sums of x (sum, offset constant) for every served token: each
+  // thread adds two neighbouring values, the 16 threads of a block reduce by
+  // DPP rotations within their row of 16 lanes; lane 0 of the row stores
+  // (computed for all token slots, stored for served ones: no branch for
+  // the compiler to sink the x loads into)
+  const float cw0 = block_offset_weight<FMT>(ex & 31), cw1 = block_offset_weight<FMT>((ex & 31) + 1);
 #pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-      opaque(gc[i]);
-      opaque(gs[i]);
-      if (FMT == MOE_FMT_Q2SM) opaque(gm[i]);
-      if (FMT == MOE_FMT_Q3G) opaque(gh[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < MAX_DROWS; ++i) {
-      opaque(dc[i]);
-      opaque(ds[i]);
-      if (FMT == MOE_FMT_Q2SM) opaque(dm[i]);
-      if (FMT == MOE_FMT_Q3G) opaque(dh[i]);
-    }
-    const float* __restrict__ xt = x + static_cast<int64_t>(t) * d;
+  for (int t = 0; t < MOE_MAX_DECODE_T; ++t) {
+    const float sx = row16_sum(xv[t].x + xv[t].y);
+    const float sc = row16_sum(fmaf(cw1, xv[t].y, cw0 * xv[t].x));
+    if (((mask >> t) & 1u) && (tid & 15) == 0 && 2 * tid < d)
+      bsum[t][tid >> 4] = make_float2(sx, block_const<FMT>(sx, sc));
+  }
+  __syncthreads();
 
-    // per-block sums of x: thread b < d/32 sums block b (fixed order), LDS
-    for (int b = tid; b < d / 32; b += KA_THREADS) {
-      const float4* p = reinterpret_cast<const float4*>(xt + 32 * b);
-      float sx = 0.0f, sc = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float4 v = p[q];
-        const float xv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          sx += xv[j];
-          sc = fmaf(block_offset_weight<FMT>(4 * q + j), xv[j], sc);
-        }
-      }
-      bsum[b] = make_float2(sx, block_const<FMT>(sx, sc));
-    }
-    __syncthreads();
+  const int nslices = a.f / SLICE;
+  // one served token: gate/up, SiLU gating, partial down product
+  auto token_pass = [&](int t) {
+    const float* __restrict__ xt = x + static_cast<int64_t>(t) * d;
 
     // gate/up rows: partial sums over this wavefront's units (x as scalar
     // operands)
@@ -174,7 +186,7 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
       const int c = wave + KA_WAVES * i;
       if (c < nu) {
         const cfloat* xw = (const cfloat*)(xt + 64 * c);
-        const float2 s0 = bsum[2 * c], s1 = bsum[2 * c + 1];
+        const float2 s0 = bsum[t][2 * c], s1 = bsum[t][2 * c + 1];
         const uint32_t hw0 = FMT == MOE_FMT_Q3G ? gh[i].x : 0u;
         const uint32_t hw1 = FMT == MOE_FMT_Q3G ? gh[i].y : 0u;
         const uint32_t m = FMT == MOE_FMT_Q2SM ? gm[i] : 0u;
@@ -204,83 +216,126 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
     }
     __syncthreads();
 
-    // down: this slice's block column of D, all rows
-    float hv[SLICE];
-#pragma unroll
-    for (int q = 0; q < SLICE / 4; ++q) {
-      const float4 v = reinterpret_cast<const float4*>(hsh)[q];
-      hv[4 * q] = v.x;
-      hv[4 * q + 1] = v.y;
-      hv[4 * q + 2] = v.z;
-      hv[4 * q + 3] = v.w;
-    }
+    // down: this slice's block column of D, all rows.  h is read from LDS
+    // (same address in every lane) 16 values at a time, each half applied to
+    // every row of the thread before the next half is read.
     const float HX = hsum[0], HK = hsum[1];
     float* __restrict__ out = a.part + ((static_cast<int64_t>(u) * a.T + t) * nslices + js) * d;
+    float a0[MAX_DROWS], a1[MAX_DROWS];
+#pragma unroll
+    for (int i = 0; i < MAX_DROWS; ++i) a0[i] = a1[i] = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float hv[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = reinterpret_cast<const float4*>(hsh)[4 * half + q];
+        hv[4 * q] = v.x;
+        hv[4 * q + 1] = v.y;
+        hv[4 * q + 2] = v.z;
+        hv[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int i = 0; i < MAX_DROWS; ++i) {
+        if (i < ndr) {
+          const uint32_t w = half ? dc[i].y : dc[i].x;
+          if (FMT == MOE_FMT_Q3G) {
+            if (half == 0) dot16_q3<0>(w, dh[i], hv, 0, a0[i], a1[i]);
+            else dot16_q3<-1>(w, dh[i], hv, 0, a0[i], a1[i]);
+          } else {
+            dot16_q2(w, hv, 0, a0[i], a1[i]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int i = 0; i < MAX_DROWS; ++i) {
-      if (i < ndr) {
-        const float acc = block_acc<FMT>(dc[i].x, dc[i].y, FMT == MOE_FMT_Q3G ? dh[i] : 0u, hv, 0);
-        out[tid + KA_THREADS * i] =
-            block_finish<FMT>(0.0f, acc, HK, HX, ds[i], FMT == MOE_FMT_Q2SM ? dm[i] : 0u);
-      }
+      if (i < ndr)
+        out[tid + KA_THREADS * i] = block_finish<FMT>(0.0f, a0[i] + a1[i], HK, HX, ds[i],
+                                                      FMT == MOE_FMT_Q2SM ? dm[i] : 0u);
     }
     __syncthreads();
+  };
+
+  // The first served token runs outside the loop, so its arithmetic waits for
+  // each load group alone (entering a loop makes the compiler wait for every
+  // outstanding load).  Later tokens reuse the weights held in registers;
+  // marking them as rewritten each iteration keeps the compiler from hoisting
+  // per-token decode work out of the loop.
+  token_pass(__builtin_ctz(mask));
+  for (uint32_t rest = mask & (mask - 1u); rest != 0u; rest &= rest - 1u) {
+#pragma unroll
+    for (int i = 0; i < UPW; ++i) {
+      opaque(gc[i]);
+      opaque(gs[i]);
+      if (FMT == MOE_FMT_Q2SM) opaque(gm[i]);
+      if (FMT == MOE_FMT_Q3G) opaque(gh[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < MAX_DROWS; ++i) {
+      opaque(dc[i]);
+      opaque(ds[i]);
+      if (FMT == MOE_FMT_Q2SM) opaque(dm[i]);
+      if (FMT == MOE_FMT_Q3G) opaque(dh[i]);
+    }
+    token_pass(__builtin_ctz(rest));
   }
 }
 
 // y = x + sum_i w_i * P(u(t,i)) + P(shared), P(u) = sum over slices of u's
-// partials.  Workgroup: 64 rows x 16 term lanes; a thread sums the slices of
-// terms g, g+16, ... for its row (all loads of a term issued together), the
-// row's 64 threads of lane 0 then add the terms in k-slot order.
-constexpr int KB_ROWS = 64;
-constexpr int KB_TERMS = 16;
+// partials.  Workgroup: 16 rows, one wavefront per term (terms i, i+16, ...);
+// lane = (row r, slice group g of 4), group g sums its quarter of the slices
+// in order (all loads of a chunk issued together), the four group sums meet
+// as (g0 + g1) + (g2 + g3), and wavefront 0 adds the terms in k-slot order,
+// shared last.  Member of term i: the first pair naming the same slot.
+constexpr int KB_ROWS = 16;
+constexpr int KB_GROUPS = 64 / KB_ROWS;
+constexpr int KB_WAVES = 16;
+constexpr int KB_CHUNK = 8;
 
-__global__ __launch_bounds__(KB_ROWS * KB_TERMS) void decode_combine_kernel(
+__global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
     const float* __restrict__ x, const int32_t* __restrict__ slot, const float* __restrict__ w,
     int T, int k, int d, int nslices, int has_shared, const float* __restrict__ part,
     float* __restrict__ y) {
   extern __shared__ float red[];  // [k+1][KB_ROWS]
   const int t = blockIdx.y;
-  const int rr = threadIdx.x % KB_ROWS;
-  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / KB_ROWS);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rr = lane % KB_ROWS, g = lane / KB_ROWS;
   const int r = blockIdx.x * KB_ROWS + rr;
   const int n = T * k;
-  const int nterms = k + 1;
-  for (int i = g; i < nterms; i += KB_TERMS) {
+  const int sp = lane < n ? slot[lane] : -1;
+  const int per = (nslices + KB_GROUPS - 1) / KB_GROUPS;
+  const int j0 = min(nslices, g * per), j1 = min(nslices, j0 + per);
+  for (int i = wave; i < k + 1; i += KB_WAVES) {
     int uu = -1;
     if (i < k) {
-      const int sl = slot[t * k + i];
-      if (sl >= 0) {
-        uu = t * k + i;
-        for (int p = 0; p < t * k + i; ++p)
-          if (slot[p] == sl) {
-            uu = p;
-            break;
-          }
-      }
+      const int sl = __builtin_amdgcn_readlane(sp, t * k + i);
+      if (sl >= 0) uu = __builtin_ctzll(__ballot(sp == sl));
     } else if (has_shared) {
       uu = n;
     }
+    if (uu < 0) continue;   // uniform
+    const float* src = part + (static_cast<int64_t>(uu) * T + t) * nslices * d + r;
     float acc = 0.0f;
-    if (uu >= 0) {
-      const float* src = part + (static_cast<int64_t>(uu) * T + t) * nslices * d + r;
-      int js = 0;
-      for (; js + 8 <= nslices; js += 8) {
-        float v[8];
+    for (int j = j0; j < j1; j += KB_CHUNK) {
+      float v[KB_CHUNK];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = src[static_cast<int64_t>(js + q) * d];
+      for (int q = 0; q < KB_CHUNK; ++q)
+        v[q] = j + q < j1 ? src[static_cast<int64_t>(j + q) * d] : 0.0f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc += v[q];
-      }
-      for (; js < nslices; ++js) acc += src[static_cast<int64_t>(js) * d];
+      for (int q = 0; q < KB_CHUNK; ++q) acc += v[q];
     }
-    red[i * KB_ROWS + rr] = acc;
+    acc += __shfl_xor(acc, KB_ROWS, 64);        // g0+g1, g2+g3
+    acc += __shfl_xor(acc, 2 * KB_ROWS, 64);    // (g0+g1)+(g2+g3)
+    if (g == 0) red[i * KB_ROWS + rr] = acc;
   }
   __syncthreads();
-  if (g != 0) return;
+  if (wave != 0 || g != 0) return;
   float acc = x[static_cast<int64_t>(t) * d + r];
   for (int i = 0; i < k; ++i)
-    if (slot[t * k + i] >= 0) acc = fmaf(w[t * k + i], red[i * KB_ROWS + rr], acc);
+    if (__builtin_amdgcn_readlane(sp, t * k + i) >= 0) acc = fmaf(w[t * k + i], red[i * KB_ROWS + rr], acc);
   if (has_shared) acc += red[k * KB_ROWS + rr];
   y[static_cast<int64_t>(t) * d + r] = acc;
 }
@@ -292,11 +347,13 @@ size_t part_bytes(int d, int f, int T, int k) {
 template <int FMT>
 hipError_t launch_ffn(const FfnArgs& a, const float* x, hipStream_t s) {
   const dim3 grid(a.f / SLICE, a.T * a.k + 1);
-  const int nu = a.d / 64;
-  if (nu <= KA_WAVES)
+  const int upw = (a.d / 64 + KA_WAVES - 1) / KA_WAVES;
+  if (upw <= 1)
     decode_ffn_kernel<FMT, 1><<<grid, KA_THREADS, 0, s>>>(a, x);
-  else
+  else if (upw <= 2)
     decode_ffn_kernel<FMT, 2><<<grid, KA_THREADS, 0, s>>>(a, x);
+  else
+    decode_ffn_kernel<FMT, 4><<<grid, KA_THREADS, 0, s>>>(a, x);
   return hipGetLastError();
 }
 
@@ -333,7 +390,7 @@ hipError_t launch_decode(const moe_layer& L, const float* x, int T, const int32_
   if (e != hipSuccess) return e;
   const dim3 grid(L.d_model / KB_ROWS, T);
   const size_t lds = static_cast<size_t>(L.top_k + 1) * KB_ROWS * 4;
-  decode_combine_kernel<<<grid, KB_ROWS * KB_TERMS, lds, s>>>(
+  decode_combine_kernel<<<grid, KB_WAVES * 64, lds, s>>>(
       x, slot, w, T, L.top_k, L.d_model, L.d_ff / SLICE, L.shared_slot >= 0 ? 1 : 0, a.part, y);
   return hipGetLastError();
 }
