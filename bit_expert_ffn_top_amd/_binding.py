@@ -48,6 +48,8 @@ SIGNATURES = {
                                   _c_sz, _vp]),
     "moe_decode_workspace_bytes": (_c_sz, [_LP, _c_int]),
     "moe_expert_ffn_decode": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
+    "moe_decode_layer": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _c_sz, _vp]),
     "moe_prefill_workspace_bytes": (_c_sz, [_LP, _c_int]),
     "moe_expert_ffn_prefill": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _c_sz, _vp]),
@@ -197,6 +199,37 @@ def expert_ffn_decode(layer: MoeLayer, x, idx, slot, w, y=None, ws=None, stream=
                                        _ptr(w), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_expert_ffn_decode")
     return y
+
+
+def decode_layer(layer: MoeLayer, x, logits, slot_of_expert, idx=None, w=None, slot=None,
+                 miss_expert=None, miss_pair=None, n_miss=None, y=None, ws=None,
+                 want_pairs=True, stream=None):
+    """Route, look up and run one decode layer (moe_decode_layer).
+    Returns (y, idx, w, slot, miss_expert, miss_pair, n_miss)."""
+    _dev(x, torch.float32, "x")
+    _dev(logits, torch.float32, "logits")
+    _dev(slot_of_expert, torch.int32, "slot_of_expert")
+    T = x.shape[0]
+    k = layer.top_k
+    dev = x.device
+    n = T * k
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev) if idx is None else idx
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    slot = torch.empty((T, k), dtype=torch.int32, device=dev) if slot is None else slot
+    if miss_expert is None:
+        miss_expert = torch.full((n,), -1, dtype=torch.int32, device=dev)
+    if want_pairs and miss_pair is None:
+        miss_pair = torch.full((n,), -1, dtype=torch.int32, device=dev)
+    n_miss = torch.zeros((4,), dtype=torch.int32, device=dev) if n_miss is None else n_miss
+    y = torch.empty_like(x) if y is None else y
+    if ws is None:
+        ws = torch.empty((decode_workspace_bytes(layer, T),), dtype=torch.uint8, device=dev)
+    L = layer.c_struct()
+    _check(lib().moe_decode_layer(ctypes.byref(L), _ptr(x), T, _ptr(logits),
+                                  _ptr(slot_of_expert), _ptr(idx), _ptr(w), _ptr(slot),
+                                  _ptr(miss_expert), _ptr(miss_pair), _ptr(n_miss), _ptr(y),
+                                  _ptr(ws), ws.numel(), _stream(stream)), "moe_decode_layer")
+    return y, idx, w, slot, miss_expert, miss_pair, n_miss
 
 
 def prefill_workspace_bytes(layer: MoeLayer, T: int) -> int:

@@ -132,6 +132,28 @@ int moe_expert_ffn_decode(const moe_layer* L, const float* x, int T, const int32
   return hip_status(bitffn::launch_decode(*L, x, T, idx, slot, w, y, ws, stream));
 }
 
+int moe_decode_layer(const moe_layer* L, const float* x, int T, const float* logits,
+                     const int32_t* slot_of_expert, int32_t* idx, float* w, int32_t* slot,
+                     int32_t* miss_expert, int32_t* miss_pair, int32_t* n_miss, float* y,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 1 || T > MOE_MAX_DECODE_T || T * L->top_k > MOE_MAX_DECODE_PAIRS) return MOE_EINVAL;
+  if (!x || !logits || !slot_of_expert || !idx || !w || !slot || !miss_expert || !n_miss || !y ||
+      !ws)
+    return MOE_EINVAL;
+  if (static_cast<const void*>(x) == static_cast<const void*>(y)) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(logits) || !aligned16(slot_of_expert) || !aligned16(idx) ||
+      !aligned16(w) || !aligned16(slot) || !aligned16(miss_expert) || !aligned16(n_miss) ||
+      (miss_pair && !aligned16(miss_pair)) || !aligned16(y))
+    return MOE_EALIGN;
+  if (!aligned256(ws)) return MOE_EALIGN;
+  if (ws_bytes < bitffn::decode_workspace_bytes(L->d_model, L->d_ff, T, L->top_k))
+    return MOE_ENOSPC;
+  return hip_status(bitffn::launch_decode_layer(*L, x, T, logits, slot_of_expert, idx, w, slot,
+                                                miss_expert, miss_pair, n_miss, y, ws, stream));
+}
+
 size_t moe_prefill_workspace_bytes(const moe_layer* L, int T) {
   if (check_layer(L) != MOE_OK || T < 1 || T > 65536) return 0;
   return bitffn::prefill_workspace_bytes(L->d_model, L->d_ff, T, L->top_k, L->n_experts);

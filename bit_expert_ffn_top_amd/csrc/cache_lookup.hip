@@ -13,6 +13,7 @@
 //   3. per chunk, one wavefront walks its tokens in order; the k pairs of a
 //      token name distinct experts, so the lanes bump distinct LDS cursors.
 #include "moe_internal.h"
+#include "route_device.h"
 
 namespace bitffn {
 namespace {
@@ -70,44 +71,19 @@ __global__ __launch_bounds__(1024) void lookup_small_kernel(
   }
 }
 
-// T*k <= 64: one wavefront, lane p = pair p; pairs are compared through lane
-// reads (uniform values), so there is no LDS traffic and no barrier.
+// T*k <= 64: one wavefront, lane p = pair p (the shared miss-list builder).
 __global__ __launch_bounds__(64) void lookup_wave_kernel(
     const int32_t* __restrict__ idx, int n, const int32_t* __restrict__ table,
     int32_t* __restrict__ slot, int32_t* __restrict__ miss_expert,
     int32_t* __restrict__ miss_pair, int32_t* __restrict__ n_miss) {
   const int p = threadIdx.x;
-  int e = 0x7FFFFFFF;
-  bool miss = false;
+  int e = 0, s = -1;
   if (p < n) {
     e = idx[p];
-    const int s = table[e];
+    s = table[e];
     slot[p] = s;
-    miss = s < 0;
   }
-  const int key = miss ? e : 0x7FFFFFFF;   // only missed pairs take part
-  int pos = 0;          // missed pairs before this one in (expert, pair) order
-  int dpos = 0;         // distinct missed experts with a smaller id
-  bool first = miss;    // first missed pair naming this expert
-  for (int q = 0; q < n; ++q) {
-    const int kq = __builtin_amdgcn_readlane(key, q);
-    if (kq == 0x7FFFFFFF) continue;
-    pos += (kq < key || (kq == key && q < p)) ? 1 : 0;
-    if (kq == key && q < p) first = false;
-  }
-  const uint64_t firsts = __ballot(first);
-  for (int q = 0; q < n; ++q) {
-    if (!((firsts >> q) & 1ull)) continue;
-    const int kq = __builtin_amdgcn_readlane(key, q);
-    dpos += kq < key ? 1 : 0;
-  }
-  const uint64_t misses = __ballot(miss);   // taken by the whole wavefront
-  if (miss && miss_pair) miss_pair[pos] = p;
-  if (first) miss_expert[dpos] = e;
-  if (p == 0) {
-    n_miss[0] = __popcll(firsts);
-    n_miss[1] = __popcll(misses);
-  }
+  wave_miss_lists(p, n, e, s, miss_expert, miss_pair, n_miss);
 }
 
 __device__ __forceinline__ bool selected(int s, bool select_hits) {

@@ -24,6 +24,7 @@
 // an exponent, each multiplied into fp32 by v_fma_mix; the block's offset sum
 // and scale/min are applied once per block.
 #include "moe_internal.h"
+#include "route_device.h"
 
 namespace bitffn {
 namespace {
@@ -45,7 +46,25 @@ struct FfnArgs {
   int d, f, T, k, shared_slot;
   const int32_t* slot;
   float* part;  // [(T*k+1) * T][f/32][d]
+  // fused routing only: inputs, and the routing outputs written by
+  // workgroup (0, 0)
+  const float* logits;          // [T][E]
+  const int32_t* table;         // slot_of_expert [E]
+  int E;
+  int32_t* o_idx;               // [T][k]
+  float* o_w;                   // [T][k]
+  int32_t* o_slot;              // [T][k]
+  int32_t* o_miss_expert;       // [<= T*k]
+  int32_t* o_miss_pair;         // [T*k] or null
+  int32_t* o_n_miss;            // [2]
 };
+
+// Survivors of the first top-k level in the fused kernel: T * ceil(E/64) * k
+// <= 16 * (T * k) <= 16 * 64.
+constexpr int kFusedCand = (MOE_MAX_EXPERTS / 64) * MOE_MAX_DECODE_PAIRS;
+static_assert(MOE_MAX_EXPERTS <= KA_THREADS, "one slot-table entry per thread");
+static_assert(MOE_MAX_DECODE_T * (MOE_MAX_EXPERTS / 64) <= 4 * KA_WAVES,
+              "logit groups per wavefront above 4");
 
 // Union member u: its slot and the mask of tokens it serves.  `sp` is the
 // slot of pair `lane` (-1 for lanes >= T*k; T*k <= 64), so the test is a
@@ -97,7 +116,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // UPW: G units (2 blocks) per wavefront, ceil(d_model / 64 / KA_WAVES); wavefront
 // w takes units w, w + KA_WAVES, ...  d_model <= 2048.
-template <int FMT, int UPW>
+// ROUTE: the workgroup first routes the T tokens itself (top-k over the
+// logits, slots from the slot table held in LDS) instead of reading the pair
+// slots; workgroups of the shared expert skip routing.
+template <int FMT, int UPW, bool ROUTE>
 __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
                                                                 const float* __restrict__ x) {
   const int js = blockIdx.x;
@@ -105,7 +127,9 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int d = a.d;
-  const int sp = lane < a.T * a.k ? a.slot[lane] : -1;
+  const int n = a.T * a.k;
+  int sp = -1;   // slot of pair `lane`
+  if (!ROUTE) sp = lane < n ? a.slot[lane] : -1;
 
   // Every load below is unconditional, with indices clamped into range (the
   // surplus values are never used), so the compiler can count outstanding
@@ -119,6 +143,35 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
     xv[t] = *reinterpret_cast<const float2*>(x + static_cast<int64_t>(tt) * d + ex);
   }
   __builtin_amdgcn_sched_barrier(0);   // keep the issue order
+
+  if (ROUTE && u < n) {   // uniform per workgroup
+    __shared__ uint64_t s_grp[KA_WAVES * 64];
+    __shared__ uint64_t s_cand[kFusedCand];
+    __shared__ uint64_t s_top[MOE_MAX_DECODE_PAIRS];
+    __shared__ int32_t s_table[MOE_MAX_EXPERTS];
+    float lg[4];
+    topk_load<4>(a.logits, a.T, a.E, lg);
+    const int tv = a.table[min(tid, a.E - 1)];
+    topk_select<4>(lg, a.T, a.E, a.k, TopkLds{s_grp, s_cand, s_top}, [&] {
+      if (tid < a.E) s_table[tid] = tv;
+    });
+    const int e = lane < n ? key_expert(s_top[lane]) : 0;
+    sp = lane < n ? s_table[e] : -1;
+    if (u == 0 && js == 0) {   // routing outputs
+      if (wave < a.T) {
+        int id;
+        float wt;
+        topk_softmax_lane(s_top + wave * a.k, a.k, lane, id, wt);
+        if (lane < a.k) {
+          a.o_idx[wave * a.k + lane] = id;
+          a.o_w[wave * a.k + lane] = wt;
+          a.o_slot[wave * a.k + lane] = s_table[id];
+        }
+      }
+      if (wave == KA_WAVES - 1)
+        wave_miss_lists(lane, n, e, sp, a.o_miss_expert, a.o_miss_pair, a.o_n_miss);
+    }
+  }
 
   int s;
   uint32_t mask;
@@ -344,16 +397,52 @@ size_t part_bytes(int d, int f, int T, int k) {
   return static_cast<size_t>(static_cast<int64_t>(T * k + 1) * T * (f / SLICE) * d * 4);
 }
 
-template <int FMT>
+template <int FMT, bool ROUTE>
 hipError_t launch_ffn(const FfnArgs& a, const float* x, hipStream_t s) {
   const dim3 grid(a.f / SLICE, a.T * a.k + 1);
   const int upw = (a.d / 64 + KA_WAVES - 1) / KA_WAVES;
   if (upw <= 1)
-    decode_ffn_kernel<FMT, 1><<<grid, KA_THREADS, 0, s>>>(a, x);
-  else if (upw <= 2)
-    decode_ffn_kernel<FMT, 2><<<grid, KA_THREADS, 0, s>>>(a, x);
+    decode_ffn_kernel<FMT, 1, ROUTE><<<grid, KA_THREADS, 0, s>>>(a, x);
   else
-    decode_ffn_kernel<FMT, 4><<<grid, KA_THREADS, 0, s>>>(a, x);
+    decode_ffn_kernel<FMT, 2, ROUTE><<<grid, KA_THREADS, 0, s>>>(a, x);
+  return hipGetLastError();
+}
+
+FfnArgs ffn_args(const moe_layer& L, int T, const int32_t* slot, void* ws) {
+  const SlotLayout lay = slot_layout(L.fmt, L.d_model, L.d_ff);
+  FfnArgs a = {};
+  a.pool = static_cast<const uint8_t*>(L.pool);
+  a.slot_bytes = L.slot_bytes;
+  a.G = lay.G;
+  a.D = lay.D;
+  a.d = L.d_model;
+  a.f = L.d_ff;
+  a.T = T;
+  a.k = L.top_k;
+  a.shared_slot = L.shared_slot;
+  a.slot = slot;
+  a.part = static_cast<float*>(ws);
+  a.E = L.n_experts;
+  return a;
+}
+
+template <bool ROUTE>
+hipError_t launch_ffn_fmt(int fmt, const FfnArgs& a, const float* x, hipStream_t s) {
+  switch (fmt) {
+    case MOE_FMT_Q2S: return launch_ffn<MOE_FMT_Q2S, ROUTE>(a, x, s);
+    case MOE_FMT_Q2SM: return launch_ffn<MOE_FMT_Q2SM, ROUTE>(a, x, s);
+    case MOE_FMT_Q3G: return launch_ffn<MOE_FMT_Q3G, ROUTE>(a, x, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_combine_partials(const moe_layer& L, const float* x, int T,
+                                   const int32_t* slot, const float* w, const float* part,
+                                   float* y, hipStream_t s) {
+  const dim3 grid(L.d_model / KB_ROWS, T);
+  const size_t lds = static_cast<size_t>(L.top_k + 1) * KB_ROWS * 4;
+  decode_combine_kernel<<<grid, KB_WAVES * 64, lds, s>>>(
+      x, slot, w, T, L.top_k, L.d_model, L.d_ff / SLICE, L.shared_slot >= 0 ? 1 : 0, part, y);
   return hipGetLastError();
 }
 
@@ -367,32 +456,28 @@ hipError_t launch_decode(const moe_layer& L, const float* x, int T, const int32_
                          const int32_t* slot, const float* w, float* y, void* ws,
                          hipStream_t s) {
   (void)idx;
-  const SlotLayout lay = slot_layout(L.fmt, L.d_model, L.d_ff);
-  FfnArgs a;
-  a.pool = static_cast<const uint8_t*>(L.pool);
-  a.slot_bytes = L.slot_bytes;
-  a.G = lay.G;
-  a.D = lay.D;
-  a.d = L.d_model;
-  a.f = L.d_ff;
-  a.T = T;
-  a.k = L.top_k;
-  a.shared_slot = L.shared_slot;
-  a.slot = slot;
-  a.part = static_cast<float*>(ws);
-  hipError_t e;
-  switch (L.fmt) {
-    case MOE_FMT_Q2S: e = launch_ffn<MOE_FMT_Q2S>(a, x, s); break;
-    case MOE_FMT_Q2SM: e = launch_ffn<MOE_FMT_Q2SM>(a, x, s); break;
-    case MOE_FMT_Q3G: e = launch_ffn<MOE_FMT_Q3G>(a, x, s); break;
-    default: return hipErrorInvalidValue;
-  }
+  const FfnArgs a = ffn_args(L, T, slot, ws);
+  const hipError_t e = launch_ffn_fmt<false>(L.fmt, a, x, s);
   if (e != hipSuccess) return e;
-  const dim3 grid(L.d_model / KB_ROWS, T);
-  const size_t lds = static_cast<size_t>(L.top_k + 1) * KB_ROWS * 4;
-  decode_combine_kernel<<<grid, KB_WAVES * 64, lds, s>>>(
-      x, slot, w, T, L.top_k, L.d_model, L.d_ff / SLICE, L.shared_slot >= 0 ? 1 : 0, a.part, y);
-  return hipGetLastError();
+  return launch_combine_partials(L, x, T, slot, w, a.part, y, s);
+}
+
+hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const float* logits,
+                               const int32_t* slot_of_expert, int32_t* idx, float* w,
+                               int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
+                               int32_t* n_miss, float* y, void* ws, hipStream_t s) {
+  FfnArgs a = ffn_args(L, T, nullptr, ws);
+  a.logits = logits;
+  a.table = slot_of_expert;
+  a.o_idx = idx;
+  a.o_w = w;
+  a.o_slot = slot;
+  a.o_miss_expert = miss_expert;
+  a.o_miss_pair = miss_pair;
+  a.o_n_miss = n_miss;
+  const hipError_t e = launch_ffn_fmt<true>(L.fmt, a, x, s);
+  if (e != hipSuccess) return e;
+  return launch_combine_partials(L, x, T, slot, w, a.part, y, s);
 }
 
 }  // namespace bitffn

@@ -49,6 +49,13 @@ hipError_t launch_decode(const moe_layer& L, const float* x, int T, const int32_
                          const int32_t* slot, const float* w, float* y, void* ws,
                          hipStream_t s);
 
+// Route, look up and run the decode layer in two launches (routing runs in
+// every FFN workgroup; workgroup (0, 0) writes the routing outputs).
+hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const float* logits,
+                               const int32_t* slot_of_expert, int32_t* idx, float* w,
+                               int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
+                               int32_t* n_miss, float* y, void* ws, hipStream_t s);
+
 size_t prefill_workspace_bytes(int d, int f, int T, int k, int E);
 hipError_t launch_prefill(const moe_layer& L, const uint16_t* x_bf16, int T,
                           const int32_t* idx, const int32_t* slot, float* out_pairs,

@@ -174,6 +174,25 @@ int moe_expert_ffn_decode(const moe_layer* L, const float* x, int T,
                           const float* w, float* y, void* ws,
                           size_t ws_bytes, hipStream_t stream);
 
+/* One whole decode / verify layer step: moe_route_topk, moe_cache_lookup
+ * and moe_expert_ffn_decode in one call, with identical results in every
+ * output ("Strata" page, "Strataとは" and "投機的デコード": the router picks
+ * 10 of 512 experts plus the shared one, the cached ones run on the GPU,
+ * the misses are handed on).  logits fp32 [T][n_experts]; slot_of_expert
+ * int32 [n_experts]; outputs as those three calls define them: idx, slot
+ * int32 [T][k], w fp32 [T][k], miss_expert int32 [T*k], miss_pair int32
+ * [T*k] (may be NULL), n_miss int32 [2], y fp32 [T][d_model] (may not alias
+ * x).  Limits: as moe_expert_ffn_decode (T * top_k <= 64); n_experts <= 1024.
+ * ws: at least moe_decode_workspace_bytes(L, T) bytes, 256-byte aligned.
+ * Runs as two kernels; routing is repeated in every workgroup of the first,
+ * so no routing result makes a round trip through memory before the expert
+ * weights are requested. */
+int moe_decode_layer(const moe_layer* L, const float* x, int T,
+                     const float* logits, const int32_t* slot_of_expert,
+                     int32_t* idx, float* w, int32_t* slot,
+                     int32_t* miss_expert, int32_t* miss_pair, int32_t* n_miss,
+                     float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* (host) Workspace bytes that moe_expert_ffn_prefill needs for T tokens. */
 size_t moe_prefill_workspace_bytes(const moe_layer* L, int T);
 
