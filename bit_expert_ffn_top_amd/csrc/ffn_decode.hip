@@ -45,7 +45,7 @@ struct FfnArgs {
   Planes G, D;
   int d, f, T, k, shared_slot;
   const int32_t* slot;
-  float* part;  // [(T*k+1) * T][f/32][d]
+  float* part;  // [T][k+1][f/32][d]: term i of token t, the shared expert at i = k
   // fused routing only: inputs, and the routing outputs written by
   // workgroup (0, 0)
   const float* logits;          // [T][E]
@@ -66,27 +66,35 @@ static_assert(MOE_MAX_EXPERTS <= KA_THREADS, "one slot-table entry per thread");
 static_assert(MOE_MAX_DECODE_T * (MOE_MAX_EXPERTS / 64) <= 4 * KA_WAVES,
               "logit groups per wavefront above 4");
 
-// Union member u: its slot and the mask of tokens it serves.  `sp` is the
-// slot of pair `lane` (-1 for lanes >= T*k; T*k <= 64), so the test is a
-// lane read and a ballot; the result is uniform across the wavefront.
+// Union member u: its slot, the mask of tokens it serves, and `same`, the
+// mask of pairs naming that slot (all of them for the shared expert, whose
+// term is i = k).  `sp` is the slot of pair `lane` (-1 for lanes >= T*k;
+// T*k <= 64), so the test is a lane read and a ballot; the result is uniform
+// across the wavefront.
 __device__ __forceinline__ bool union_member(int sp, int T, int k, int shared_slot, int u,
-                                             int& s, uint32_t& mask) {
+                                             int& s, uint32_t& mask, uint64_t& same) {
   const int n = T * k;
   if (u == n) {
     if (shared_slot < 0) return false;
     s = shared_slot;
     mask = (1u << T) - 1u;
+    same = 0;
     return true;
   }
   s = __builtin_amdgcn_readlane(sp, u);
   if (s < 0) return false;
-  const uint64_t same = __ballot(sp == s);
+  same = __ballot(sp == s);
   if (same & ((1ull << u) - 1ull)) return false;   // an earlier pair names this slot
   const uint64_t kmask = k >= 64 ? ~0ull : (1ull << k) - 1ull;
   mask = 0;
   for (int t = 0; t < T; ++t)
     if ((same >> (t * k)) & kmask) mask |= 1u << t;
   return true;
+}
+
+// k-slot of the member's pair in token t (a token names a slot at most once)
+__device__ __forceinline__ int member_term(uint64_t same, int t, int k, bool shared) {
+  return shared ? k : __builtin_ctzll(same >> (t * k));
 }
 
 // value of v in lane `src` (uniform result)
@@ -108,10 +116,11 @@ __device__ __forceinline__ float row16_sum(float v) {
   return add_dpp<0x128>(v);   // row_ror:8
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// sum over the wavefront (uniform result): rows of 16 by DPP, then the four
+// row sums in the fixed order (r0 + r1) + (r2 + r3)
+__device__ __forceinline__ float wave_total(float v) {
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 // UPW: G units (2 blocks) per wavefront, ceil(d_model / 64 / KA_WAVES); wavefront
@@ -175,7 +184,8 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
 
   int s;
   uint32_t mask;
-  if (!union_member(sp, a.T, a.k, a.shared_slot, u, s, mask)) return;
+  uint64_t same;
+  if (!union_member(sp, a.T, a.k, a.shared_slot, u, s, mask, same)) return;
   const uint8_t* __restrict__ base = a.pool + static_cast<int64_t>(s) * a.slot_bytes;
   const int64_t R = 2 * static_cast<int64_t>(a.f);   // G rows
   const int64_t grow = 2 * SLICE * js + lane;        // this lane's G row
@@ -255,13 +265,15 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
       float rs = red[0][lane];
 #pragma unroll
       for (int w = 1; w < KA_WAVES; ++w) rs += red[w][lane];
-      const float up = __shfl_xor(rs, 1, 64);
+      // up row 2j+1 sits in the lane after gate row 2j (DPP quad_perm [1,0,3,2])
+      const float up = __builtin_bit_cast(
+          float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, rs), 0xB1, 0xF, 0xF, false));
       const float hv = silu(rs) * up;                       // valid in even lanes
       const int j = lane >> 1;
       const bool even = (lane & 1) == 0;
       if (even) hsh[j] = hv;
-      const float hx = wave_sum(even ? hv : 0.0f);
-      const float hc = wave_sum(even ? block_offset_weight<FMT>(j) * hv : 0.0f);
+      const float hx = wave_total(even ? hv : 0.0f);
+      const float hc = wave_total(even ? block_offset_weight<FMT>(j) * hv : 0.0f);
       if (lane == 0) {
         hsum[0] = hx;
         hsum[1] = block_const<FMT>(hx, hc);
@@ -273,7 +285,9 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
     // (same address in every lane) 16 values at a time, each half applied to
     // every row of the thread before the next half is read.
     const float HX = hsum[0], HK = hsum[1];
-    float* __restrict__ out = a.part + ((static_cast<int64_t>(u) * a.T + t) * nslices + js) * d;
+    const int term = member_term(same, t, a.k, u == n);
+    float* __restrict__ out =
+        a.part + ((static_cast<int64_t>(t) * (a.k + 1) + term) * nslices + js) * d;
     float a0[MAX_DROWS], a1[MAX_DROWS];
 #pragma unroll
     for (int i = 0; i < MAX_DROWS; ++i) a0[i] = a1[i] = 0.0f;
@@ -336,12 +350,13 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
   }
 }
 
-// y = x + sum_i w_i * P(u(t,i)) + P(shared), P(u) = sum over slices of u's
-// partials.  Workgroup: 16 rows, one wavefront per term (terms i, i+16, ...);
-// lane = (row r, slice group g of 4), group g sums its quarter of the slices
-// in order (all loads of a chunk issued together), the four group sums meet
-// as (g0 + g1) + (g2 + g3), and wavefront 0 adds the terms in k-slot order,
-// shared last.  Member of term i: the first pair naming the same slot.
+// y = x + sum_{i: slot >= 0} w_i * P(t, i) + P(t, k), P(t, i) = sum over
+// slices of term i's partials (P(t, k): the shared expert, if any).
+// Workgroup: 16 rows, one wavefront per term (terms i, i+16, ...); lane =
+// (row r, slice group g of 4), group g sums its quarter of the slices in
+// order, the four group sums meet as (g0 + g1) + (g2 + g3), and wavefront 0
+// adds the terms in k-slot order, shared last.  No load depends on another:
+// x, w, the pair slots and every partial are requested up front.
 constexpr int KB_ROWS = 16;
 constexpr int KB_GROUPS = 64 / KB_ROWS;
 constexpr int KB_WAVES = 16;
@@ -357,28 +372,22 @@ __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rr = lane % KB_ROWS, g = lane / KB_ROWS;
   const int r = blockIdx.x * KB_ROWS + rr;
-  const int n = T * k;
-  const int sp = lane < n ? slot[lane] : -1;
+  const int ti = min(lane, k - 1);
+  const int sp = slot[t * k + ti];               // lane i < k: slot of term i
+  const float wv = w[t * k + ti];                // lane i < k: weight of term i
+  const float xr = x[static_cast<int64_t>(t) * d + r];
   const int per = (nslices + KB_GROUPS - 1) / KB_GROUPS;
   const int j0 = min(nslices, g * per), j1 = min(nslices, j0 + per);
   for (int i = wave; i < k + 1; i += KB_WAVES) {
-    int uu = -1;
-    if (i < k) {
-      const int sl = __builtin_amdgcn_readlane(sp, t * k + i);
-      if (sl >= 0) uu = __builtin_ctzll(__ballot(sp == sl));
-    } else if (has_shared) {
-      uu = n;
-    }
-    if (uu < 0) continue;   // uniform
-    const float* src = part + (static_cast<int64_t>(uu) * T + t) * nslices * d + r;
+    const float* src = part + ((static_cast<int64_t>(t) * (k + 1) + i) * nslices) * d + r;
     float acc = 0.0f;
     for (int j = j0; j < j1; j += KB_CHUNK) {
       float v[KB_CHUNK];
 #pragma unroll
       for (int q = 0; q < KB_CHUNK; ++q)
-        v[q] = j + q < j1 ? src[static_cast<int64_t>(j + q) * d] : 0.0f;
+        v[q] = src[static_cast<int64_t>(min(j + q, j1 - 1)) * d];
 #pragma unroll
-      for (int q = 0; q < KB_CHUNK; ++q) acc += v[q];
+      for (int q = 0; q < KB_CHUNK; ++q) acc += j + q < j1 ? v[q] : 0.0f;
     }
     acc += __shfl_xor(acc, KB_ROWS, 64);        // g0+g1, g2+g3
     acc += __shfl_xor(acc, 2 * KB_ROWS, 64);    // (g0+g1)+(g2+g3)
@@ -386,15 +395,17 @@ __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
   }
   __syncthreads();
   if (wave != 0 || g != 0) return;
-  float acc = x[static_cast<int64_t>(t) * d + r];
+  float acc = xr;
   for (int i = 0; i < k; ++i)
-    if (__builtin_amdgcn_readlane(sp, t * k + i) >= 0) acc = fmaf(w[t * k + i], red[i * KB_ROWS + rr], acc);
+    if (__builtin_amdgcn_readlane(sp, i) >= 0)
+      acc = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), i)),
+                 red[i * KB_ROWS + rr], acc);
   if (has_shared) acc += red[k * KB_ROWS + rr];
   y[static_cast<int64_t>(t) * d + r] = acc;
 }
 
 size_t part_bytes(int d, int f, int T, int k) {
-  return static_cast<size_t>(static_cast<int64_t>(T * k + 1) * T * (f / SLICE) * d * 4);
+  return static_cast<size_t>(static_cast<int64_t>(T) * (k + 1) * (f / SLICE) * d * 4);
 }
 
 template <int FMT, bool ROUTE>
