@@ -33,6 +33,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 N_LAYERS = 48
+COPY_BYTES = 512 << 20         # calibration copy of the counter pass
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_layer_e512_k10_d2048_f768_q2sm_traffic.txt")
+DECODE_SOURCES = ["bit_expert_ffn_top_amd/csrc/ffn_decode.hip",
+                  "bit_expert_ffn_top_amd/csrc/moe_common.h",
+                  "bit_expert_ffn_top_amd/csrc/route_device.h"]
 
 
 def log(*a):
@@ -48,6 +53,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=2)
+    ap.add_argument("--counters", action="store_true",
+                    help="counter pass for rocprofv3 --pmc: eager decode layer calls plus one "
+                         "device copy of COPY_BYTES for calibration; prints no result line")
     return ap.parse_args()
 
 
@@ -134,6 +142,47 @@ def time_graph_steps(torch, chain, logits_sets, steps, warmup, n_graphs):
     return dt, ev0.elapsed_time(ev1), graphs
 
 
+def sources_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per moe_decode_layer call from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy); None when the file
+    is missing or the decode kernels' sources changed since it was taken."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    kv[key.strip()] = val.strip()
+        if kv.get("sources_sha256_16") != sources_digest(DECODE_SOURCES):
+            return None
+        return int(float(kv["bytes_per_call"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def counter_pass(torch, bf, synth, chain, logits_sets, dev):
+    """Eager decode layer calls, then one device copy of COPY_BYTES (the
+    counters' calibration); run under rocprofv3 --pmc."""
+    for g in range(2):
+        chain.step(logits_sets[g])
+    torch.cuda.synchronize()
+    src = torch.empty((COPY_BYTES // 4,), dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"counter pass: {2 * len(chain.layers)} decode layer calls, copy of {COPY_BYTES} bytes")
+
+
 def decode_bytes_per_call(synth, shape, fmt, T, n_union):
     """Algorithmic HBM bytes of one moe_decode_layer call: the packed bytes of
     every distinct resident expert chosen (plus the shared one) read once,
@@ -169,6 +218,9 @@ def main():
     n_graphs = args.graphs
     logits_sets = [torch.stack([synth.make_logits(1, l, 1, E, 1.5, device=dev, step=g)
                                 for l in range(N_LAYERS)]) for g in range(n_graphs)]
+    if args.counters:
+        counter_pass(torch, bf, synth, chain, logits_sets, dev)
+        return
     dt, ev_ms, graphs = time_graph_steps(torch, chain, logits_sets, args.steps, args.warmup,
                                          n_graphs)
     tok_s = args.steps / dt
@@ -211,7 +263,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "avg_call_us": round(call_us, 3),
             "bytes_per_call": bytes_call,
         },

@@ -352,15 +352,17 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
 
 // y = x + sum_{i: slot >= 0} w_i * P(t, i) + P(t, k), P(t, i) = sum over
 // slices of term i's partials (P(t, k): the shared expert, if any).
-// Workgroup: 16 rows, one wavefront per term (terms i, i+16, ...); lane =
-// (row r, slice group g of 4), group g sums its quarter of the slices in
-// order, the four group sums meet as (g0 + g1) + (g2 + g3), and wavefront 0
-// adds the terms in k-slot order, shared last.  No load depends on another:
-// x, w, the pair slots and every partial are requested up front.
-constexpr int KB_ROWS = 16;
+// Workgroup: 32 rows (128 bytes of a partial row: whole memory lines), one
+// wavefront per term (terms i, i+16, ...); lane = (row r, slice group g of
+// 2), group g sums its half of the slices in order, the two group sums meet
+// as g0 + g1, and wavefront 0 adds the terms in k-slot order, shared last.
+// No load depends on another: x, w, the pair slots and every partial are
+// requested up front.
+constexpr int KB_ROWS = 32;
 constexpr int KB_GROUPS = 64 / KB_ROWS;
 constexpr int KB_WAVES = 16;
-constexpr int KB_CHUNK = 8;
+constexpr int KB_CHUNK = 16;
+static_assert(KB_GROUPS == 2, "the group sums meet in one exchange");
 
 __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
     const float* __restrict__ x, const int32_t* __restrict__ slot, const float* __restrict__ w,
@@ -389,8 +391,7 @@ __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
 #pragma unroll
       for (int q = 0; q < KB_CHUNK; ++q) acc += j + q < j1 ? v[q] : 0.0f;
     }
-    acc += __shfl_xor(acc, KB_ROWS, 64);        // g0+g1, g2+g3
-    acc += __shfl_xor(acc, 2 * KB_ROWS, 64);    // (g0+g1)+(g2+g3)
+    acc += __shfl_xor(acc, KB_ROWS, 64);        // g0 + g1
     if (g == 0) red[i * KB_ROWS + rr] = acc;
   }
   __syncthreads();
