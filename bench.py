@@ -195,7 +195,7 @@ def decode_bytes_per_call(synth, shape, fmt, T, n_union):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import numpy as np
     import torch
@@ -286,7 +286,7 @@ def run_extras(torch, np, bf, synth, pools, dev, args):
 
     # ---------------- expert-cache workload, config 2 ----------------
     t0 = time.perf_counter()
-    c2 = synth.CONFIGS[2]
+    c2 = synth.WORKLOADS[2]
     pools2 = build_pools(torch, synth, 2, lambda l: synth.FMT_Q2SM, dev)
     chain2 = DecodeChain(torch, bf, shape, pools2, 1, dev,
                          [synth.make_x(2, l, 1, d, device=dev) for l in range(N_LAYERS)])
@@ -361,7 +361,7 @@ def run_extras(torch, np, bf, synth, pools, dev, args):
 def run_prefill(torch, np, bf, synth, pools, dev, args):
     shape = synth.config_shape(4)
     E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
-    T = synth.CONFIGS[4]["T"]
+    T = synth.WORKLOADS[4]["T"]
     layers = [bf.MoeLayer(d, f, E, k, fmt, pool, shared_slot)
               for pool, _, shared_slot, fmt in pools]
     tables = [t for _, t, _, _ in pools]

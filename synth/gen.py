@@ -1,9 +1,8 @@
 """Seeded generator, block quantizer and slot packer.
 
-Everything here produces inputs.  Workload shapes follow the five layer
-configurations of the task (tiny plumbing layer; one decode layer at the
-model's counts; the expert-cache hit/miss layer; the 1+3-token verify step;
-the 8,192-token prefill chunk).  The model counts behind them -- 48 layers,
+Everything here produces inputs.  There are five layer workloads (a tiny
+plumbing layer; one decode layer at the model's counts; the expert-cache
+hit/miss layer; the 1+3-token verify step; the 8,192-token prefill chunk).  The model counts behind them -- 48 layers,
 512 routed experts per layer, 10 chosen per token plus one shared expert --
 are given in "Strata" (news.blueqat.app post 3262), section "Strataとは".
 
@@ -62,7 +61,7 @@ class LayerShape:
 
 
 # Workload table.  `fmt` may be a tuple that alternates by layer index.
-CONFIGS = {
+WORKLOADS = {
     0: dict(shape=LayerShape(64, 4, 256, 128, False), T=1, fmt=FMT_Q2S,
             logit_sigma=1.0, n_layers=1, x_dtype="f32", routing="normal",
             resident="all_identity"),
@@ -82,11 +81,11 @@ CONFIGS = {
 
 
 def config_shape(cfg: int) -> LayerShape:
-    return CONFIGS[cfg]["shape"]
+    return WORKLOADS[cfg]["shape"]
 
 
 def layer_format(cfg: int, layer: int) -> int:
-    fmt = CONFIGS[cfg]["fmt"]
+    fmt = WORKLOADS[cfg]["fmt"]
     if isinstance(fmt, tuple):
         return fmt[layer % len(fmt)]
     return fmt
@@ -313,7 +312,7 @@ def zipf_residency(cfg: int, layer: int, E: int, n_top: int, n_resident: int) ->
 def make_slot_table(cfg: int, layer: int):
     """Returns (slot_of_expert int32 [E], shared_slot, slot_expert list) where
     slot_expert[s] is the expert id stored in slot s (E = shared expert)."""
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     shape = c["shape"]
     E = shape.n_experts
     if c["resident"] == "all_identity":

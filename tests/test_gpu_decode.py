@@ -79,7 +79,7 @@ def test_decode_with_misses_and_verify_equals_decode():
     resident part; the verify step (T=4) equals four one-token steps."""
     dev = need_gpu()
     shape = synth.config_shape(2)
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS[2]
     table, _, slot_expert = synth.make_slot_table(2, 0)
     resident = [e for e in slot_expert if e < shape.n_experts]
     L = GpuLayer(2, 0, shape, synth.FMT_Q2SM, dev, resident=resident)

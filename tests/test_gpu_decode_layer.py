@@ -94,7 +94,7 @@ def test_decode_layer_misses_zipf():
     """94 of 512 experts resident, Zipf routing: misses and hits mixed."""
     dev = need_gpu()
     shape = synth.config_shape(2)
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS[2]
     table, _, slot_expert = synth.make_slot_table(2, 1)
     resident = [e for e in slot_expert if e < shape.n_experts]
     L = GpuLayer(2, 1, shape, synth.FMT_Q2SM, dev, resident=resident)

@@ -107,7 +107,7 @@ def test_lookup_random(T, E, k, n_res):
 def test_lookup_zipf_layer_hit_rate():
     """The expert-cache workload: ~72% of chosen experts resident."""
     dev = need_gpu()
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS[2]
     hits = total = 0
     for layer in range(4):
         table, _, _ = synth.make_slot_table(2, layer)
