@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=2)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the prefill workload (for profiling); prints its object")
     ap.add_argument("--counters", action="store_true",
                     help="counter pass for rocprofv3 --pmc: eager decode layer calls plus one "
                          "device copy of COPY_BYTES for calibration; prints no result line")
@@ -212,7 +214,11 @@ def main():
     torch.cuda.synchronize()
     log(f"decode pools: {N_LAYERS} layers x {E + 1} experts in {time.perf_counter() - t_gen:.1f} s")
 
-    # ---------------- decode, config 1 (headline) ----------------
+    if args.prefill_only:
+        print(json.dumps({"prefill": run_prefill(torch, np, bf, synth, pools, dev, args)}), flush=True)
+        return
+
+    # ---------------- decode (headline) ----------------
     xs = [synth.make_x(1, l, 1, d, device=dev) for l in range(N_LAYERS)]
     chain = DecodeChain(torch, bf, shape, pools, 1, dev, xs)
     n_graphs = args.graphs
@@ -284,7 +290,7 @@ def run_extras(torch, np, bf, synth, pools, dev, args):
     shape = synth.config_shape(1)
     E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
 
-    # ---------------- expert-cache workload, config 2 ----------------
+    # ---------------- expert-cache workload ----------------
     t0 = time.perf_counter()
     c2 = synth.WORKLOADS[2]
     pools2 = build_pools(torch, synth, 2, lambda l: synth.FMT_Q2SM, dev)
@@ -313,7 +319,7 @@ def run_extras(torch, np, bf, synth, pools, dev, args):
     del pools2, chain2, logits2
     torch.cuda.empty_cache()
 
-    # ---------------- verify step, config 3 ----------------
+    # ---------------- verify step ----------------
     t0 = time.perf_counter()
     pools3 = []
     for l in range(N_LAYERS):
@@ -353,7 +359,7 @@ def run_extras(torch, np, bf, synth, pools, dev, args):
     del pools3, chain3, logits3
     torch.cuda.empty_cache()
 
-    # ---------------- prefill chunk, config 4 ----------------
+    # ---------------- prefill chunk ----------------
     out["prefill"] = run_prefill(torch, np, bf, synth, pools, dev, args)
     return out
 

@@ -8,10 +8,12 @@
 // Large inputs (prefill chunks): a three-pass counting sort that is stable in
 // (t, i) order and needs no sort of keys:
 //   1. per chunk of 32 tokens, a histogram of the selected pairs per expert;
-//   2. one workgroup turns the histograms into per-(chunk, expert) start
-//      positions (exclusive scan over chunks, then over experts);
-//   3. per chunk, one wavefront walks its tokens in order; the k pairs of a
-//      token name distinct experts, so the lanes bump distinct LDS cursors.
+//   2. a workgroup per expert scans its histogram entries over the chunks
+//      (exclusive, in place); one workgroup then scans the experts' totals
+//      into the groups' starts;
+//   3. per chunk, one wavefront walks its tokens in order from cursors
+//      start + chunk prefix; the k pairs of a token name distinct experts,
+//      so the lanes bump distinct LDS cursors.
 #include "moe_internal.h"
 #include "route_device.h"
 
@@ -111,31 +113,56 @@ __global__ __launch_bounds__(256) void group_count_kernel(
     chunk_counts[static_cast<int64_t>(chunk) * E + e] = hist[e];
 }
 
-// pass 2: start positions, offsets, distinct list, tile bases
+// pass 2a: for each expert (one workgroup), the exclusive prefix of its
+// counts over the chunks, in place, and its total.  Thread i owns a run of
+// consecutive chunks; the run sums meet in a fixed-order scan in LDS.
+constexpr int kScanThreads = 256;
+
+__global__ __launch_bounds__(kScanThreads) void group_scan_chunks_kernel(
+    int n_chunks, int E, int32_t* __restrict__ chunk_counts, int32_t* __restrict__ totals) {
+  __shared__ int32_t s_run[kScanThreads];
+  const int e = blockIdx.x;
+  const int i = threadIdx.x;
+  const int per = (n_chunks + kScanThreads - 1) / kScanThreads;
+  const int c0 = min(n_chunks, i * per), c1 = min(n_chunks, c0 + per);
+  int run = 0;
+  for (int c = c0; c < c1; ++c) run += chunk_counts[static_cast<int64_t>(c) * E + e];
+  s_run[i] = run;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {   // inclusive Hillis-Steele
+    const int v = i >= off ? s_run[i - off] : 0;
+    __syncthreads();
+    s_run[i] += v;
+    __syncthreads();
+  }
+  int acc = s_run[i] - run;   // exclusive start of this thread's run
+  for (int c = c0; c < c1; ++c) {
+    int32_t* p = chunk_counts + static_cast<int64_t>(c) * E + e;
+    const int v = *p;
+    *p = acc;
+    acc += v;
+  }
+  if (i == kScanThreads - 1) totals[e] = s_run[i];
+}
+
+// pass 2b: over the experts (one workgroup): start of every group (into
+// `starts`, and `offsets` if wanted), the distinct list, the counts and the
+// tile bases.  Fixed-order Hillis-Steele scans.
 __global__ __launch_bounds__(1024) void group_scan_kernel(
-    int n_chunks, int E, int T, int32_t* __restrict__ chunk_counts,
+    int E, int T, const int32_t* __restrict__ totals, int32_t* __restrict__ starts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ distinct,
     int32_t* __restrict__ counts_out, int32_t* __restrict__ tile_base, int tile_m) {
   __shared__ int32_t s_tot[kMaxE];
   __shared__ int32_t s_nz[kMaxE];
   __shared__ int32_t s_tiles[kMaxE];
   const int e = threadIdx.x;
-  int tot = 0;
-  if (e < E) {
-    for (int c = 0; c < n_chunks; ++c) {
-      int32_t* p = chunk_counts + static_cast<int64_t>(c) * E + e;
-      const int v = *p;
-      *p = tot;  // exclusive within the expert, over chunks
-      tot += v;
-    }
-  }
+  const int tot = e < E ? totals[e] : 0;
   if (e < kMaxE) {
-    s_tot[e] = e < E ? tot : 0;
-    s_nz[e] = (e < E && tot > 0) ? 1 : 0;
-    s_tiles[e] = (e < E) ? (tot + tile_m - 1) / tile_m : 0;
+    s_tot[e] = tot;
+    s_nz[e] = tot > 0 ? 1 : 0;
+    s_tiles[e] = (tot + tile_m - 1) / tile_m;
   }
   __syncthreads();
-  // Hillis-Steele inclusive scans over the E entries (fixed order)
   for (int off = 1; off < kMaxE; off <<= 1) {
     int a = 0, b = 0, c = 0;
     if (e < kMaxE && e >= off) {
@@ -153,7 +180,7 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(
   }
   if (e < E) {
     const int start = s_tot[e] - tot;  // exclusive
-    for (int c = 0; c < n_chunks; ++c) chunk_counts[static_cast<int64_t>(c) * E + e] += start;
+    starts[e] = start;
     if (offsets) offsets[e] = start;
     if (distinct && tot > 0) distinct[s_nz[e] - 1] = e;
     if (tile_base) tile_base[e] = s_tiles[e] - (tot + tile_m - 1) / tile_m;
@@ -177,12 +204,13 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(
 __global__ __launch_bounds__(64) void group_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ slot_of_pair,
     const int32_t* __restrict__ table, int T, int k, int E, bool select_hits,
-    const int32_t* __restrict__ chunk_start, int32_t* __restrict__ perm,
-    int32_t* __restrict__ pos) {
+    const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ starts,
+    int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
   __shared__ int32_t cursor[kMaxE];
   const int chunk = blockIdx.x;
   const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) cursor[e] = chunk_start[static_cast<int64_t>(chunk) * E + e];
+  for (int e = lane; e < E; e += 64)
+    cursor[e] = starts[e] + chunk_start[static_cast<int64_t>(chunk) * E + e];
   __syncthreads();
   const int t0 = chunk * kGroupChunkTokens;
   const int t1 = min(T, t0 + kGroupChunkTokens);
@@ -236,7 +264,7 @@ hipError_t launch_lookup_small(const int32_t* idx, int T, int k, const int32_t* 
 
 size_t group_workspace_bytes(int T, int E) {
   const int64_t n_chunks = (T + kGroupChunkTokens - 1) / kGroupChunkTokens;
-  return static_cast<size_t>(align256(n_chunks * E * 4) + align256((E + 1) * 4));
+  return static_cast<size_t>(align256(n_chunks * E * 4) + align256(2 * kMaxE * 4));
 }
 
 GroupWorkspace group_workspace(void* ws, int T, int E) {
@@ -256,10 +284,12 @@ hipError_t launch_group_pairs(const int32_t* idx, const int32_t* slot_of_pair,
   const int n_chunks = (T + kGroupChunkTokens - 1) / kGroupChunkTokens;
   group_count_kernel<<<n_chunks, 256, 0, s>>>(idx, slot_of_pair, table, T, k, E, select_hits,
                                               gws.chunk_counts);
-  group_scan_kernel<<<1, 1024, 0, s>>>(n_chunks, E, T, gws.chunk_counts, offsets, distinct,
+  group_scan_chunks_kernel<<<E, kScanThreads, 0, s>>>(n_chunks, E, gws.chunk_counts,
+                                                      gws.totals);
+  group_scan_kernel<<<1, 1024, 0, s>>>(E, T, gws.totals, gws.totals + kMaxE, offsets, distinct,
                                        counts_out, tile_base, tile_m > 0 ? tile_m : 1);
   group_scatter_kernel<<<n_chunks, 64, 0, s>>>(idx, slot_of_pair, table, T, k, E, select_hits,
-                                               gws.chunk_counts, perm, pos);
+                                               gws.chunk_counts, gws.totals + kMaxE, perm, pos);
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ hipError_t launch_lookup_small(const int32_t* idx, int T, int k, const int32_t* 
 // the E groups plus one extra group of T rows (the shared expert).
 struct GroupWorkspace {
   int32_t* chunk_counts;  // [n_chunks * E]
-  int32_t* totals;        // [E + 1]
+  int32_t* totals;        // [2 * MOE_MAX_EXPERTS]: per-expert totals, then group starts
 };
 constexpr int kGroupChunkTokens = 32;
 size_t group_workspace_bytes(int T, int E);
