@@ -34,11 +34,14 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // native 16-byte 
 
 // A job: up to PM rows of one group (all rows of a routed expert's group in
 // practice) times PN output columns, reduced in steps of PK.
-constexpr int PM = 256;                  // rows (8 MFMA row tiles of 32)
-constexpr int PN = 128;                  // output columns
+constexpr int PM = 256;                  // rows: 8 MFMA tiles of 32 tokens
+constexpr int PN = 256;                  // output columns: 8 MFMA tiles of 32
 constexpr int PK = 64;                   // reduction step
 constexpr int PS = PK + 8;               // LDS row stride in bf16 (padding against bank conflicts)
-constexpr int PTHREADS = 256;            // 4 wavefronts; two workgroups share a CU
+constexpr int PTHREADS = 512;            // 8 wavefronts, two per SIMD
+constexpr int TILE_ELEMS = PM * PS;      // one LDS tile
+constexpr size_t PREFILL_LDS = 4 * TILE_ELEMS * sizeof(__bf16);   // A and B, double-buffered
+static_assert(PM == PN, "A and B tiles share one shape");
 
 struct GroupInfo {
   const int32_t* offsets;    // [E+1]
@@ -146,64 +149,198 @@ __device__ __forceinline__ void store_block_bf16(const BlockRaw& r, __bf16* dst)
     d4[q] = u32x4{packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]};
 }
 
-// One step's global loads, held in registers while the step before it is
-// multiplied.  A: the step's 64 bf16 of 8 tile rows, 32*i + t/8 for i = 0..7,
-// chunk t%8 of 16 bytes each (eight consecutive lanes read one 128-byte row
-// piece).  B: one packed block, block t%2 of tile row t/2.
-struct StepRegs {
-  u32x4 a[8];
-  BlockRaw b;
+// One step's global loads.  A: 64 bf16 of rows 64*i + t/8, i = 0..3, chunk
+// t%8 of 16 bytes (eight consecutive lanes read one 128-byte row piece).
+// B: block t%2 of weight row t/2.
+struct StepA {
+  u32x4 a[4];
 };
 
-template <int FMT, bool GATEUP>
-__device__ __forceinline__ void load_step(StepRegs& r, const uint16_t* __restrict__ a_src,
-                                          const uint32_t (&a_off)[8], int ch, int ks,
-                                          const uint8_t* __restrict__ base, const Planes& P,
-                                          int64_t b_row, int bb, int d, int f) {
+// Buffer resource over `bytes` bytes at base (raw, unswizzled; gfx9 word 3).
+// Loads through it take a 32-bit per-lane offset and a wave-uniform offset,
+// so the per-step advance costs no vector instructions.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ void load_a(StepA& r, BufRsrc rs, const uint32_t (&voff)[4], int ks) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    r.a[i] = *reinterpret_cast<const u32x4*>(a_src + a_off[i] + ks * PK + 8 * ch);
-  if (GATEUP) {   // G: units of 2 blocks, unit c of row r at c * 2f + r
-    const int64_t unit = static_cast<int64_t>(ks) * (2 * static_cast<int64_t>(f)) + b_row;
-    r.b = load_block<FMT>(base, P.codes + unit * 16 + 8 * bb, P.scale + unit * 4 + 2 * bb,
-                          P.min + unit * 4 + 2 * bb, P.hi + unit * 8 + 4 * bb);
-  } else {        // D: units of 1 block, unit c of row r at c * d + r
-    const int64_t unit = static_cast<int64_t>(2 * ks + bb) * d + b_row;
-    r.b = load_block<FMT>(base, P.codes + unit * 8, P.scale + unit * 2, P.min + unit * 2,
-                          P.hi + unit * 4);
-  }
+  for (int i = 0; i < 4; ++i)
+    r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], ks * (PK * 2), 0);
+}
+
+// The weight block of this thread for step ks: block vb of the step's
+// blocks, whose first block index is sblk (wave-uniform).
+template <int FMT, bool GATEUP>
+__device__ __forceinline__ BlockRaw load_b(BufRsrc rs, const Planes& P, uint32_t vb, int ks, int d,
+                                           int f) {
+  // G: units of 2 blocks, unit c of row r at c * 2f + r, so step ks starts
+  // at block 4f*ks; D: units of 1 block, unit c of row r at c * d + r, and a
+  // step is two units
+  const int64_t sblk = GATEUP ? static_cast<int64_t>(ks) * 4 * f : static_cast<int64_t>(ks) * 2 * d;
+  BlockRaw r;
+  const auto c = __builtin_amdgcn_raw_buffer_load_b64(rs, vb * 8,
+                                                      static_cast<int>(P.codes + sblk * 8), 0);
+  r.codes = make_uint2(c[0], c[1]);
+  r.scale = __builtin_amdgcn_raw_buffer_load_b16(rs, vb * 2, static_cast<int>(P.scale + sblk * 2),
+                                                 0);
+  r.min = FMT == MOE_FMT_Q2SM ? __builtin_amdgcn_raw_buffer_load_b16(
+                                    rs, vb * 2, static_cast<int>(P.min + sblk * 2), 0)
+                              : 0u;
+  r.hi = FMT == MOE_FMT_Q3G
+             ? __builtin_amdgcn_raw_buffer_load_b32(rs, vb * 4, static_cast<int>(P.hi + sblk * 4), 0)
+             : 0u;
+  return r;
+}
+
+// Rows past the group's end (bit i of valid clear) are neither loaded nor
+// stored: their LDS rows keep stale values that only reach output rows that
+// are never written.
+__device__ __forceinline__ void store_a(const StepA& r, __bf16* As, int tid, uint32_t valid) {
+  const int ar = tid >> 3, ch = tid & 7;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if ((valid >> i) & 1u) *reinterpret_cast<u32x4*>(As + (64 * i + ar) * PS + 8 * ch) = r.a[i];
 }
 
 template <int FMT>
-__device__ __forceinline__ void store_step(const StepRegs& r, __bf16* As, __bf16* Bs, int tid) {
-  const int ar = tid >> 3, ch = tid & 7;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<u32x4*>(As + (32 * i + ar) * PS + 8 * ch) = r.a[i];
-  store_block_bf16<FMT>(r.b, Bs + (tid >> 1) * PS + 32 * (tid & 1));
+__device__ __forceinline__ void store_b(const BlockRaw& b, __bf16* Bs, int tid) {
+  store_block_bf16<FMT>(b, Bs + (tid >> 1) * PS + 32 * (tid & 1));
 }
 
-// MFMAs of one step for a wavefront holding row tiles rh + 2i, i < nt, and
-// the two 32-column tiles at column 64*chf of the job.  All fragments of a
-// 16-wide sub-step are read first (reads of unused row tiles stay inside the
-// LDS tile), then the MFMAs of the used tiles run.
-__device__ __forceinline__ void mfma_step(f32x16 (&acc)[4][2], const __bf16* As, const __bf16* Bs,
-                                          int lane, int rh, int chf, int nt) {
+// MFMAs of one step for a wavefront holding token tiles rh + 2i, i < NT, and
+// the two 32-column tiles 2cq, 2cq + 1 of the job.  The weights are the MFMA's
+// first operand, so that an accumulator holds 4 consecutive columns of one
+// token per group of 4 registers: element r of lane l is column
+// 8(r/4) + 4(l/32) + r%4 of its tile and token l%32.
+template <int NT>
+struct Frags {
+  bf16x8 w[2];
+  bf16x8 x[NT > 0 ? NT : 1];
+};
+
+template <int NT>
+__device__ __forceinline__ void read_frags(Frags<NT>& fr, const __bf16* a0, const __bf16* b0,
+                                           int kk) {
+  fr.w[0] = *reinterpret_cast<const bf16x8*>(b0 + 16 * kk);
+  fr.w[1] = *reinterpret_cast<const bf16x8*>(b0 + 32 * PS + 16 * kk);
+#pragma unroll
+  for (int i = 0; i < NT; ++i) fr.x[i] = *reinterpret_cast<const bf16x8*>(a0 + 64 * i * PS + 16 * kk);
+}
+
+template <int NT>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[NT > 0 ? NT : 1][2], const __bf16* As,
+                                          const __bf16* Bs, int lane, int rh, int cq) {
   const __bf16* a0 = As + (32 * rh + (lane & 31)) * PS + 8 * (lane >> 5);
-  const __bf16* b0 = Bs + (64 * chf + (lane & 31)) * PS + 8 * (lane >> 5);
+  const __bf16* b0 = Bs + (64 * cq + (lane & 31)) * PS + 8 * (lane >> 5);
 #pragma unroll
   for (int kk = 0; kk < PK / 16; ++kk) {
-    const bf16x8 bv0 = *reinterpret_cast<const bf16x8*>(b0 + 16 * kk);
-    const bf16x8 bv1 = *reinterpret_cast<const bf16x8*>(b0 + 32 * PS + 16 * kk);
-    bf16x8 av[4];
+    Frags<NT> c;
+    read_frags<NT>(c, a0, b0, kk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      av[i] = *reinterpret_cast<const bf16x8*>(a0 + 64 * i * PS + 16 * kk);
+    for (int i = 0; i < NT; ++i) {
+      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.w[0], c.x[i], acc[i][0], 0, 0, 0);
+      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.w[1], c.x[i], acc[i][1], 0, 0, 0);
+    }
+  }
+}
+
+// Everything one workgroup needs to run one job.
+struct JobCtx {
+  BufRsrc a_rs;              // the A rows (x or H)
+  BufRsrc b_rs;              // the expert's slot
+  uint32_t a_voff[4];        // byte offsets of this thread's 4 A row pieces
+  uint32_t a_valid;          // bit i: A row i of this thread is inside the group
+  uint32_t vb;               // this thread's block within a step's blocks
+  int rows, cq, lane, tid;
+  int nK;
+};
+
+// One step of a job: step ks is multiplied from one LDS buffer while step
+// ks+1 (loaded one step earlier: x rows in ra, weight block in rb_use) goes
+// to the other: the x rows at once, then step ks+2 is requested (into ra and
+// rb_load), and the weight block is dequantized.  The last
+// stores of a job are repeats that nobody reads; they keep the loads
+// unconditional.
+template <int FMT, bool GATEUP, int NT, int RH>
+__device__ __forceinline__ void job_step(const JobCtx& c, const Planes& P, int d, int f,
+                                         __bf16* lds, int ks, f32x16 (&acc)[NT > 0 ? NT : 1][2],
+                                         StepA& ra, const BlockRaw& rb_use, BlockRaw& rb_load) {
+  __bf16* cur = lds + (ks & 1) * (2 * TILE_ELEMS);
+  __bf16* nxt = lds + ((ks + 1) & 1) * (2 * TILE_ELEMS);
+  store_a(ra, nxt, c.tid, c.a_valid);
+  const int kn = min(ks + 2, c.nK - 1);
+  load_a(ra, c.a_rs, c.a_voff, kn);
+  rb_load = load_b<FMT, GATEUP>(c.b_rs, P, c.vb, kn, d, f);
+  __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
+  if (NT > 0) mfma_step<NT>(acc, cur, cur + TILE_ELEMS, c.lane, RH, c.cq);
+  store_b<FMT>(rb_use, nxt + TILE_ELEMS, c.tid);
+  __syncthreads();
+}
+
+// One job for a wavefront holding NT token tiles (NT = 0: the wavefront only
+// loads and stores; every wavefront takes the same barriers).  The LDS holds
+// two steps, with one barrier per step.
+template <int FMT, bool GATEUP, int NT, int RH>
+__device__ __forceinline__ void run_job(const JobCtx& c, const Planes& P, int d, int f,
+                                        __bf16* lds, uint16_t* hdst, float* odst) {
+  f32x16 acc[NT > 0 ? NT : 1][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i < nt) {   // uniform
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv0, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv1, acc[i][1], 0, 0, 0);
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  StepA ra;
+  load_a(ra, c.a_rs, c.a_voff, 0);
+  BlockRaw rb0 = load_b<FMT, GATEUP>(c.b_rs, P, c.vb, 0, d, f), rb1;
+  store_a(ra, lds, c.tid, c.a_valid);
+  store_b<FMT>(rb0, lds + TILE_ELEMS, c.tid);
+  load_a(ra, c.a_rs, c.a_voff, min(1, c.nK - 1));
+  rb0 = load_b<FMT, GATEUP>(c.b_rs, P, c.vb, min(1, c.nK - 1), d, f);
+  __syncthreads();
+  // two steps per trip, so that the two weight registers swap roles without
+  // a copy (a copy would wait for the loads just issued)
+  int ks = 0;
+  for (; ks + 1 < c.nK; ks += 2) {
+    job_step<FMT, GATEUP, NT, RH>(c, P, d, f, lds, ks, acc, ra, rb0, rb1);
+    job_step<FMT, GATEUP, NT, RH>(c, P, d, f, lds, ks + 1, acc, ra, rb1, rb0);
+  }
+  if (ks < c.nK) job_step<FMT, GATEUP, NT, RH>(c, P, d, f, lds, ks, acc, ra, rb0, rb1);
+  if (NT == 0) return;
+
+  // epilogue: lane l holds token 32(rh + 2i) + l%32; registers 4q..4q+3 of
+  // tile j hold 4 consecutive columns.  The row stride and this lane's token
+  // are hidden from the optimizer so that per-element offsets are not hoisted
+  // out of the job loop.
+  uint32_t ld = GATEUP ? f : d;
+  int mt = 32 * RH + (c.lane & 31);
+  opaque(ld);
+  opaque(mt);
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int m = mt + 64 * i;
+    if (m < c.rows) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (GATEUP) {
+          uint2 v;
+          v.x = pack_bf16x2(silu_fast(acc[i][0][4 * q]) * acc[i][1][4 * q],
+                            silu_fast(acc[i][0][4 * q + 1]) * acc[i][1][4 * q + 1]);
+          v.y = pack_bf16x2(silu_fast(acc[i][0][4 * q + 2]) * acc[i][1][4 * q + 2],
+                            silu_fast(acc[i][0][4 * q + 3]) * acc[i][1][4 * q + 3]);
+          *reinterpret_cast<uint2*>(hdst + static_cast<uint32_t>(m) * ld + 8 * q) = v;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                         acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            *reinterpret_cast<float4*>(odst + static_cast<uint32_t>(m) * ld + 32 * j + 8 * q) = v;
+          }
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -213,22 +350,29 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[4][2], const __bf16* As,
 // GATEUP: A = gathered x rows (bf16 [T][d]), B = G rows, epilogue silu(g)*u -> H bf16.
 // !GATEUP: A = H rows of the group, B = D rows, epilogue fp32 rows.
 template <int FMT, bool GATEUP>
-__global__ __launch_bounds__(PTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void
-prefill_gemm_kernel(const uint8_t* __restrict__ pool, int64_t slot_bytes, Planes P, int d, int f,
-                    GroupInfo g, const uint16_t* __restrict__ a_src, uint16_t* __restrict__ h_out,
-                    float* __restrict__ out_pairs, float* __restrict__ out_shared) {
-  __shared__ __attribute__((aligned(16))) __bf16 As[PM * PS];
-  __shared__ __attribute__((aligned(16))) __bf16 Bs[PN * PS];
+__global__ __launch_bounds__(PTHREADS) void prefill_gemm_kernel(
+    const uint8_t* __restrict__ pool, int64_t slot_bytes, Planes P, int d, int f, GroupInfo g,
+    const uint16_t* __restrict__ a_src, uint16_t* __restrict__ h_out,
+    float* __restrict__ out_pairs, float* __restrict__ out_shared) {
+  extern __shared__ __attribute__((aligned(16))) __bf16 lds[];
   const int K = GATEUP ? d : f;              // reduction length
   const int N = GATEUP ? 2 * f : d;          // output columns of the job space
-  const int nK = K / PK;
   const int n_slices = (N + PN - 1) / PN;
   const int n_gm = g.tile_base[g.E + 1];     // (group, 256-row chunk) items
   const int total = ((n_gm + 7) / 8) * 8 * n_slices;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int chf = wave & 1;                  // column half: 64 columns, two MFMA tiles
-  const int rh = wave >> 1;                  // row tiles rh, rh + 2, rh + 4, rh + 6
+  JobCtx c;
+  c.tid = threadIdx.x;
+  c.lane = c.tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
+  // wavefronts w and w + 4 share a SIMD: they take the two token-tile
+  // parities of the same columns, so every SIMD gets half of the rows
+  c.cq = wave & 3;                           // columns 64cq .. 64cq + 63
+  const int rh = wave >> 2;                  // token tiles rh, rh + 2, rh + 4, rh + 6
+  c.nK = K / PK;
+  // x is [T][d]; H is [T*k + T][f] (the host keeps it under 4 GiB)
+  c.a_rs = buf_rsrc(a_src, GATEUP ? static_cast<uint32_t>(g.T) * d * 2
+                                  : static_cast<uint32_t>(g.T * (g.k + 1)) * f * 2);
+  const int br = c.tid >> 1, bb = c.tid & 1;
 
   for (int job = blockIdx.x; job < total; job += gridDim.x) {
     const int q = job >> 3;
@@ -237,97 +381,56 @@ prefill_gemm_kernel(const uint8_t* __restrict__ pool, int64_t slot_bytes, Planes
     if (gm >= n_gm) continue;                // uniform: a padding job
     const TileInfo ti = find_tile(g, gm);
     if (ti.slot < 0) continue;               // the shared group when no shared output is wanted
-    const uint8_t* __restrict__ base = pool + static_cast<int64_t>(ti.slot) * slot_bytes;
-    const int rows = ti.rows;
-    const int row_tiles = (rows + 31) >> 5;
-    const int nt = min(4, max(0, (row_tiles - rh + 1) >> 1));   // this wavefront's row tiles
+    c.b_rs = buf_rsrc(pool + static_cast<int64_t>(ti.slot) * slot_bytes,
+                      static_cast<uint32_t>(slot_bytes));
+    c.rows = ti.rows;
+    const int row_tiles = (c.rows + 31) >> 5;
+    const bool cols_ok = GATEUP ? (ns * (PN / 2) + 32 * c.cq < f) : (ns * PN + 64 * c.cq < d);
+    const int nt = cols_ok ? min(4, max(0, (row_tiles - rh + 1) >> 1)) : 0;
 
-    // the 8 A rows this thread loads (clamped: rows past the group's end are
-    // loaded but never stored), as element offsets; its B tile row and block
-    uint32_t a_off[8];
+    // the 4 A rows of this thread, 16-byte piece t%8 of each (a row past the
+    // group's end gets an offset outside the buffer: its loads return zero
+    // without a memory access); its weight block
+    c.a_valid = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ar = min(32 * i + (tid >> 3), rows - 1);
-      a_off[i] = GATEUP ? static_cast<uint32_t>(tile_token(g, ti, ti.m0 + ar)) * d
-                        : static_cast<uint32_t>(ti.row_base + ti.m0 + ar) * f;
+    for (int i = 0; i < 4; ++i) {
+      const int ar0 = 64 * i + (c.tid >> 3);
+      const int ar = min(ar0, c.rows - 1);
+      const uint32_t row = GATEUP ? static_cast<uint32_t>(tile_token(g, ti, ti.m0 + ar))
+                                  : static_cast<uint32_t>(ti.row_base + ti.m0 + ar);
+      const bool ok = ar0 < c.rows;
+      c.a_voff[i] = ok ? row * (2u * K) + 16u * (c.tid & 7) : 0xFFFFFF00u;
+      c.a_valid |= (ok ? 1u : 0u) << i;
     }
-    const int ch = tid & 7;
-    const int br = tid >> 1, bb = tid & 1;
-    int64_t b_row;
-    if (GATEUP) {   // B rows: [gate h0..31 | up h0..31 | gate h32..63 | up h32..63]
+    if (GATEUP) {   // weight rows: tile 2j = gate, tile 2j+1 = up of h block j
       const int h = min(ns * (PN / 2) + (br >> 6) * 32 + (br & 31), f - 1);
-      b_row = 2 * static_cast<int64_t>(h) + ((br >> 5) & 1);
+      const uint32_t b_row = 2u * h + ((br >> 5) & 1);
+      c.vb = 2u * b_row + bb;
     } else {
-      b_row = min(ns * PN + br, d - 1);
+      const uint32_t b_row = min(ns * PN + br, d - 1);
+      c.vb = static_cast<uint32_t>(bb) * d + b_row;
     }
-    const bool cols_ok = GATEUP ? (ns * (PN / 2) + chf * 32 < f) : (ns * PN + chf * 64 < d);
-
-    f32x16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // Step ks+1 is loaded into registers while step ks is multiplied; the
-    // other workgroup on the CU fills the gaps at the two barriers.
-    StepRegs R;
-    load_step<FMT, GATEUP>(R, a_src, a_off, ch, 0, base, P, b_row, bb, d, f);
-    store_step<FMT>(R, As, Bs, tid);
-    __syncthreads();
-    for (int ks = 0; ks < nK; ++ks) {
-      const bool more = ks + 1 < nK;
-      if (more) load_step<FMT, GATEUP>(R, a_src, a_off, ch, ks + 1, base, P, b_row, bb, d, f);
-      if (cols_ok) {
-        mfma_step(acc, As, Bs, lane, rh, chf, nt);
-      }
-      __syncthreads();
-      if (more) {
-        store_step<FMT>(R, As, Bs, tid);
-        __syncthreads();
-      }
+    uint16_t* hdst = nullptr;
+    float* odst = nullptr;
+    if (GATEUP) {
+      hdst = h_out + static_cast<int64_t>(ti.row_base + ti.m0) * f + ns * (PN / 2) + 32 * c.cq +
+             4 * (c.lane >> 5);
+    } else {
+      odst = (ti.group < g.E ? out_pairs + static_cast<int64_t>(ti.row_base + ti.m0) * d
+                             : out_shared + static_cast<int64_t>(ti.m0) * d) +
+             static_cast<int64_t>(ns) * PN + 64 * c.cq + 4 * (c.lane >> 5);
     }
-
-    // epilogue: accumulator element r of lane l holds row 8(r/4) + 4(l/32) + r%4
-    // and column l%32 of its 32 x 32 tile
-    if (cols_ok) {
-      // row stride of the output and this lane's row base, hidden from the
-      // optimizer per job so that per-element offsets are not hoisted out of
-      // the job loop
-      uint32_t ld = GATEUP ? f : d;
-      int mlane = 4 * (lane >> 5);
-      opaque(ld);
-      opaque(mlane);
-      uint16_t* hdst = nullptr;
-      float* odst = nullptr;
-      if (GATEUP) {
-        hdst = h_out + static_cast<int64_t>(ti.row_base + ti.m0) * f + ns * (PN / 2) + 32 * chf +
-               (lane & 31);
-      } else {
-        odst = (ti.group < g.E ? out_pairs + static_cast<int64_t>(ti.row_base + ti.m0) * d
-                               : out_shared + static_cast<int64_t>(ti.m0) * d) +
-               static_cast<int64_t>(ns) * PN + 64 * chf + (lane & 31);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i >= nt) continue;   // uniform
-        const int rt = rh + 2 * i;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = 32 * rt + 8 * (r >> 2) + (r & 3) + mlane;
-          if (m < rows) {
-            if (GATEUP) {
-              hdst[static_cast<uint32_t>(m) * ld] =
-                  float_to_bf16_rne(silu_fast(acc[i][0][r]) * acc[i][1][r]);
-            } else {
-              odst[static_cast<uint32_t>(m) * ld] = acc[i][0][r];
-              odst[static_cast<uint32_t>(m) * ld + 32] = acc[i][1][r];
-            }
-          }
-          if ((r & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+    switch (2 * nt + rh) {   // uniform per wavefront
+      case 8: run_job<FMT, GATEUP, 4, 0>(c, P, d, f, lds, hdst, odst); break;
+      case 9: run_job<FMT, GATEUP, 4, 1>(c, P, d, f, lds, hdst, odst); break;
+      case 6: run_job<FMT, GATEUP, 3, 0>(c, P, d, f, lds, hdst, odst); break;
+      case 7: run_job<FMT, GATEUP, 3, 1>(c, P, d, f, lds, hdst, odst); break;
+      case 4: run_job<FMT, GATEUP, 2, 0>(c, P, d, f, lds, hdst, odst); break;
+      case 5: run_job<FMT, GATEUP, 2, 1>(c, P, d, f, lds, hdst, odst); break;
+      case 2: run_job<FMT, GATEUP, 1, 0>(c, P, d, f, lds, hdst, odst); break;
+      case 3: run_job<FMT, GATEUP, 1, 1>(c, P, d, f, lds, hdst, odst); break;
+      case 0: run_job<FMT, GATEUP, 0, 0>(c, P, d, f, lds, hdst, odst); break;
+      default: run_job<FMT, GATEUP, 0, 1>(c, P, d, f, lds, hdst, odst); break;
     }
   }
 }
@@ -354,7 +457,7 @@ PrefillWs prefill_ws(void* ws, int d, int f, int T, int k, int E) {
   return w;
 }
 
-// Persistent grid: two workgroups per CU, a multiple of 8 so that job j and
+// Persistent grid: one workgroup per CU, a multiple of 8 so that job j and
 // workgroup j mod grid share an XCD.
 int prefill_grid(int64_t max_jobs) {
   static int n_cu = 0;
@@ -367,7 +470,7 @@ int prefill_grid(int64_t max_jobs) {
       n_cu = prop.multiProcessorCount;
   }
   int64_t grid = (max_jobs + 7) / 8 * 8;
-  const int64_t cap = (2 * n_cu + 7) / 8 * 8;
+  const int64_t cap = (n_cu + 7) / 8 * 8;
   if (grid > cap) grid = cap;
   return static_cast<int>(grid > 8 ? grid : 8);
 }
@@ -376,7 +479,15 @@ template <int FMT, bool GATEUP>
 hipError_t launch_gemm(const GroupInfo& g, int64_t max_jobs, const moe_layer& L, Planes P,
                        const uint16_t* a, uint16_t* h, float* out_pairs, float* out_shared,
                        hipStream_t s) {
-  prefill_gemm_kernel<FMT, GATEUP><<<prefill_grid(max_jobs), PTHREADS, 0, s>>>(
+  static bool lds_set = false;   // per instantiation
+  if (!lds_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&prefill_gemm_kernel<FMT, GATEUP>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(PREFILL_LDS));
+    if (e != hipSuccess) return e;
+    lds_set = true;
+  }
+  prefill_gemm_kernel<FMT, GATEUP><<<prefill_grid(max_jobs), PTHREADS, PREFILL_LDS, s>>>(
       static_cast<const uint8_t*>(L.pool), L.slot_bytes, P, L.d_model, L.d_ff, g, a, h, out_pairs,
       out_shared);
   return hipGetLastError();
