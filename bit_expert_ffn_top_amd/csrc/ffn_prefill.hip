@@ -38,7 +38,9 @@ constexpr int PM = 256;                  // rows: 8 MFMA tiles of 32 tokens
 constexpr int PN = 256;                  // output columns: 8 MFMA tiles of 32
 constexpr int PK = 64;                   // reduction step
 constexpr int PS = PK + 8;               // LDS row stride in bf16 (padding against bank conflicts)
-constexpr int PTHREADS = 512;            // 8 wavefronts, two per SIMD
+constexpr int NCONS = 512;               // 8 MFMA wavefronts, two per SIMD
+constexpr int NPROD = 256;               // 4 loading / dequantizing wavefronts, one per SIMD
+constexpr int PTHREADS = NCONS + NPROD;
 constexpr int TILE_ELEMS = PM * PS;      // one LDS tile
 constexpr size_t PREFILL_LDS = 4 * TILE_ELEMS * sizeof(__bf16);   // A and B, double-buffered
 static_assert(PM == PN, "A and B tiles share one shape");
@@ -126,11 +128,51 @@ __device__ __forceinline__ BlockRaw load_block(const uint8_t* base, int64_t oc, 
 
 // The block's 32 weights (dequant_one, rounded to bf16 nearest even) as 64
 // bytes at dst.
+// 16 codes of one 32-bit word (2-bit formats) as weights m + s*q: each code is
+// read as an fp16 value c_j + q in place (the extraction of the decode path,
+// c_j = q2_offset(j)), and w = s*(c_j + q) + (m - c_j*s) in one fused
+// multiply-add.  m - c_j*s is exact unless 0 < |m| < s/128, so w is then the
+// correctly rounded m + s*q, as the plain formula gives.
+__device__ __forceinline__ void weights16_q2(uint32_t w, float s, float m, float (&out)[16]) {
+  const uint32_t b = w >> 6, c = w << 6;
+  const uint32_t rr[8] = {
+      and_or(c, 0x00C000C0u, 0x4C004C00u),   // 16+q0  | 16+q8
+      and_or(c, 0x03000300u, 0x44004400u),   // 4+q1   | 4+q9
+      and_or(w, 0x00300030u, 0x54005400u),   // 64+q2  | 64+q10
+      and_or(w, 0x00C000C0u, 0x4C004C00u),   // 16+q3  | 16+q11
+      and_or(w, 0x03000300u, 0x44004400u),   // 4+q4   | 4+q12
+      and_or(b, 0x00300030u, 0x54005400u),   // 64+q5  | 64+q13
+      and_or(b, 0x00C000C0u, 0x4C004C00u),   // 16+q6  | 16+q14
+      and_or(b, 0x03000300u, 0x44004400u)};  // 4+q7   | 4+q15
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float mj = fmaf(-q2_offset(j), s, m);
+    out[j] = fmaf(s, h_lo(rr[j]), mj);
+    out[j + 8] = fmaf(s, h_hi(rr[j]), mj);
+  }
+}
+
 template <int FMT>
 __device__ __forceinline__ void store_block_bf16(const BlockRaw& r, __bf16* dst) {
   const float s = half_bits_to_float(r.scale);
   const float m = half_bits_to_float(r.min);
   uint32_t packed[16];
+  if (FMT != MOE_FMT_Q3G) {
+    // Q2S: s*(q - 1.5) = s*q + (-1.5 s), -1.5 s exact
+    const float m0 = FMT == MOE_FMT_Q2SM ? m : -1.5f * s;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float wv[16];
+      weights16_q2(h == 0 ? r.codes.x : r.codes.y, s, m0, wv);
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) packed[8 * h + j / 2] = pack_bf16x2(wv[j], wv[j + 1]);
+    }
+    u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      d4[q] = u32x4{packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]};
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 32; j += 2) {
     const uint32_t word = j < 16 ? r.codes.x : r.codes.y;
@@ -149,13 +191,6 @@ __device__ __forceinline__ void store_block_bf16(const BlockRaw& r, __bf16* dst)
     d4[q] = u32x4{packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]};
 }
 
-// One step's global loads.  A: 64 bf16 of rows 64*i + t/8, i = 0..3, chunk
-// t%8 of 16 bytes (eight consecutive lanes read one 128-byte row piece).
-// B: block t%2 of weight row t/2.
-struct StepA {
-  u32x4 a[4];
-};
-
 // Buffer resource over `bytes` bytes at base (raw, unswizzled; gfx9 word 3).
 // Loads through it take a 32-bit per-lane offset and a wave-uniform offset,
 // so the per-step advance costs no vector instructions.
@@ -163,12 +198,6 @@ typedef __amdgpu_buffer_rsrc_t BufRsrc;
 __device__ __forceinline__ BufRsrc buf_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
                                            static_cast<int>(bytes), 0x00020000);
-}
-
-__device__ __forceinline__ void load_a(StepA& r, BufRsrc rs, const uint32_t (&voff)[4], int ks) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i], ks * (PK * 2), 0);
 }
 
 // The weight block of this thread for step ks: block vb of the step's
@@ -195,19 +224,67 @@ __device__ __forceinline__ BlockRaw load_b(BufRsrc rs, const Planes& P, uint32_t
   return r;
 }
 
+// Producer side.  The 256 producer threads (index p) load one step: A rows
+// 32*i + p/8 (i = 0..7), 16-byte piece p%8 of each (eight consecutive lanes
+// read one 128-byte row piece), and both weight blocks of tile row p.
+struct StepRegs {
+  u32x4 a[8];
+  BlockRaw b[2];
+};
+
+struct ProdCtx {
+  BufRsrc a_rs;              // the A rows (x or H)
+  BufRsrc b_rs;              // the expert's slot
+  uint32_t a_voff[8];        // byte offsets of this thread's 8 A row pieces
+  uint32_t a_valid;          // bit i: A row i of this thread is inside the group
+  uint32_t vb[2];            // this thread's two blocks within a step's blocks
+  int p, nK;
+};
+
+template <int FMT, bool GATEUP>
+__device__ __forceinline__ void load_step(StepRegs& r, const ProdCtx& c, const Planes& P, int ks,
+                                          int d, int f) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(c.a_rs, c.a_voff[i], ks * (PK * 2), 0);
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) r.b[bb] = load_b<FMT, GATEUP>(c.b_rs, P, c.vb[bb], ks, d, f);
+}
+
 // Rows past the group's end (bit i of valid clear) are neither loaded nor
 // stored: their LDS rows keep stale values that only reach output rows that
 // are never written.
-__device__ __forceinline__ void store_a(const StepA& r, __bf16* As, int tid, uint32_t valid) {
-  const int ar = tid >> 3, ch = tid & 7;
+template <int FMT>
+__device__ __forceinline__ void store_step(const StepRegs& r, __bf16* As, __bf16* Bs,
+                                           const ProdCtx& c) {
+  const int ar = c.p >> 3, ch = c.p & 7;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if ((valid >> i) & 1u) *reinterpret_cast<u32x4*>(As + (64 * i + ar) * PS + 8 * ch) = r.a[i];
+  for (int i = 0; i < 8; ++i)
+    if ((c.a_valid >> i) & 1u)
+      *reinterpret_cast<u32x4*>(As + (32 * i + ar) * PS + 8 * ch) = r.a[i];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) store_block_bf16<FMT>(r.b[bb], Bs + c.p * PS + 32 * bb);
 }
 
-template <int FMT>
-__device__ __forceinline__ void store_b(const BlockRaw& b, __bf16* Bs, int tid) {
-  store_block_bf16<FMT>(b, Bs + (tid >> 1) * PS + 32 * (tid & 1));
+// The producers' part of a job.  The LDS holds two steps: while the MFMA
+// wavefronts multiply step ks from one buffer, step ks+1 (loaded one step
+// earlier) is written to the other and step ks+2 is requested; one barrier
+// per step.  The last store of a job is a repeat that nobody reads; it keeps
+// the loads unconditional.
+template <int FMT, bool GATEUP>
+__device__ __forceinline__ void produce_job(const ProdCtx& c, const Planes& P, int d, int f,
+                                            __bf16* lds) {
+  StepRegs R;
+  load_step<FMT, GATEUP>(R, c, P, 0, d, f);
+  store_step<FMT>(R, lds, lds + TILE_ELEMS, c);
+  load_step<FMT, GATEUP>(R, c, P, min(1, c.nK - 1), d, f);
+  __syncthreads();
+  for (int ks = 0; ks < c.nK; ++ks) {
+    __bf16* nxt = lds + ((ks + 1) & 1) * (2 * TILE_ELEMS);
+    store_step<FMT>(R, nxt, nxt + TILE_ELEMS, c);
+    load_step<FMT, GATEUP>(R, c, P, min(ks + 2, c.nK - 1), d, f);
+    __syncthreads();
+  }
 }
 
 // MFMAs of one step for a wavefront holding token tiles rh + 2i, i < NT, and
@@ -247,45 +324,11 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[NT > 0 ? NT : 1][2], con
   }
 }
 
-// Everything one workgroup needs to run one job.
-struct JobCtx {
-  BufRsrc a_rs;              // the A rows (x or H)
-  BufRsrc b_rs;              // the expert's slot
-  uint32_t a_voff[4];        // byte offsets of this thread's 4 A row pieces
-  uint32_t a_valid;          // bit i: A row i of this thread is inside the group
-  uint32_t vb;               // this thread's block within a step's blocks
-  int rows, cq, lane, tid;
-  int nK;
-};
-
-// One step of a job: step ks is multiplied from one LDS buffer while step
-// ks+1 (loaded one step earlier: x rows in ra, weight block in rb_use) goes
-// to the other: the x rows at once, then step ks+2 is requested (into ra and
-// rb_load), and the weight block is dequantized.  The last
-// stores of a job are repeats that nobody reads; they keep the loads
-// unconditional.
-template <int FMT, bool GATEUP, int NT, int RH>
-__device__ __forceinline__ void job_step(const JobCtx& c, const Planes& P, int d, int f,
-                                         __bf16* lds, int ks, f32x16 (&acc)[NT > 0 ? NT : 1][2],
-                                         StepA& ra, const BlockRaw& rb_use, BlockRaw& rb_load) {
-  __bf16* cur = lds + (ks & 1) * (2 * TILE_ELEMS);
-  __bf16* nxt = lds + ((ks + 1) & 1) * (2 * TILE_ELEMS);
-  store_a(ra, nxt, c.tid, c.a_valid);
-  const int kn = min(ks + 2, c.nK - 1);
-  load_a(ra, c.a_rs, c.a_voff, kn);
-  rb_load = load_b<FMT, GATEUP>(c.b_rs, P, c.vb, kn, d, f);
-  __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
-  if (NT > 0) mfma_step<NT>(acc, cur, cur + TILE_ELEMS, c.lane, RH, c.cq);
-  store_b<FMT>(rb_use, nxt + TILE_ELEMS, c.tid);
-  __syncthreads();
-}
-
-// One job for a wavefront holding NT token tiles (NT = 0: the wavefront only
-// loads and stores; every wavefront takes the same barriers).  The LDS holds
-// two steps, with one barrier per step.
-template <int FMT, bool GATEUP, int NT, int RH>
-__device__ __forceinline__ void run_job(const JobCtx& c, const Planes& P, int d, int f,
-                                        __bf16* lds, uint16_t* hdst, float* odst) {
+// The MFMA wavefronts' part of a job, for a wavefront holding NT token
+// tiles of parity RH (NT = 0: it only takes the barriers).
+template <bool GATEUP, int NT, int RH>
+__device__ __forceinline__ void consume_job(int nK, int lane, int cq, int rows, int d, int f,
+                                            const __bf16* lds, uint16_t* hdst, float* odst) {
   f32x16 acc[NT > 0 ? NT : 1][2];
 #pragma unroll
   for (int i = 0; i < NT; ++i)
@@ -293,23 +336,12 @@ __device__ __forceinline__ void run_job(const JobCtx& c, const Planes& P, int d,
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  StepA ra;
-  load_a(ra, c.a_rs, c.a_voff, 0);
-  BlockRaw rb0 = load_b<FMT, GATEUP>(c.b_rs, P, c.vb, 0, d, f), rb1;
-  store_a(ra, lds, c.tid, c.a_valid);
-  store_b<FMT>(rb0, lds + TILE_ELEMS, c.tid);
-  load_a(ra, c.a_rs, c.a_voff, min(1, c.nK - 1));
-  rb0 = load_b<FMT, GATEUP>(c.b_rs, P, c.vb, min(1, c.nK - 1), d, f);
-  __syncthreads();
-  // two steps per trip, so that the two weight registers swap roles without
-  // a copy (a copy would wait for the loads just issued)
-  int ks = 0;
-  for (; ks + 1 < c.nK; ks += 2) {
-    job_step<FMT, GATEUP, NT, RH>(c, P, d, f, lds, ks, acc, ra, rb0, rb1);
-    job_step<FMT, GATEUP, NT, RH>(c, P, d, f, lds, ks + 1, acc, ra, rb1, rb0);
+  __syncthreads();   // step 0 is in buffer 0
+  for (int ks = 0; ks < nK; ++ks) {
+    const __bf16* cur = lds + (ks & 1) * (2 * TILE_ELEMS);
+    if (NT > 0) mfma_step<NT>(acc, cur, cur + TILE_ELEMS, lane, RH, cq);
+    __syncthreads();
   }
-  if (ks < c.nK) job_step<FMT, GATEUP, NT, RH>(c, P, d, f, lds, ks, acc, ra, rb0, rb1);
   if (NT == 0) return;
 
   // epilogue: lane l holds token 32(rh + 2i) + l%32; registers 4q..4q+3 of
@@ -317,13 +349,13 @@ __device__ __forceinline__ void run_job(const JobCtx& c, const Planes& P, int d,
   // are hidden from the optimizer so that per-element offsets are not hoisted
   // out of the job loop.
   uint32_t ld = GATEUP ? f : d;
-  int mt = 32 * RH + (c.lane & 31);
+  int mt = 32 * RH + (lane & 31);
   opaque(ld);
   opaque(mt);
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const int m = mt + 64 * i;
-    if (m < c.rows) {
+    if (m < rows) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (GATEUP) {
@@ -349,6 +381,8 @@ __device__ __forceinline__ void run_job(const JobCtx& c, const Planes& P, int d,
 
 // GATEUP: A = gathered x rows (bf16 [T][d]), B = G rows, epilogue silu(g)*u -> H bf16.
 // !GATEUP: A = H rows of the group, B = D rows, epilogue fp32 rows.
+// Wavefronts 0..7 run the MFMAs, 8..11 load and dequantize; both walk the
+// same jobs and take the same barriers.
 template <int FMT, bool GATEUP>
 __global__ __launch_bounds__(PTHREADS) void prefill_gemm_kernel(
     const uint8_t* __restrict__ pool, int64_t slot_bytes, Planes P, int d, int f, GroupInfo g,
@@ -357,80 +391,96 @@ __global__ __launch_bounds__(PTHREADS) void prefill_gemm_kernel(
   extern __shared__ __attribute__((aligned(16))) __bf16 lds[];
   const int K = GATEUP ? d : f;              // reduction length
   const int N = GATEUP ? 2 * f : d;          // output columns of the job space
+  const int nK = K / PK;
   const int n_slices = (N + PN - 1) / PN;
   const int n_gm = g.tile_base[g.E + 1];     // (group, 256-row chunk) items
   const int total = ((n_gm + 7) / 8) * 8 * n_slices;
-  JobCtx c;
-  c.tid = threadIdx.x;
-  c.lane = c.tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(c.tid >> 6);
-  // wavefronts w and w + 4 share a SIMD: they take the two token-tile
-  // parities of the same columns, so every SIMD gets half of the rows
-  c.cq = wave & 3;                           // columns 64cq .. 64cq + 63
-  const int rh = wave >> 2;                  // token tiles rh, rh + 2, rh + 4, rh + 6
-  c.nK = K / PK;
-  // x is [T][d]; H is [T*k + T][f] (the host keeps it under 4 GiB)
-  c.a_rs = buf_rsrc(a_src, GATEUP ? static_cast<uint32_t>(g.T) * d * 2
-                                  : static_cast<uint32_t>(g.T * (g.k + 1)) * f * 2);
-  const int br = c.tid >> 1, bb = c.tid & 1;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  for (int job = blockIdx.x; job < total; job += gridDim.x) {
-    const int q = job >> 3;
-    const int ns = q % n_slices;
-    const int gm = (q / n_slices) * 8 + (job & 7);
-    if (gm >= n_gm) continue;                // uniform: a padding job
-    const TileInfo ti = find_tile(g, gm);
-    if (ti.slot < 0) continue;               // the shared group when no shared output is wanted
-    c.b_rs = buf_rsrc(pool + static_cast<int64_t>(ti.slot) * slot_bytes,
-                      static_cast<uint32_t>(slot_bytes));
-    c.rows = ti.rows;
-    const int row_tiles = (c.rows + 31) >> 5;
-    const bool cols_ok = GATEUP ? (ns * (PN / 2) + 32 * c.cq < f) : (ns * PN + 64 * c.cq < d);
-    const int nt = cols_ok ? min(4, max(0, (row_tiles - rh + 1) >> 1)) : 0;
-
-    // the 4 A rows of this thread, 16-byte piece t%8 of each (a row past the
-    // group's end gets an offset outside the buffer: its loads return zero
-    // without a memory access); its weight block
-    c.a_valid = 0;
+  if (wave < NCONS / 64) {
+    const int lane = tid & 63;
+    // wavefronts w and w + 4 share a SIMD: they take the two token-tile
+    // parities of the same columns, so every SIMD gets half of the rows
+    const int cq = wave & 3;                 // columns 64cq .. 64cq + 63
+    const int rh = wave >> 2;                // token tiles rh, rh + 2, rh + 4, rh + 6
+    for (int job = blockIdx.x; job < total; job += gridDim.x) {
+      const int q = job >> 3;
+      const int ns = q % n_slices;
+      const int gm = (q / n_slices) * 8 + (job & 7);
+      if (gm >= n_gm) continue;              // uniform: a padding job
+      const TileInfo ti = find_tile(g, gm);
+      if (ti.slot < 0) continue;             // the shared group when no shared output is wanted
+      const int rows = ti.rows;
+      const int row_tiles = (rows + 31) >> 5;
+      const bool cols_ok = GATEUP ? (ns * (PN / 2) + 32 * cq < f) : (ns * PN + 64 * cq < d);
+      const int nt = cols_ok ? min(4, max(0, (row_tiles - rh + 1) >> 1)) : 0;
+      uint16_t* hdst = nullptr;
+      float* odst = nullptr;
+      if (GATEUP) {
+        hdst = h_out + static_cast<int64_t>(ti.row_base + ti.m0) * f + ns * (PN / 2) + 32 * cq +
+               4 * (lane >> 5);
+      } else {
+        odst = (ti.group < g.E ? out_pairs + static_cast<int64_t>(ti.row_base + ti.m0) * d
+                               : out_shared + static_cast<int64_t>(ti.m0) * d) +
+               static_cast<int64_t>(ns) * PN + 64 * cq + 4 * (lane >> 5);
+      }
+#define BITFFN_CONSUME(NT_, RH_) \
+  consume_job<GATEUP, NT_, RH_>(nK, lane, cq, rows, d, f, lds, hdst, odst)
+      switch (2 * nt + rh) {   // uniform per wavefront
+        case 8: BITFFN_CONSUME(4, 0); break;
+        case 9: BITFFN_CONSUME(4, 1); break;
+        case 6: BITFFN_CONSUME(3, 0); break;
+        case 7: BITFFN_CONSUME(3, 1); break;
+        case 4: BITFFN_CONSUME(2, 0); break;
+        case 5: BITFFN_CONSUME(2, 1); break;
+        case 2: BITFFN_CONSUME(1, 0); break;
+        case 3: BITFFN_CONSUME(1, 1); break;
+        default: BITFFN_CONSUME(0, 0); break;
+      }
+#undef BITFFN_CONSUME
+    }
+  } else {
+    ProdCtx c;
+    c.p = tid - NCONS;
+    c.nK = nK;
+    // x is [T][d]; H is [T*k + T][f] (the host keeps it under 4 GiB)
+    c.a_rs = buf_rsrc(a_src, GATEUP ? static_cast<uint32_t>(g.T) * d * 2
+                                    : static_cast<uint32_t>(g.T * (g.k + 1)) * f * 2);
+    for (int job = blockIdx.x; job < total; job += gridDim.x) {
+      const int q = job >> 3;
+      const int ns = q % n_slices;
+      const int gm = (q / n_slices) * 8 + (job & 7);
+      if (gm >= n_gm) continue;
+      const TileInfo ti = find_tile(g, gm);
+      if (ti.slot < 0) continue;
+      c.b_rs = buf_rsrc(pool + static_cast<int64_t>(ti.slot) * slot_bytes,
+                        static_cast<uint32_t>(slot_bytes));
+      // the 8 A rows of this thread (a row past the group's end gets an
+      // offset outside the buffer: its loads return zero without a memory
+      // access)
+      c.a_valid = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ar0 = 64 * i + (c.tid >> 3);
-      const int ar = min(ar0, c.rows - 1);
-      const uint32_t row = GATEUP ? static_cast<uint32_t>(tile_token(g, ti, ti.m0 + ar))
-                                  : static_cast<uint32_t>(ti.row_base + ti.m0 + ar);
-      const bool ok = ar0 < c.rows;
-      c.a_voff[i] = ok ? row * (2u * K) + 16u * (c.tid & 7) : 0xFFFFFF00u;
-      c.a_valid |= (ok ? 1u : 0u) << i;
-    }
-    if (GATEUP) {   // weight rows: tile 2j = gate, tile 2j+1 = up of h block j
-      const int h = min(ns * (PN / 2) + (br >> 6) * 32 + (br & 31), f - 1);
-      const uint32_t b_row = 2u * h + ((br >> 5) & 1);
-      c.vb = 2u * b_row + bb;
-    } else {
-      const uint32_t b_row = min(ns * PN + br, d - 1);
-      c.vb = static_cast<uint32_t>(bb) * d + b_row;
-    }
-    uint16_t* hdst = nullptr;
-    float* odst = nullptr;
-    if (GATEUP) {
-      hdst = h_out + static_cast<int64_t>(ti.row_base + ti.m0) * f + ns * (PN / 2) + 32 * c.cq +
-             4 * (c.lane >> 5);
-    } else {
-      odst = (ti.group < g.E ? out_pairs + static_cast<int64_t>(ti.row_base + ti.m0) * d
-                             : out_shared + static_cast<int64_t>(ti.m0) * d) +
-             static_cast<int64_t>(ns) * PN + 64 * c.cq + 4 * (c.lane >> 5);
-    }
-    switch (2 * nt + rh) {   // uniform per wavefront
-      case 8: run_job<FMT, GATEUP, 4, 0>(c, P, d, f, lds, hdst, odst); break;
-      case 9: run_job<FMT, GATEUP, 4, 1>(c, P, d, f, lds, hdst, odst); break;
-      case 6: run_job<FMT, GATEUP, 3, 0>(c, P, d, f, lds, hdst, odst); break;
-      case 7: run_job<FMT, GATEUP, 3, 1>(c, P, d, f, lds, hdst, odst); break;
-      case 4: run_job<FMT, GATEUP, 2, 0>(c, P, d, f, lds, hdst, odst); break;
-      case 5: run_job<FMT, GATEUP, 2, 1>(c, P, d, f, lds, hdst, odst); break;
-      case 2: run_job<FMT, GATEUP, 1, 0>(c, P, d, f, lds, hdst, odst); break;
-      case 3: run_job<FMT, GATEUP, 1, 1>(c, P, d, f, lds, hdst, odst); break;
-      case 0: run_job<FMT, GATEUP, 0, 0>(c, P, d, f, lds, hdst, odst); break;
-      default: run_job<FMT, GATEUP, 0, 1>(c, P, d, f, lds, hdst, odst); break;
+      for (int i = 0; i < 8; ++i) {
+        const int ar0 = 32 * i + (c.p >> 3);
+        const int ar = min(ar0, ti.rows - 1);
+        const uint32_t row = GATEUP ? static_cast<uint32_t>(tile_token(g, ti, ti.m0 + ar))
+                                    : static_cast<uint32_t>(ti.row_base + ti.m0 + ar);
+        const bool ok = ar0 < ti.rows;
+        c.a_voff[i] = ok ? row * (2u * K) + 16u * (c.p & 7) : 0xFFFFFF00u;
+        c.a_valid |= (ok ? 1u : 0u) << i;
+      }
+      if (GATEUP) {   // weight rows: tile 2j = gate, tile 2j+1 = up of h block j
+        const int h = min(ns * (PN / 2) + (c.p >> 6) * 32 + (c.p & 31), f - 1);
+        const uint32_t b_row = 2u * h + ((c.p >> 5) & 1);
+        c.vb[0] = 2u * b_row;
+        c.vb[1] = 2u * b_row + 1u;
+      } else {
+        const uint32_t b_row = min(ns * PN + c.p, d - 1);
+        c.vb[0] = b_row;
+        c.vb[1] = static_cast<uint32_t>(d) + b_row;
+      }
+      produce_job<FMT, GATEUP>(c, P, d, f, lds);
     }
   }
 }
