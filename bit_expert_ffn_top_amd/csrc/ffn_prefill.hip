@@ -37,13 +37,20 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // native 16-byte 
 constexpr int PM = 256;                  // rows: 8 MFMA tiles of 32 tokens
 constexpr int PN = 256;                  // output columns: 8 MFMA tiles of 32
 constexpr int PK = 64;                   // reduction step
-constexpr int PS = PK + 8;               // LDS row stride in bf16 (padding against bank conflicts)
 constexpr int NCONS = 512;               // 8 MFMA wavefronts, two per SIMD
 constexpr int NPROD = 256;               // 4 loading / dequantizing wavefronts, one per SIMD
 constexpr int PTHREADS = NCONS + NPROD;
-constexpr int TILE_ELEMS = PM * PS;      // one LDS tile
-constexpr size_t PREFILL_LDS = 4 * TILE_ELEMS * sizeof(__bf16);   // A and B, double-buffered
-static_assert(PM == PN, "A and B tiles share one shape");
+// LDS: three A tiles (token rows) and two B tiles (dequantized weight rows),
+// 128 bytes per row (half of the 64 banks) with the 16-byte piece c of row r
+// at position c ^ swz(r), swz(r) = (r % 8) ^ (r/8 % 2): the 16 consecutive rows
+// that a 16-byte-per-lane LDS access serves together then fall in 16
+// distinct groups of 4 banks.  160 KB: all of a CU's LDS.
+constexpr int A_TILE = PM * PK;          // bf16 elements
+constexpr int B_TILE = PN * PK;
+constexpr int A_BUFS = 3;
+constexpr size_t PREFILL_LDS = (A_BUFS * A_TILE + 2 * B_TILE) * sizeof(__bf16);
+
+__host__ __device__ constexpr int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 struct GroupInfo {
   const int32_t* offsets;    // [E+1]
@@ -126,8 +133,6 @@ __device__ __forceinline__ BlockRaw load_block(const uint8_t* base, int64_t oc, 
   return r;
 }
 
-// The block's 32 weights (dequant_one, rounded to bf16 nearest even) as 64
-// bytes at dst.
 // 16 codes of one 32-bit word (2-bit formats) as weights m + s*q: each code is
 // read as an fp16 value c_j + q in place (the extraction of the decode path,
 // c_j = q2_offset(j)), and w = s*(c_j + q) + (m - c_j*s) in one fused
@@ -152,8 +157,12 @@ __device__ __forceinline__ void weights16_q2(uint32_t w, float s, float m, float
   }
 }
 
+// The block's 32 weights (dequant_one, rounded to bf16 nearest even) as four
+// 16-byte pieces piece0 .. piece0+3 of a 128-byte LDS row, piece c stored at
+// position c ^ key.
 template <int FMT>
-__device__ __forceinline__ void store_block_bf16(const BlockRaw& r, __bf16* dst) {
+__device__ __forceinline__ void store_block_bf16(const BlockRaw& r, __bf16* row, int piece0,
+                                                 int key) {
   const float s = half_bits_to_float(r.scale);
   const float m = half_bits_to_float(r.min);
   uint32_t packed[16];
@@ -167,10 +176,11 @@ __device__ __forceinline__ void store_block_bf16(const BlockRaw& r, __bf16* dst)
 #pragma unroll
       for (int j = 0; j < 16; j += 2) packed[8 * h + j / 2] = pack_bf16x2(wv[j], wv[j + 1]);
     }
-    u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+    u32x4* d4 = reinterpret_cast<u32x4*>(row);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      d4[q] = u32x4{packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]};
+      d4[(piece0 + q) ^ key] =
+          u32x4{packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]};
     return;
   }
 #pragma unroll
@@ -185,10 +195,11 @@ __device__ __forceinline__ void store_block_bf16(const BlockRaw& r, __bf16* dst)
     }
     packed[j >> 1] = pack_bf16x2(dequant_one<FMT>(q0, s, m), dequant_one<FMT>(q1, s, m));
   }
-  u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+  u32x4* d4 = reinterpret_cast<u32x4*>(row);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    d4[q] = u32x4{packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]};
+    d4[(piece0 + q) ^ key] =
+        u32x4{packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]};
 }
 
 // Buffer resource over `bytes` bytes at base (raw, unswizzled; gfx9 word 3).
@@ -224,67 +235,106 @@ __device__ __forceinline__ BlockRaw load_b(BufRsrc rs, const Planes& P, uint32_t
   return r;
 }
 
-// Producer side.  The 256 producer threads (index p) load one step: A rows
-// 32*i + p/8 (i = 0..7), 16-byte piece p%8 of each (eight consecutive lanes
-// read one 128-byte row piece), and both weight blocks of tile row p.
-struct StepRegs {
-  u32x4 a[8];
-  BlockRaw b[2];
-};
-
+// Producer side.  The 256 producer threads (index p, wavefront pw = p/64,
+// lane l) move the token rows of a step straight from memory into an A tile:
+// eight 1 KB loads per wavefront that write LDS directly, lane l's 16 bytes
+// at 16*l, so load j covers tile rows 64pw + 8j .. +7 and lane l reads piece
+// (l%8) ^ swz(r) of row r = 64pw + 8j + l/8 from memory (a row past the
+// group's end has an offset outside the buffer, which loads zero).  They also load
+// both weight blocks of tile row p and dequantize them into the B tile.
 struct ProdCtx {
   BufRsrc a_rs;              // the A rows (x or H)
   BufRsrc b_rs;              // the expert's slot
-  uint32_t a_voff[8];        // byte offsets of this thread's 8 A row pieces
-  uint32_t a_valid;          // bit i: A row i of this thread is inside the group
+  uint32_t a_voff[8];        // byte offsets of this lane's 8 row pieces
   uint32_t vb[2];            // this thread's two blocks within a step's blocks
   int p, nK;
 };
 
-template <int FMT, bool GATEUP>
-__device__ __forceinline__ void load_step(StepRegs& r, const ProdCtx& c, const Planes& P, int ks,
-                                          int d, int f) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(c.a_rs, c.a_voff[i], ks * (PK * 2), 0);
-#pragma unroll
-  for (int bb = 0; bb < 2; ++bb) r.b[bb] = load_b<FMT, GATEUP>(c.b_rs, P, c.vb[bb], ks, d, f);
-}
-
-// Rows past the group's end (bit i of valid clear) are neither loaded nor
-// stored: their LDS rows keep stale values that only reach output rows that
-// are never written.
 template <int FMT>
-__device__ __forceinline__ void store_step(const StepRegs& r, __bf16* As, __bf16* Bs,
-                                           const ProdCtx& c) {
-  const int ar = c.p >> 3, ch = c.p & 7;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if ((c.a_valid >> i) & 1u)
-      *reinterpret_cast<u32x4*>(As + (32 * i + ar) * PS + 8 * ch) = r.a[i];
-#pragma unroll
-  for (int bb = 0; bb < 2; ++bb) store_block_bf16<FMT>(r.b[bb], Bs + c.p * PS + 32 * bb);
+constexpr int block_loads() {   // memory instructions per block
+  return 2 + (FMT == MOE_FMT_Q2SM ? 1 : 0) + (FMT == MOE_FMT_Q3G ? 1 : 0);
 }
 
-// The producers' part of a job.  The LDS holds two steps: while the MFMA
-// wavefronts multiply step ks from one buffer, step ks+1 (loaded one step
-// earlier) is written to the other and step ks+2 is requested; one barrier
-// per step.  The last store of a job is a repeat that nobody reads; it keeps
-// the loads unconditional.
+__device__ __forceinline__ void load_a_lds(const ProdCtx& c, __bf16* abuf, int ks) {
+  const int pw = c.p >> 6;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        c.a_rs, (__attribute__((address_space(3))) void*)(abuf + (64 * pw + 8 * j) * PK), 16,
+        c.a_voff[j], ks * (PK * 2), 0, 0);
+}
+
+template <int FMT, bool GATEUP>
+__device__ __forceinline__ void load_step(BlockRaw (&r)[2], const ProdCtx& c, const Planes& P,
+                                          int ks, int d, int f) {
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) r[bb] = load_b<FMT, GATEUP>(c.b_rs, P, c.vb[bb], ks, d, f);
+}
+
+template <int FMT>
+__device__ __forceinline__ void store_step(const BlockRaw (&r)[2], __bf16* Bs, const ProdCtx& c) {
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) store_block_bf16<FMT>(r[bb], Bs + c.p * PK, 4 * bb, swz(c.p));
+}
+
+// Wait until at most N memory instructions of this wavefront are in flight
+// (they complete in order).  s_waitcnt fields: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4 (7: no wait), lgkmcnt 11:8 (15: no wait).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// One producer step ks: the token rows of step ks+2 are requested into the A
+// buffer that step ks-1 used, the weight blocks of step ks+3 into `load`, the
+// blocks of step ks+1 (`use`, requested two steps earlier) are dequantized
+// into the free B buffer, and the rows of step ks+1 (requested one step
+// earlier) are waited for before the barrier.  Weight loads past the last
+// step repeat it (unconditional loads); the last stores of a job are repeats
+// that nobody reads.
+template <int FMT, bool GATEUP>
+__device__ __forceinline__ void produce_step(const ProdCtx& c, const Planes& P, int d, int f,
+                                             __bf16* abuf, __bf16* bbuf, int ks,
+                                             const BlockRaw (&use)[2], BlockRaw (&load)[2]) {
+  constexpr int NB = 2 * block_loads<FMT>();
+  const bool more = ks + 2 < c.nK;
+  if (more) load_a_lds(c, abuf + ((ks + 2) % A_BUFS) * A_TILE, ks + 2);
+  store_step<FMT>(use, bbuf + ((ks + 1) & 1) * B_TILE, c);
+  load_step<FMT, GATEUP>(load, c, P, min(ks + 3, c.nK - 1), d, f);
+  // newer than the rows of step ks+1: the blocks of steps ks+2 and ks+3 and
+  // the rows of step ks+2
+  if (more)
+    wait_vm<2 * NB + 8>();
+  else
+    wait_vm<2 * NB>();
+  __syncthreads();
+}
+
 template <int FMT, bool GATEUP>
 __device__ __forceinline__ void produce_job(const ProdCtx& c, const Planes& P, int d, int f,
-                                            __bf16* lds) {
-  StepRegs R;
-  load_step<FMT, GATEUP>(R, c, P, 0, d, f);
-  store_step<FMT>(R, lds, lds + TILE_ELEMS, c);
-  load_step<FMT, GATEUP>(R, c, P, min(1, c.nK - 1), d, f);
+                                            __bf16* abuf, __bf16* bbuf) {
+  constexpr int NB = 2 * block_loads<FMT>();
+  BlockRaw R0[2], R1[2];
+  load_a_lds(c, abuf, 0);
+  load_step<FMT, GATEUP>(R0, c, P, 0, d, f);
+  if (c.nK > 1) load_a_lds(c, abuf + A_TILE, 1);
+  store_step<FMT>(R0, bbuf, c);
+  load_step<FMT, GATEUP>(R0, c, P, min(1, c.nK - 1), d, f);
+  load_step<FMT, GATEUP>(R1, c, P, min(2, c.nK - 1), d, f);
+  // newer than the rows of step 0: the rows of step 1 and the blocks of
+  // steps 0, 1, 2 (those of step 0 are done)
+  if (c.nK > 1)
+    wait_vm<3 * NB + 8>();
+  else
+    wait_vm<3 * NB>();
   __syncthreads();
-  for (int ks = 0; ks < c.nK; ++ks) {
-    __bf16* nxt = lds + ((ks + 1) & 1) * (2 * TILE_ELEMS);
-    store_step<FMT>(R, nxt, nxt + TILE_ELEMS, c);
-    load_step<FMT, GATEUP>(R, c, P, min(ks + 2, c.nK - 1), d, f);
-    __syncthreads();
+  int ks = 0;
+  for (; ks + 1 < c.nK; ks += 2) {
+    produce_step<FMT, GATEUP>(c, P, d, f, abuf, bbuf, ks, R0, R0);
+    produce_step<FMT, GATEUP>(c, P, d, f, abuf, bbuf, ks + 1, R1, R1);
   }
+  if (ks < c.nK) produce_step<FMT, GATEUP>(c, P, d, f, abuf, bbuf, ks, R0, R0);
 }
 
 // MFMAs of one step for a wavefront holding token tiles rh + 2i, i < NT, and
@@ -298,29 +348,68 @@ struct Frags {
   bf16x8 x[NT > 0 ? NT : 1];
 };
 
-template <int NT>
-__device__ __forceinline__ void read_frags(Frags<NT>& fr, const __bf16* a0, const __bf16* b0,
-                                           int kk) {
-  fr.w[0] = *reinterpret_cast<const bf16x8*>(b0 + 16 * kk);
-  fr.w[1] = *reinterpret_cast<const bf16x8*>(b0 + 32 * PS + 16 * kk);
-#pragma unroll
-  for (int i = 0; i < NT; ++i) fr.x[i] = *reinterpret_cast<const bf16x8*>(a0 + 64 * i * PS + 16 * kk);
-}
-
+// A fragment of row r (r % 16 = lane % 16 for every tile of a lane, in A and
+// in B) at 16-byte piece 2kk + lane/32 sits at byte r*128 + 16*((2kk + lane/32) ^ swz(lane)).
 template <int NT>
 __device__ __forceinline__ void mfma_step(f32x16 (&acc)[NT > 0 ? NT : 1][2], const __bf16* As,
                                           const __bf16* Bs, int lane, int rh, int cq) {
-  const __bf16* a0 = As + (32 * rh + (lane & 31)) * PS + 8 * (lane >> 5);
-  const __bf16* b0 = Bs + (64 * cq + (lane & 31)) * PS + 8 * (lane >> 5);
+  const char* a0 = reinterpret_cast<const char*>(As) + (32 * rh + (lane & 31)) * (PK * 2);
+  const char* b0 = reinterpret_cast<const char*>(Bs) + (64 * cq + (lane & 31)) * (PK * 2);
+  const int h = lane >> 5, l7 = swz(lane & 15);
+  if (NT == 4) {   // no registers to spare: fragments read per sub-step
+#pragma unroll
+    for (int kk = 0; kk < PK / 16; ++kk) {
+      const int pc = 16 * ((2 * kk + h) ^ l7);
+      Frags<NT> c;
+      c.w[0] = *reinterpret_cast<const bf16x8*>(b0 + pc);
+      c.w[1] = *reinterpret_cast<const bf16x8*>(b0 + 32 * (PK * 2) + pc);
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+        c.x[i] = *reinterpret_cast<const bf16x8*>(a0 + 64 * i * (PK * 2) + pc);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.w[0], c.x[i], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.w[1], c.x[i], acc[i][1], 0, 0, 0);
+      }
+    }
+    return;
+  }
+  // Fragments roll through one register set: in sub-step kk the MFMAs with
+  // weight fragment 0 go first, after which it is refilled with sub-step
+  // kk+1; then those with weight fragment 1, each followed by the refill of
+  // its token fragment, and last weight fragment 1.  Every read has the
+  // MFMAs of the other tiles to arrive.
+  Frags<NT> c;
+  c.w[0] = *reinterpret_cast<const bf16x8*>(b0 + 16 * (h ^ l7));
+  c.w[1] = *reinterpret_cast<const bf16x8*>(b0 + 32 * (PK * 2) + 16 * (h ^ l7));
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+    c.x[i] = *reinterpret_cast<const bf16x8*>(a0 + 64 * i * (PK * 2) + 16 * (h ^ l7));
 #pragma unroll
   for (int kk = 0; kk < PK / 16; ++kk) {
-    Frags<NT> c;
-    read_frags<NT>(c, a0, b0, kk);
+    const bool next = kk + 1 < PK / 16;
+    const int pn = 16 * ((2 * kk + 2 + h) ^ l7);   // piece of sub-step kk+1
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.w[0], c.x[i], acc[i][0], 0, 0, 0);
+    if (next) c.w[0] = *reinterpret_cast<const bf16x8*>(b0 + pn);
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.w[0], c.x[i], acc[i][0], 0, 0, 0);
       acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.w[1], c.x[i], acc[i][1], 0, 0, 0);
+      if (next) c.x[i] = *reinterpret_cast<const bf16x8*>(a0 + 64 * i * (PK * 2) + pn);
     }
+    if (next) c.w[1] = *reinterpret_cast<const bf16x8*>(b0 + 32 * (PK * 2) + pn);
+    if (next) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);   // MFMAs with weight 0
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // weight 0 refill
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // weight 1 refill
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -329,6 +418,8 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[NT > 0 ? NT : 1][2], con
 template <bool GATEUP, int NT, int RH>
 __device__ __forceinline__ void consume_job(int nK, int lane, int cq, int rows, int d, int f,
                                             const __bf16* lds, uint16_t* hdst, float* odst) {
+  const __bf16* abuf = lds;
+  const __bf16* bbuf = lds + A_BUFS * A_TILE;
   f32x16 acc[NT > 0 ? NT : 1][2];
 #pragma unroll
   for (int i = 0; i < NT; ++i)
@@ -336,10 +427,10 @@ __device__ __forceinline__ void consume_job(int nK, int lane, int cq, int rows, 
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  __syncthreads();   // step 0 is in buffer 0
+  __syncthreads();   // step 0 is in buffers 0
   for (int ks = 0; ks < nK; ++ks) {
-    const __bf16* cur = lds + (ks & 1) * (2 * TILE_ELEMS);
-    if (NT > 0) mfma_step<NT>(acc, cur, cur + TILE_ELEMS, lane, RH, cq);
+    if (NT > 0)
+      mfma_step<NT>(acc, abuf + (ks % A_BUFS) * A_TILE, bbuf + (ks & 1) * B_TILE, lane, RH, cq);
     __syncthreads();
   }
   if (NT == 0) return;
@@ -447,6 +538,7 @@ __global__ __launch_bounds__(PTHREADS) void prefill_gemm_kernel(
     // x is [T][d]; H is [T*k + T][f] (the host keeps it under 4 GiB)
     c.a_rs = buf_rsrc(a_src, GATEUP ? static_cast<uint32_t>(g.T) * d * 2
                                     : static_cast<uint32_t>(g.T * (g.k + 1)) * f * 2);
+    const int lane = c.p & 63, pw = c.p >> 6;
     for (int job = blockIdx.x; job < total; job += gridDim.x) {
       const int q = job >> 3;
       const int ns = q % n_slices;
@@ -456,19 +548,14 @@ __global__ __launch_bounds__(PTHREADS) void prefill_gemm_kernel(
       if (ti.slot < 0) continue;
       c.b_rs = buf_rsrc(pool + static_cast<int64_t>(ti.slot) * slot_bytes,
                         static_cast<uint32_t>(slot_bytes));
-      // the 8 A rows of this thread (a row past the group's end gets an
-      // offset outside the buffer: its loads return zero without a memory
-      // access)
-      c.a_valid = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ar0 = 32 * i + (c.p >> 3);
+      for (int j = 0; j < 8; ++j) {
+        const int ar0 = 64 * pw + 8 * j + (lane >> 3);
         const int ar = min(ar0, ti.rows - 1);
         const uint32_t row = GATEUP ? static_cast<uint32_t>(tile_token(g, ti, ti.m0 + ar))
                                     : static_cast<uint32_t>(ti.row_base + ti.m0 + ar);
-        const bool ok = ar0 < ti.rows;
-        c.a_voff[i] = ok ? row * (2u * K) + 16u * (c.p & 7) : 0xFFFFFF00u;
-        c.a_valid |= (ok ? 1u : 0u) << i;
+        c.a_voff[j] = ar0 < ti.rows ? row * (2u * K) + 16u * ((lane & 7) ^ swz(ar0 & 15))
+                                    : 0xFFFFFF00u;
       }
       if (GATEUP) {   // weight rows: tile 2j = gate, tile 2j+1 = up of h block j
         const int h = min(ns * (PN / 2) + (c.p >> 6) * 32 + (c.p & 31), f - 1);
@@ -480,7 +567,7 @@ __global__ __launch_bounds__(PTHREADS) void prefill_gemm_kernel(
         c.vb[0] = b_row;
         c.vb[1] = static_cast<uint32_t>(d) + b_row;
       }
-      produce_job<FMT, GATEUP>(c, P, d, f, lds);
+      produce_job<FMT, GATEUP>(c, P, d, f, lds, lds + A_BUFS * A_TILE);
     }
   }
 }
