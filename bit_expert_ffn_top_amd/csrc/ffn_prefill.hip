@@ -135,10 +135,11 @@ __device__ __forceinline__ BlockRaw load_block(const uint8_t* base, int64_t oc, 
 
 // 16 codes of one 32-bit word (2-bit formats) as weights m + s*q: each code is
 // read as an fp16 value c_j + q in place (the extraction of the decode path,
-// c_j = q2_offset(j)), and w = s*(c_j + q) + (m - c_j*s) in one fused
-// multiply-add.  m - c_j*s is exact unless 0 < |m| < s/128, so w is then the
-// correctly rounded m + s*q, as the plain formula gives.
+// c_j = q2_offset(j)), two codes per register; one packed fp16 subtraction
+// leaves q exactly, and w = fma(s, q, m) is the correctly rounded value the
+// plain formula gives (about 2.6 vector instructions per weight instead of 3.5).
 __device__ __forceinline__ void weights16_q2(uint32_t w, float s, float m, float (&out)[16]) {
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
   const uint32_t b = w >> 6, c = w << 6;
   const uint32_t rr[8] = {
       and_or(c, 0x00C000C0u, 0x4C004C00u),   // 16+q0  | 16+q8
@@ -151,9 +152,10 @@ __device__ __forceinline__ void weights16_q2(uint32_t w, float s, float m, float
       and_or(b, 0x03000300u, 0x44004400u)};  // 4+q7   | 4+q15
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float mj = fmaf(-q2_offset(j), s, m);
-    out[j] = fmaf(s, h_lo(rr[j]), mj);
-    out[j + 8] = fmaf(s, h_hi(rr[j]), mj);
+    const _Float16 cj = static_cast<_Float16>(q2_offset(j));
+    const half2_t q = __builtin_bit_cast(half2_t, rr[j]) - half2_t{cj, cj};
+    out[j] = fmaf(s, static_cast<float>(q.x), m);
+    out[j + 8] = fmaf(s, static_cast<float>(q.y), m);
   }
 }
 
@@ -166,9 +168,9 @@ __device__ __forceinline__ void store_block_bf16(const BlockRaw& r, __bf16* row,
   const float s = half_bits_to_float(r.scale);
   const float m = half_bits_to_float(r.min);
   uint32_t packed[16];
+  // Q2S: s*(q - 1.5) = s*q + (-1.5 s), -1.5 s exact
+  const float m0 = FMT == MOE_FMT_Q2SM ? m : -1.5f * s;
   if (FMT != MOE_FMT_Q3G) {
-    // Q2S: s*(q - 1.5) = s*q + (-1.5 s), -1.5 s exact
-    const float m0 = FMT == MOE_FMT_Q2SM ? m : -1.5f * s;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float wv[16];

@@ -76,6 +76,44 @@ def test_prefill_small(name, shape, fmt, T):
     check_close(y.numpy(), ry, xd)
 
 
+def test_prefill_q2sm_tiny_min():
+    """Q2SM blocks whose min is tiny next to the scale (|m| = s/2048), on
+    every other block, beside ordinary ones: a dequantization that folded
+    the min into an offset (m - c*s) would round there; the GEMMs must still
+    match the oracle."""
+    dev = need_gpu()
+    shape = synth.LayerShape(64, 4, 256, 128, True)
+    fmt = synth.FMT_Q2SM
+    L = GpuLayer(4, 3, shape, fmt, dev)
+    lay = synth.slot_layout(fmt, shape.d_model, shape.d_ff)
+    host = L.pool.cpu().numpy()
+    for mat in ("G", "D"):
+        s_off, s_len = lay[(mat, "scale")]
+        m_off, m_len = lay[(mat, "min")]
+        scale = host[:, s_off:s_off + s_len].copy().view(np.float16).astype(np.float32)
+        mins = host[:, m_off:m_off + m_len].copy().view(np.float16)
+        tiny = (scale * np.float32(2.0 ** -11)).astype(np.float16)
+        sign = np.where(np.arange(mins.shape[1]) % 4 == 0, -1, 1).astype(np.float16)
+        mins[:, ::2] = tiny[:, ::2] * sign[::2]
+        host[:, m_off:m_off + m_len] = mins.view(np.uint8)
+    L.pool.copy_(torch.from_numpy(host).to(dev))
+    L._bytes = {s_: host[s_] for s_ in L._bytes}
+    L._w = {}
+    T = 96
+    x = synth.make_x(4, 3, T, shape.d_model, dtype=torch.bfloat16)
+    logits = synth.make_logits(4, 3, T, shape.n_experts, 1.5)
+    out_pairs, pair_pos, offs, out_sh, y, idx, slot, w = _prefill(L, x, logits, shape.top_k, dev)
+    ridx, rw = oracle.route_topk(logits.numpy(), shape.top_k)
+    np.testing.assert_array_equal(idx, ridx)
+    xd = x.double().numpy()
+    ro, rsh, ry = oracle.prefill_layer(xd, ridx, rw, L.weights_of_expert,
+                                       L.weights_of_slot(L.shared_slot), shape.n_experts)
+    n = int(offs[-1])
+    check_close(out_pairs.numpy()[:n], ro[:n], what="out_pairs")
+    check_close(out_sh.numpy(), rsh, what="out_shared")
+    check_close(y.numpy(), ry, xd)
+
+
 def test_prefill_with_misses():
     dev = need_gpu()
     shape = synth.LayerShape(64, 4, 256, 128, True)
