@@ -1,7 +1,8 @@
 // Routing-weighted combine into the residual:
 //   y[t] = x[t] + sum_i w[t,i] * rows[pair_pos[t,i]] + shared[t]
 // One thread per 4 consecutive columns of one token; the k terms are added in
-// i order with fused multiply-adds, the shared row last.
+// i order with fused multiply-adds, the shared row last.  A missed pair
+// (pair_pos < 0) contributes nothing.
 #include "moe_internal.h"
 
 namespace bitffn {
@@ -31,15 +32,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ x
     acc = *reinterpret_cast<const float4*>(static_cast<const float*>(x) +
                                            static_cast<int64_t>(t) * d + c);
   }
-  for (int i = 0; i < k; ++i) {
-    const int p = pair_pos[static_cast<int64_t>(t) * k + i];
-    if (p < 0) continue;
-    const float wi = w[static_cast<int64_t>(t) * k + i];
-    const float4 r = *reinterpret_cast<const float4*>(rows + static_cast<int64_t>(p) * d + c);
-    acc.x = fmaf(wi, r.x, acc.x);
-    acc.y = fmaf(wi, r.y, acc.y);
-    acc.z = fmaf(wi, r.z, acc.z);
-    acc.w = fmaf(wi, r.w, acc.w);
+  // the k terms in batches of KC: all pair positions and weights of a batch,
+  // then all its row loads (a missed pair re-reads a row of the batch that is
+  // present, so that every load is unconditional and in bounds, and is
+  // skipped), then the fused multiply-adds in i order
+  constexpr int KC = 16;
+  for (int i0 = 0; i0 < k; i0 += KC) {
+    int p[KC];
+    float wi[KC];
+    float4 r[KC];
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const bool in = i0 + j < k;
+      const int64_t q = static_cast<int64_t>(t) * k + min(i0 + j, k - 1);
+      p[j] = in ? pair_pos[q] : -1;
+      wi[j] = w[q];
+    }
+    int any = -1;
+#pragma unroll
+    for (int j = KC - 1; j >= 0; --j) any = p[j] >= 0 ? p[j] : any;
+    if (any < 0) continue;   // the token's whole batch missed (uniform per wavefront)
+#pragma unroll
+    for (int j = 0; j < KC; ++j)
+      r[j] = *reinterpret_cast<const float4*>(rows + static_cast<int64_t>(p[j] >= 0 ? p[j] : any) * d + c);
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      if (p[j] >= 0) {
+        acc.x = fmaf(wi[j], r[j].x, acc.x);
+        acc.y = fmaf(wi[j], r[j].y, acc.y);
+        acc.z = fmaf(wi[j], r[j].z, acc.z);
+        acc.w = fmaf(wi[j], r[j].w, acc.w);
+      }
+    }
   }
   if (shared) {
     const float4 r = *reinterpret_cast<const float4*>(shared + static_cast<int64_t>(t) * d + c);
