@@ -1,31 +1,54 @@
-// Router top-k: one workgroup per token, one wavefront per group of 64
-// experts; the two-level rank selection and the softmax over the k chosen
-// logits are the shared routing building blocks (also used by the fused
-// decode layer, so both give identical bits).
+// Router top-k, one wavefront per token: lane l holds the keys of experts
+// 64j + l (the 64-bit keys of the shared routing building blocks: value desc,
+// index asc, -0 as +0, NaN as -inf; all distinct), and k rounds each take the
+// wavefront's largest remaining key, so choice r is the key of rank r, as the
+// two-level rank selection of the fused decode layer finds it.  The softmax
+// over the k chosen logits is the shared one, so both give identical bits.
 #include "moe_internal.h"
 #include "route_device.h"
 
 namespace bitffn {
 namespace {
 
-constexpr int kMaxGroups = MOE_MAX_EXPERTS / 64;
+constexpr int kTokensPerBlock = 4;   // one wavefront each
 
-__global__ __launch_bounds__(kMaxGroups * 64) void route_topk_kernel(
-    const float* __restrict__ logits, int E, int k, int32_t* __restrict__ idx,
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int M>   // keys per lane: E <= 64 * M
+__global__ __launch_bounds__(64 * kTokensPerBlock) void route_topk_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ idx,
     float* __restrict__ w) {
-  __shared__ uint64_t grp[kMaxGroups * 64];
-  __shared__ uint64_t cand[kMaxGroups * MOE_MAX_TOPK];
-  __shared__ uint64_t top[MOE_MAX_TOPK];
-  const int64_t t = blockIdx.x;
-  block_topk<1>(logits + t * E, 1, E, k, TopkLds{grp, cand, top});
-  if (threadIdx.x < 64) {
-    int id;
-    float wt;
-    topk_softmax_lane(top, k, threadIdx.x, id, wt);
-    if (static_cast<int>(threadIdx.x) < k) {
-      idx[t * k + threadIdx.x] = id;
-      w[t * k + threadIdx.x] = wt;
-    }
+  __shared__ uint64_t top[kTokensPerBlock][MOE_MAX_TOPK];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + wave;
+  if (t >= T) return;   // uniform per wavefront; no barrier follows
+  const float* lg = logits + t * E;
+  uint64_t key[M];
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const int e = 64 * j + lane;
+    key[j] = route_key(lg[min(e, E - 1)], e, e < E);
+  }
+  uint64_t mine = 0;   // lane r < k: the key of rank r
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int j = 1; j < M; ++j) best = max_u64(best, key[j]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) best = max_u64(best, __shfl_xor(best, off, 64));
+    if (lane == r) mine = best;
+#pragma unroll
+    for (int j = 0; j < M; ++j) key[j] = key[j] == best ? 0 : key[j];   // keys are never 0
+  }
+  top[wave][lane] = mine;
+  __builtin_amdgcn_wave_barrier();
+  int id;
+  float wt;
+  topk_softmax_lane(top[wave], k, lane, id, wt);
+  if (lane < k) {
+    idx[t * k + lane] = id;
+    w[t * k + lane] = wt;
   }
 }
 
@@ -34,8 +57,17 @@ __global__ __launch_bounds__(kMaxGroups * 64) void route_topk_kernel(
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx,
                              float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int groups = (E + 63) / 64;   // <= kMaxGroups: every group has its wavefront
-  route_topk_kernel<<<T, groups * 64, 0, s>>>(logits, E, k, idx, w);
+  const int blocks = (T + kTokensPerBlock - 1) / kTokensPerBlock;
+  const int threads = 64 * kTokensPerBlock;
+  const int m = (E + 63) / 64;   // E <= MOE_MAX_EXPERTS = 1024: m <= 16
+  if (m <= 2)
+    route_topk_kernel<2><<<blocks, threads, 0, s>>>(logits, T, E, k, idx, w);
+  else if (m <= 4)
+    route_topk_kernel<4><<<blocks, threads, 0, s>>>(logits, T, E, k, idx, w);
+  else if (m <= 8)
+    route_topk_kernel<8><<<blocks, threads, 0, s>>>(logits, T, E, k, idx, w);
+  else
+    route_topk_kernel<16><<<blocks, threads, 0, s>>>(logits, T, E, k, idx, w);
   return hipGetLastError();
 }
 
