@@ -108,7 +108,7 @@ int moe_cache_lookup(const int32_t* idx, int T, int k, const int32_t* slot_of_ex
   const bitffn::GroupWorkspace gws = bitffn::group_workspace(ws, T, E);
   return hip_status(bitffn::launch_group_pairs(idx, slot, nullptr, T, k, E, false, gws, nullptr,
                                                miss_pair, nullptr, miss_expert, n_miss, nullptr,
-                                               0, stream));
+                                               0, nullptr, nullptr, stream));
 }
 
 size_t moe_decode_workspace_bytes(const moe_layer* L, int T) {

@@ -151,7 +151,8 @@ __global__ __launch_bounds__(kScanThreads) void group_scan_chunks_kernel(
 __global__ __launch_bounds__(1024) void group_scan_kernel(
     int E, int T, const int32_t* __restrict__ totals, int32_t* __restrict__ starts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ distinct,
-    int32_t* __restrict__ counts_out, int32_t* __restrict__ tile_base, int tile_m) {
+    int32_t* __restrict__ counts_out, int32_t* __restrict__ tile_base, int tile_m,
+    int32_t* __restrict__ tile_group) {
   __shared__ int32_t s_tot[kMaxE];
   __shared__ int32_t s_nz[kMaxE];
   __shared__ int32_t s_tiles[kMaxE];
@@ -183,7 +184,13 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(
     starts[e] = start;
     if (offsets) offsets[e] = start;
     if (distinct && tot > 0) distinct[s_nz[e] - 1] = e;
-    if (tile_base) tile_base[e] = s_tiles[e] - (tot + tile_m - 1) / tile_m;
+    if (tile_base) {
+      const int nt = (tot + tile_m - 1) / tile_m;
+      const int tb = s_tiles[e] - nt;
+      tile_base[e] = tb;
+      if (tile_group)
+        for (int i = 0; i < nt; ++i) tile_group[tb + i] = e;
+    }
   }
   if (e == 0) {
     const int total = s_tot[E - 1];
@@ -194,8 +201,11 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(
     }
     if (tile_base) {
       const int base = s_tiles[E - 1];
+      const int nt = (T + tile_m - 1) / tile_m;
       tile_base[E] = base;
-      tile_base[E + 1] = base + (T + tile_m - 1) / tile_m;
+      tile_base[E + 1] = base + nt;
+      if (tile_group)
+        for (int i = 0; i < nt; ++i) tile_group[base + i] = E;
     }
   }
 }
@@ -205,7 +215,7 @@ __global__ __launch_bounds__(64) void group_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ slot_of_pair,
     const int32_t* __restrict__ table, int T, int k, int E, bool select_hits,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ starts,
-    int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
+    int32_t* __restrict__ perm, int32_t* __restrict__ pos, int32_t* __restrict__ group_slot) {
   __shared__ int32_t cursor[kMaxE];
   const int chunk = blockIdx.x;
   const int lane = threadIdx.x;
@@ -225,6 +235,7 @@ __global__ __launch_bounds__(64) void group_scatter_kernel(
         if (selected(s, select_hits)) {
           at = atomicAdd(&cursor[e], 1);
           if (perm) perm[at] = p;
+          if (group_slot && at == starts[e]) group_slot[e] = s;   // the group's first pair
         }
         if (pos) pos[p] = at;
       }
@@ -280,16 +291,19 @@ hipError_t launch_group_pairs(const int32_t* idx, const int32_t* slot_of_pair,
                               const int32_t* table, int T, int k, int E, bool select_hits,
                               GroupWorkspace gws, int32_t* offsets, int32_t* perm,
                               int32_t* pos, int32_t* distinct, int32_t* counts_out,
-                              int32_t* tile_base, int tile_m, hipStream_t s) {
+                              int32_t* tile_base, int tile_m, int32_t* tile_group,
+                              int32_t* group_slot, hipStream_t s) {
   const int n_chunks = (T + kGroupChunkTokens - 1) / kGroupChunkTokens;
   group_count_kernel<<<n_chunks, 256, 0, s>>>(idx, slot_of_pair, table, T, k, E, select_hits,
                                               gws.chunk_counts);
   group_scan_chunks_kernel<<<E, kScanThreads, 0, s>>>(n_chunks, E, gws.chunk_counts,
                                                       gws.totals);
   group_scan_kernel<<<1, 1024, 0, s>>>(E, T, gws.totals, gws.totals + kMaxE, offsets, distinct,
-                                       counts_out, tile_base, tile_m > 0 ? tile_m : 1);
+                                       counts_out, tile_base, tile_m > 0 ? tile_m : 1,
+                                       tile_group);
   group_scatter_kernel<<<n_chunks, 64, 0, s>>>(idx, slot_of_pair, table, T, k, E, select_hits,
-                                               gws.chunk_counts, gws.totals + kMaxE, perm, pos);
+                                               gws.chunk_counts, gws.totals + kMaxE, perm, pos,
+                                               group_slot);
   return hipGetLastError();
 }
 

@@ -53,36 +53,30 @@ constexpr size_t PREFILL_LDS = (A_BUFS * A_TILE + 2 * B_TILE) * sizeof(__bf16);
 __host__ __device__ constexpr int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 struct GroupInfo {
-  const int32_t* offsets;    // [E+1]
-  const int32_t* perm;       // [T*k]
-  const int32_t* tile_base;  // [E+2]
-  const int32_t* slot;       // [T*k] slot of each pair
+  const int32_t* offsets;     // [E+1]
+  const int32_t* perm;        // [T*k]
+  const int32_t* tile_base;   // [E+2]
+  const int32_t* tile_group;  // [tiles]: the group of every tile
+  const int32_t* group_slot;  // [E]: the slot of every non-empty group
   int E, T, k, shared_slot;
 };
 
-// Group of flat m-tile index mt (binary search over tile_base), its row
-// count, first local row, slot, and the row offset of its rows in H / out.
+// Group of flat m-tile index mt, its row count, first local row, slot, and
+// the row offset of its rows in H / out: two levels of loads (the tile's
+// group, then that group's bounds and slot).
 struct TileInfo {
   int group, m0, rows, slot, row_base;
 };
 
 __device__ __forceinline__ TileInfo find_tile(const GroupInfo& g, int mt) {
-  int lo = 0, hi = g.E + 1;  // tile_base[lo] <= mt < tile_base[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (g.tile_base[mid] <= mt)
-      lo = mid;
-    else
-      hi = mid;
-  }
+  const int e = g.tile_group[mt];
   TileInfo ti;
-  ti.group = lo;
-  ti.m0 = (mt - g.tile_base[lo]) * PM;
-  if (lo < g.E) {
-    const int start = g.offsets[lo];
-    const int n = g.offsets[lo + 1] - start;
-    ti.rows = min(PM, n - ti.m0);
-    ti.slot = g.slot[g.perm[start]];
+  ti.group = e;
+  ti.m0 = (mt - g.tile_base[e]) * PM;
+  if (e < g.E) {
+    const int start = g.offsets[e];
+    ti.rows = min(PM, g.offsets[e + 1] - start - ti.m0);
+    ti.slot = g.group_slot[e];
     ti.row_base = start;
   } else {
     ti.rows = min(PM, g.T - ti.m0);
@@ -90,6 +84,19 @@ __device__ __forceinline__ TileInfo find_tile(const GroupInfo& g, int mt) {
     ti.row_base = g.T * g.k;
   }
   return ti;
+}
+
+// Job j of the job space: its column slice and tile; false for a padding job
+// or a group with nothing to run (the shared expert without a shared output).
+__device__ __forceinline__ bool fetch_job(const GroupInfo& g, int n_slices, int n_gm, int total,
+                                          int job, int& ns, TileInfo& ti) {
+  if (job >= total) return false;
+  const int q = job >> 3;
+  ns = q % n_slices;
+  const int gm = (q / n_slices) * 8 + (job & 7);
+  if (gm >= n_gm) return false;
+  ti = find_tile(g, gm);
+  return ti.slot >= 0;
 }
 
 // token of local row m of the tile's group (the load is unconditional, with a
@@ -498,12 +505,11 @@ __global__ __launch_bounds__(PTHREADS) void prefill_gemm_kernel(
     const int cq = wave & 3;                 // columns 64cq .. 64cq + 63
     const int rh = wave >> 2;                // token tiles rh, rh + 2, rh + 4, rh + 6
     for (int job = blockIdx.x; job < total; job += gridDim.x) {
-      const int q = job >> 3;
-      const int ns = q % n_slices;
-      const int gm = (q / n_slices) * 8 + (job & 7);
-      if (gm >= n_gm) continue;              // uniform: a padding job
-      const TileInfo ti = find_tile(g, gm);
-      if (ti.slot < 0) continue;             // the shared group when no shared output is wanted
+      // (the MFMA wavefronts' own lookup is hidden behind the producers'
+      // first loads of the job)
+      int ns = 0;
+      TileInfo ti;
+      if (!fetch_job(g, n_slices, n_gm, total, job, ns, ti)) continue;   // uniform
       const int rows = ti.rows;
       const int row_tiles = (rows + 31) >> 5;
       const bool cols_ok = GATEUP ? (ns * (PN / 2) + 32 * cq < f) : (ns * PN + 64 * cq < d);
@@ -541,13 +547,16 @@ __global__ __launch_bounds__(PTHREADS) void prefill_gemm_kernel(
     c.a_rs = buf_rsrc(a_src, GATEUP ? static_cast<uint32_t>(g.T) * d * 2
                                     : static_cast<uint32_t>(g.T * (g.k + 1)) * f * 2);
     const int lane = c.p & 63, pw = c.p >> 6;
+    // the next job's tile is fetched while the current one runs
+    int ns_n = 0;
+    TileInfo ti_n = {};
+    bool ok_n = fetch_job(g, n_slices, n_gm, total, blockIdx.x, ns_n, ti_n);
     for (int job = blockIdx.x; job < total; job += gridDim.x) {
-      const int q = job >> 3;
-      const int ns = q % n_slices;
-      const int gm = (q / n_slices) * 8 + (job & 7);
-      if (gm >= n_gm) continue;
-      const TileInfo ti = find_tile(g, gm);
-      if (ti.slot < 0) continue;
+      const int ns = ns_n;
+      const TileInfo ti = ti_n;
+      const bool ok = ok_n;
+      ok_n = fetch_job(g, n_slices, n_gm, total, job + gridDim.x, ns_n, ti_n);
+      if (!ok) continue;                     // uniform
       c.b_rs = buf_rsrc(pool + static_cast<int64_t>(ti.slot) * slot_bytes,
                         static_cast<uint32_t>(slot_bytes));
 #pragma unroll
@@ -578,11 +587,20 @@ struct PrefillWs {
   GroupWorkspace gws;
   int32_t* perm;
   int32_t* tile_base;
+  int32_t* tile_group;
+  int32_t* group_slot;
   uint16_t* h;
 };
 
+// upper bound on (group, 256-row chunk) tiles: every group rounds up once,
+// plus the shared expert's group of T rows
+int64_t max_tiles(int T, int k, int E) {
+  return (static_cast<int64_t>(T) * k + PM - 1) / PM + E + (T + PM - 1) / PM;
+}
+
 PrefillWs prefill_ws(void* ws, int d, int f, int T, int k, int E) {
   (void)d;
+  (void)f;
   char* p = static_cast<char*>(ws);
   PrefillWs w;
   w.gws = group_workspace(p, T, E);
@@ -591,8 +609,11 @@ PrefillWs prefill_ws(void* ws, int d, int f, int T, int k, int E) {
   p += align256(static_cast<int64_t>(T) * k * 4);
   w.tile_base = reinterpret_cast<int32_t*>(p);
   p += align256(static_cast<int64_t>(E + 2) * 4);
+  w.tile_group = reinterpret_cast<int32_t*>(p);
+  p += align256(max_tiles(T, k, E) * 4);
+  w.group_slot = reinterpret_cast<int32_t*>(p);
+  p += align256(static_cast<int64_t>(E) * 4);
   w.h = reinterpret_cast<uint16_t*>(p);
-  (void)f;
   return w;
 }
 
@@ -641,14 +662,14 @@ hipError_t launch_prefill_fmt(const moe_layer& L, const uint16_t* x, int T, cons
   g.offsets = expert_offsets;
   g.perm = w.perm;
   g.tile_base = w.tile_base;
-  g.slot = slot;
+  g.tile_group = w.tile_group;
+  g.group_slot = w.group_slot;
   g.E = L.n_experts;
   g.T = T;
   g.k = L.top_k;
   g.shared_slot = out_shared ? L.shared_slot : -1;
-  // upper bound on (group, 256-row chunk) items: every group rounds up once
-  const int64_t max_gm = (static_cast<int64_t>(T) * L.top_k + PM - 1) / PM + L.n_experts +
-                         (out_shared ? (T + PM - 1) / PM : 0);
+  (void)slot;
+  const int64_t max_gm = max_tiles(T, L.top_k, L.n_experts);
   hipError_t e = launch_gemm<FMT, true>(g, max_gm * ((2 * L.d_ff + PN - 1) / PN), L, lay.G, x,
                                         w.h, nullptr, nullptr, s);
   if (e != hipSuccess) return e;
@@ -662,6 +683,8 @@ size_t prefill_workspace_bytes(int d, int f, int T, int k, int E) {
   (void)d;
   return group_workspace_bytes(T, E) + static_cast<size_t>(align256(static_cast<int64_t>(T) * k * 4)) +
          static_cast<size_t>(align256(static_cast<int64_t>(E + 2) * 4)) +
+         static_cast<size_t>(align256(max_tiles(T, k, E) * 4)) +
+         static_cast<size_t>(align256(static_cast<int64_t>(E) * 4)) +
          static_cast<size_t>(align256((static_cast<int64_t>(T) * k + T) * f * 2));
 }
 
@@ -673,7 +696,7 @@ hipError_t launch_prefill(const moe_layer& L, const uint16_t* x_bf16, int T, con
   const int T_shared = out_shared ? T : 0;
   hipError_t e = launch_group_pairs(idx, slot, nullptr, T, L.top_k, L.n_experts, true, w.gws,
                                     expert_offsets, w.perm, pair_pos, nullptr, nullptr,
-                                    w.tile_base, PM, s);
+                                    w.tile_base, PM, w.tile_group, w.group_slot, s);
   if (e != hipSuccess) return e;
   (void)T_shared;
   switch (L.fmt) {

@@ -30,7 +30,10 @@ hipError_t launch_lookup_small(const int32_t* idx, int T, int k, const int32_t* 
 // distinct[E] (ascending ids of non-empty groups; may be null),
 // counts_out[2] = {non-empty groups, selected pairs} (may be null),
 // tile_base[E+2] (may be null): prefix sums of ceil(group size / tile_m) for
-// the E groups plus one extra group of T rows (the shared expert).
+// the E groups plus one extra group of T rows (the shared expert);
+// tile_group[tile_base[E+1]] (may be null, needs tile_base): the group of
+// every tile; group_slot[E] (may be null): the slot of the first selected
+// pair of every non-empty group (all its pairs name one expert, so one slot).
 struct GroupWorkspace {
   int32_t* chunk_counts;  // [n_chunks * E]
   int32_t* totals;        // [2 * MOE_MAX_EXPERTS]: per-expert totals, then group starts
@@ -42,7 +45,8 @@ hipError_t launch_group_pairs(const int32_t* idx, const int32_t* slot_of_pair,
                               const int32_t* table, int T, int k, int E, bool select_hits,
                               GroupWorkspace gws, int32_t* offsets, int32_t* perm,
                               int32_t* pos, int32_t* distinct, int32_t* counts_out,
-                              int32_t* tile_base, int tile_m, hipStream_t s);
+                              int32_t* tile_base, int tile_m, int32_t* tile_group,
+                              int32_t* group_slot, hipStream_t s);
 
 size_t decode_workspace_bytes(int d, int f, int T, int k);
 hipError_t launch_decode(const moe_layer& L, const float* x, int T, const int32_t* idx,
