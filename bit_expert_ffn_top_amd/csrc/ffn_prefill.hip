@@ -93,8 +93,10 @@ __device__ __forceinline__ bool fetch_job(const GroupInfo& g, int n_slices, int 
   if (job >= total) return false;
   const int q = job >> 3;
   ns = q % n_slices;
-  const int gm = (q / n_slices) * 8 + (job & 7);
-  if (gm >= n_gm) return false;
+  // tiles from the last one down: the shared expert's full 256-row tiles
+  // (the longest jobs) first, so that the short ones fill the end
+  const int gm = n_gm - 1 - ((q / n_slices) * 8 + (job & 7));
+  if (gm < 0) return false;
   ti = find_tile(g, gm);
   return ti.slot >= 0;
 }
