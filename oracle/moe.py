@@ -259,6 +259,54 @@ def layer_decode(x, idx, slot, w, slot_weights, shared_slot, hits_only=True):
     return y
 
 
+def layer_decode_tiers(x, idx, w, slot, slot_weights, shared_slot, host_slot, host_weights,
+                       max_rank=None):
+    """One layer whose chosen experts sit in two tiers: the GPU cache and a
+    host-memory copy of the layer's experts.
+
+    [P2] "その2" and [P1] "共通の仕組み": the resident experts run on the GPU,
+    the misses are computed from host memory at the same time, and the two
+    parts are joined before the next layer.  [P4] "どう見るか": a setting
+    (on by default for NVIDIA GPUs from release 0.1.42) leaves out missed
+    experts of low rank, which changes the output slightly.
+
+    Readings: a miss's rank is its k-slot i (route_topk lists each token's
+    experts by descending logit); with max_rank = r a miss runs only if
+    i < r (None: every miss runs); the weights of the terms kept are not
+    renormalised (the pages name no rescaling); a miss whose expert has no
+    host slot (host_slot[e] < 0) contributes nothing.
+
+    y_t = x_t + sum_i term(t, i) + FFN_shared(x_t), where term(t, i) is
+      w[t,i] * FFN of GPU slot slot[t,i]          if slot[t,i] >= 0,
+      w[t,i] * FFN of host slot host_slot[e]      if slot[t,i] < 0, i < r and
+                                                  host_slot[e] >= 0 (e = idx[t,i]),
+      0                                           otherwise.
+    `slot_weights(s)` / `host_weights(h)` return (Wg, Wu, Wd) float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    r = k if max_rank is None else int(max_rank)
+    hs = np.asarray(host_slot)
+    y = x.copy()
+    for t in range(T):
+        acc = np.zeros_like(x[t])
+        for i in range(k):
+            s = int(slot[t][i])
+            if s >= 0:
+                W = slot_weights(s)
+            else:
+                h = int(hs[int(idx[t, i])])
+                if i >= r or h < 0:
+                    continue
+                W = host_weights(h)
+            acc += w[t][i] * expert_ffn(x[t:t + 1], *W)[0]
+        if shared_slot is not None and shared_slot >= 0:
+            acc += expert_ffn(x[t:t + 1], *slot_weights(int(shared_slot)))[0]
+        y[t] = x[t] + acc
+    return y
+
+
 def layer_dense_mixture(x, logits, expert_w, k, shared_w=None):
     """Dense definition: every one of the E experts evaluated, then only the
     top-k of each token kept with softmax weights.  Used to pin the sparse

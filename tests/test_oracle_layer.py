@@ -7,6 +7,10 @@
   experts followed by selection
 * combine is linear in the rows; a one-hot weight selects one row
 * hits-only partial + the missed experts = the full layer
+* two tiers (GPU cache + host copy): with every miss run it is the dense
+  brute-force layer; raising the rank limit by one adds exactly the missed
+  terms of that rank; a rank limit of 0 leaves the hits-only layer; the host
+  slot order does not matter; an expert in neither tier adds nothing
 * verify: T tokens at once equal T separate one-token layers
 """
 import numpy as np
@@ -112,6 +116,81 @@ def test_partial_plus_misses_is_full():
     ref = oracle.layer_dense_mixture(x, logits, W, k, Wsh)
     np.testing.assert_allclose(full, ref, rtol=1e-12, atol=1e-13)
     assert n[1] > 0 and n[1] < 3 * k
+
+
+def _two_tier_case(seed=11, E=16, d=64, f=32, k=5, T=4):
+    W, Wsh = _tiny_layer(E, d, f, shared=True, seed=seed)
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=(T, d))
+    logits = rng.normal(size=(T, E)).astype(np.float32)
+    idx, w = oracle.route_topk(logits, k)
+    resident = [0, 3, 4, 9, 12, 13]
+    table = np.full(E, -1, np.int32)
+    table[resident] = np.arange(len(resident))
+    gpu_W = [W[e] for e in resident] + [Wsh]
+    host_order = rng.permutation(E)              # host slot h holds expert host_order[h]
+    host_slot = np.empty(E, np.int32)
+    host_slot[host_order] = np.arange(E)
+    host_W = [W[e] for e in host_order]
+    slot, _, miss_p, _ = oracle.cache_lookup(idx, table)
+    return W, Wsh, x, logits, idx, w, slot, gpu_W, len(resident), host_slot, host_W, miss_p
+
+
+def test_two_tiers_full_is_dense():
+    W, Wsh, x, logits, idx, w, slot, gpu_W, sh, host_slot, host_W, miss_p = _two_tier_case()
+    assert len(miss_p) > 0
+    y = oracle.layer_decode_tiers(x, idx, w, slot, lambda s: gpu_W[s], sh, host_slot,
+                                  lambda h: host_W[h])
+    ref = oracle.layer_dense_mixture(x, logits, W, idx.shape[1], Wsh)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_two_tiers_rank_limit():
+    W, Wsh, x, logits, idx, w, slot, gpu_W, sh, host_slot, host_W, miss_p = _two_tier_case(seed=12)
+    T, k = idx.shape
+    ys = [oracle.layer_decode_tiers(x, idx, w, slot, lambda s: gpu_W[s], sh, host_slot,
+                                    lambda h: host_W[h], max_rank=r) for r in range(k + 1)]
+    # rank limit 0: the hits-only layer, whatever the host tier holds
+    part = oracle.layer_decode(x, idx, slot, w, lambda s: gpu_W[s], sh)
+    np.testing.assert_array_equal(ys[0], part)
+    zero_W = [tuple(np.zeros_like(m) for m in Wt) for Wt in host_W]
+    y0z = oracle.layer_decode_tiers(x, idx, w, slot, lambda s: gpu_W[s], sh, host_slot,
+                                    lambda h: zero_W[h], max_rank=0)
+    np.testing.assert_array_equal(y0z, part)
+    # each step of the limit adds the missed terms of that rank, nothing else
+    for r in range(1, k + 1):
+        for t in range(T):
+            want = np.zeros(x.shape[1])
+            if slot[t, r - 1] < 0:
+                want = w[t, r - 1] * oracle.expert_ffn(x[t:t + 1], *W[idx[t, r - 1]])[0]
+            np.testing.assert_allclose(ys[r][t] - ys[r - 1][t], want, rtol=1e-9, atol=1e-12)
+    np.testing.assert_array_equal(ys[k], oracle.layer_decode_tiers(
+        x, idx, w, slot, lambda s: gpu_W[s], sh, host_slot, lambda h: host_W[h]))
+
+
+def test_two_tiers_host_order_and_absent():
+    W, Wsh, x, logits, idx, w, slot, gpu_W, sh, host_slot, host_W, miss_p = _two_tier_case(seed=13)
+    T, k = idx.shape
+    E = len(W)
+    full = oracle.layer_decode_tiers(x, idx, w, slot, lambda s: gpu_W[s], sh, host_slot,
+                                     lambda h: host_W[h])
+    # identity host order gives the same result
+    same = oracle.layer_decode_tiers(x, idx, w, slot, lambda s: gpu_W[s], sh,
+                                     np.arange(E, dtype=np.int32), lambda h: W[h])
+    np.testing.assert_allclose(same, full, rtol=1e-13, atol=1e-14)
+    # a missed expert absent from the host tier drops exactly its terms
+    p = int(miss_p[0])
+    e = int(idx.reshape(-1)[p])
+    hs = host_slot.copy()
+    hs[e] = -1
+    got = oracle.layer_decode_tiers(x, idx, w, slot, lambda s: gpu_W[s], sh, hs,
+                                    lambda h: host_W[h])
+    for t in range(T):
+        want = full[t].copy()
+        for i in range(k):
+            if idx[t, i] == e and slot[t, i] < 0:
+                want -= w[t, i] * oracle.expert_ffn(x[t:t + 1], *W[e])[0]
+        np.testing.assert_allclose(got[t], want, rtol=1e-9, atol=1e-12)
 
 
 def test_verify_equals_separate_tokens():
