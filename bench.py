@@ -82,9 +82,11 @@ class DecodeChain:
     between layers, y = x + MoE(x) fed back grows without bound) and writes
     its y to a scratch buffer."""
 
-    def __init__(self, torch, bf, shape, pools, T, dev, xs):
+    def __init__(self, torch, bf, shape, pools, T, dev, xs, tiers=None, host_table=None,
+                 max_rank=None):
         self.torch, self.bf = torch, bf
         self.T = T
+        self.tiers, self.host_table, self.max_rank = tiers, host_table, max_rank
         self.layers = [bf.MoeLayer(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k, fmt,
                                    pool, shared_slot) for pool, _, shared_slot, fmt in pools]
         self.tables = [t for _, t, _, _ in pools]
@@ -102,12 +104,16 @@ class DecodeChain:
 
     def step(self, logits):
         """logits [n_layers, T, E].  One moe_decode_layer call per layer:
-        route, look up, expert FFN, combine."""
+        route, look up, expert FFN, combine; with host tiers, then one
+        moe_decode_misses call that adds the missed experts."""
         bf = self.bf
         for l, L in enumerate(self.layers):
             bf.decode_layer(L, self.xs[l], logits[l], self.tables[l], idx=self.idx, w=self.w,
                             slot=self.slot, miss_expert=self.miss_e, miss_pair=self.miss_p,
                             n_miss=self.n_miss, y=self.y, ws=self.ws)
+            if self.tiers is not None:
+                bf.decode_misses(self.tiers[l], self.xs[l], self.idx, self.slot, self.w,
+                                 self.host_table, self.y, max_rank=self.max_rank, ws=self.ws)
         return self.y
 
 
@@ -316,7 +322,10 @@ def run_extras(torch, np, bf, synth, pools, dev, args):
         "hit_rate": round(hits / tot, 4),
     }
     log(f"expert cache: {steps2 / dt:.1f} tok/s, hit rate {hits / tot:.3f} ({time.perf_counter() - t0:.1f} s)")
-    del pools2, chain2, logits2
+    del chain2
+    out["expert_cache"].update(run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev,
+                                             steps2, n_graphs, tot - hits))
+    del pools2, logits2
     torch.cuda.empty_cache()
 
     # ---------------- verify step ----------------
@@ -362,6 +371,67 @@ def run_extras(torch, np, bf, synth, pools, dev, args):
     # ---------------- prefill chunk ----------------
     out["prefill"] = run_prefill(torch, np, bf, synth, pools, dev, args)
     return out
+
+
+def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_graphs, n_missed):
+    """The expert-cache workload as whole layers: after each layer's GPU
+    part, moe_decode_misses reads the missed experts from a pinned host copy
+    of that layer (all 512 experts) and joins them into y.  Timed with every
+    miss run and with misses of rank >= 5 left out; the change that leaving
+    them out makes to the layers' updates is reported too."""
+    E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
+    t0 = time.perf_counter()
+    sb = synth.slot_bytes(synth.FMT_Q2SM, d, f)
+    tiers = []
+    for l in range(N_LAYERS):
+        hp = torch.empty((E, sb), dtype=torch.uint8, pin_memory=True)
+        for e0 in range(0, E, 128):
+            ids = list(range(e0, min(E, e0 + 128)))
+            hp[e0:e0 + len(ids)].copy_(synth.make_layer_pool(2, l, ids, device=dev,
+                                                             fmt=synth.FMT_Q2SM, batch=64))
+        tiers.append(bf.HostTier(d, f, E, k, synth.FMT_Q2SM, hp))
+    host_table = torch.arange(E, dtype=torch.int32, device=dev)   # host slot = expert id
+    torch.cuda.synchronize()
+    log(f"host tiers: {N_LAYERS} x {E} experts pinned ({N_LAYERS * E * sb / 1e9:.1f} GB) "
+        f"in {time.perf_counter() - t0:.1f} s")
+    xs = [synth.make_x(2, l, 1, d, device=dev) for l in range(N_LAYERS)]
+    res = {}
+    misses_per_token = n_missed / n_graphs
+    for name, r in (("full_layer", None), ("rank_limit_5", 5)):
+        chain = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, tiers=tiers,
+                            host_table=host_table, max_rank=r)
+        dt, _, graphs = time_graph_steps(torch, chain, logits2, steps, 5, n_graphs)
+        del graphs
+        res[name + "_tok_s"] = round(steps / dt, 2)
+        res[name + "_ms_per_step"] = round(dt * 1e3 / steps, 5)
+        log(f"expert cache, {name}: {steps / dt:.1f} tok/s")
+    # at batch 1 every missed pair is a distinct expert read from the host tier
+    res["missed_experts_per_token"] = round(misses_per_token, 2)
+    res["host_read_MB_per_token"] = round(misses_per_token * sb / 1e6, 1)
+    # effect of the rank limit on each layer's update y - x (graph 0's routing)
+    chain_full = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, tiers=tiers,
+                             host_table=host_table)
+    rel = []
+    for l in range(N_LAYERS):
+        L = chain_full.layers[l]
+        args = dict(idx=chain_full.idx, w=chain_full.w, slot=chain_full.slot,
+                    miss_expert=chain_full.miss_e, miss_pair=chain_full.miss_p,
+                    n_miss=chain_full.n_miss, ws=chain_full.ws)
+        y_full, *_ = bf.decode_layer(L, xs[l], logits2[0][l], chain_full.tables[l], **args)
+        y_lim = y_full.clone()
+        bf.decode_misses(tiers[l], xs[l], chain_full.idx, chain_full.slot, chain_full.w,
+                         host_table, y_full, ws=chain_full.ws)
+        bf.decode_misses(tiers[l], xs[l], chain_full.idx, chain_full.slot, chain_full.w,
+                         host_table, y_lim, max_rank=5, ws=chain_full.ws)
+        upd = (y_full - xs[l]).norm().item()
+        rel.append((y_full - y_lim).norm().item() / upd if upd > 0 else 0.0)
+    res["rank_limit_5_rel_change_of_update"] = round(float(np.mean(rel)), 4)
+    res["host_tier"] = ("all 512 experts of each layer in pinned host memory, read by the decode "
+                        "kernel over the host link (no copy engine); one moe_decode_misses call "
+                        "per layer after the GPU part, in the same graph")
+    log(f"host tier: {res} ({time.perf_counter() - t0:.1f} s)")
+    del tiers, chain, chain_full
+    return res
 
 
 def run_prefill(torch, np, bf, synth, pools, dev, args):

@@ -5,7 +5,8 @@ include/bitffn_moe.h); this package is its thin Python binding.
 """
 from ._binding import (  # noqa: F401
     DTYPE_BF16, DTYPE_F32, FMT_Q2S, FMT_Q2SM, FMT_Q3G, MoeError, MoeLayer, abi_version,
-    cache_lookup, combine, decode_layer, decode_workspace_bytes, expert_ffn_decode,
+    HostTier, cache_lookup, combine, decode_layer, decode_misses, decode_workspace_bytes,
+    expert_ffn_decode,
     expert_ffn_prefill,
     lib, lib_path, lookup_workspace_bytes, prefill_workspace_bytes, route_topk, slot_bytes,
 )

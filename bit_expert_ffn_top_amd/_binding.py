@@ -50,6 +50,8 @@ SIGNATURES = {
     "moe_expert_ffn_decode": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
     "moe_decode_layer": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _c_sz, _vp]),
+    "moe_decode_misses": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, _vp,
+                                   _c_sz, _vp]),
     "moe_prefill_workspace_bytes": (_c_sz, [_LP, _c_int]),
     "moe_expert_ffn_prefill": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _c_sz, _vp]),
@@ -230,6 +232,51 @@ def decode_layer(layer: MoeLayer, x, logits, slot_of_expert, idx=None, w=None, s
                                   _ptr(miss_expert), _ptr(miss_pair), _ptr(n_miss), _ptr(y),
                                   _ptr(ws), ws.numel(), _stream(stream)), "moe_decode_layer")
     return y, idx, w, slot, miss_expert, miss_pair, n_miss
+
+
+@dataclasses.dataclass
+class HostTier:
+    """A layer's experts in pinned host memory that the GPU reads directly
+    (the tier the GPU cache's misses are computed from)."""
+    d_model: int
+    d_ff: int
+    n_experts: int
+    top_k: int
+    fmt: int
+    pool: torch.Tensor            # uint8 [n_slots, slot_bytes], pinned host (or device) memory
+
+    def __post_init__(self):
+        if self.pool.dtype != torch.uint8 or self.pool.dim() != 2 or not self.pool.is_contiguous():
+            raise ValueError("host tier pool: contiguous uint8 [n_slots, slot_bytes] expected")
+        if not (self.pool.is_cuda or self.pool.is_pinned()):
+            raise ValueError("host tier pool: pinned host memory or device memory expected")
+
+    def c_struct(self) -> MoeLayerC:
+        n_slots, sb = self.pool.shape
+        return MoeLayerC(self.d_model, self.d_ff, self.n_experts, self.top_k, self.fmt,
+                         n_slots, -1, 0, sb, self.pool.data_ptr())
+
+
+def decode_misses(tier: HostTier, x, idx, slot, w, host_slot_of_expert, y, max_rank=None,
+                  ws=None, stream=None):
+    """Add the missed pairs of a decode step, computed from the host tier,
+    into y (moe_decode_misses).  y holds the GPU part on entry.  Returns y."""
+    for t, dt, name in ((x, torch.float32, "x"), (idx, torch.int32, "idx"),
+                        (slot, torch.int32, "slot"), (w, torch.float32, "w"),
+                        (host_slot_of_expert, torch.int32, "host_slot_of_expert"),
+                        (y, torch.float32, "y")):
+        _dev(t, dt, name)
+    T = x.shape[0]
+    k = tier.top_k
+    r = k if max_rank is None else int(max_rank)
+    L = tier.c_struct()
+    if ws is None:
+        ws = torch.empty((int(lib().moe_decode_workspace_bytes(ctypes.byref(L), T)),),
+                         dtype=torch.uint8, device=x.device)
+    _check(lib().moe_decode_misses(ctypes.byref(L), _ptr(x), T, _ptr(idx), _ptr(slot), _ptr(w),
+                                   _ptr(host_slot_of_expert), r, _ptr(y), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "moe_decode_misses")
+    return y
 
 
 def prefill_workspace_bytes(layer: MoeLayer, T: int) -> int:

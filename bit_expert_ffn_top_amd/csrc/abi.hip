@@ -154,6 +154,38 @@ int moe_decode_layer(const moe_layer* L, const float* x, int T, const float* log
                                                 miss_expert, miss_pair, n_miss, y, ws, stream));
 }
 
+int moe_decode_misses(const moe_layer* H, const float* x, int T, const int32_t* idx,
+                      const int32_t* slot, const float* w, const int32_t* host_slot_of_expert,
+                      int max_rank, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int st = check_layer(H);
+  if (st != MOE_OK) return st;
+  if (H->shared_slot != -1) return MOE_EINVAL;
+  if (T < 1 || T > MOE_MAX_DECODE_T || T * H->top_k > MOE_MAX_DECODE_PAIRS) return MOE_EINVAL;
+  if (max_rank < 0 || max_rank > H->top_k) return MOE_EINVAL;
+  if (!x || !idx || !slot || !w || !host_slot_of_expert || !y || !ws) return MOE_EINVAL;
+  if (static_cast<const void*>(x) == static_cast<const void*>(y)) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(idx) || !aligned16(slot) || !aligned16(w) ||
+      !aligned16(host_slot_of_expert) || !aligned16(y))
+    return MOE_EALIGN;
+  if (!aligned256(ws)) return MOE_EALIGN;
+  if (ws_bytes < bitffn::decode_workspace_bytes(H->d_model, H->d_ff, T, H->top_k))
+    return MOE_ENOSPC;
+  // The pool must be memory this device can address: pinned host memory
+  // (its device-side address is used) or device memory.  Pageable host
+  // memory is refused.
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, H->pool) != hipSuccess) {
+    (void)hipGetLastError();   // leave no error behind for the next launch check
+    return MOE_EINVAL;
+  }
+  const void* pool_dev = attr.devicePointer;
+  if (!pool_dev || (attr.type != hipMemoryTypeHost && attr.type != hipMemoryTypeDevice))
+    return MOE_EINVAL;
+  if (max_rank == 0) return MOE_OK;   // no miss can run
+  return hip_status(bitffn::launch_decode_misses(*H, pool_dev, x, T, idx, slot, w,
+                                                 host_slot_of_expert, max_rank, y, ws, stream));
+}
+
 size_t moe_prefill_workspace_bytes(const moe_layer* L, int T) {
   if (check_layer(L) != MOE_OK || T < 1 || T > 65536) return 0;
   return bitffn::prefill_workspace_bytes(L->d_model, L->d_ff, T, L->top_k, L->n_experts);

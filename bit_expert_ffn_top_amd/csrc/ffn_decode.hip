@@ -39,6 +39,13 @@ constexpr int SLICE = 32;          // h indices per workgroup
 constexpr int MAX_DROWS = 2048 / KA_THREADS;   // D rows per thread: d_model <= 2048
 static_assert(2048 / 64 <= 4 * KA_WAVES, "G units per wavefront above 4");
 
+// What selects the union members' slots.
+enum FfnMode {
+  kPairs = 0,   // the pair slots given by the caller
+  kRoute = 1,   // routing done in the kernel (top-k, slot table)
+  kMiss = 2,    // missed pairs only, their slots in a second pool (host tier)
+};
+
 struct FfnArgs {
   const uint8_t* pool;
   int64_t slot_bytes;
@@ -57,6 +64,11 @@ struct FfnArgs {
   int32_t* o_miss_expert;       // [<= T*k]
   int32_t* o_miss_pair;         // [T*k] or null
   int32_t* o_n_miss;            // [2]
+  // miss mode only: the pairs' experts; `table` is then the host tier's
+  // slot of each expert (entries outside [0, n_slots) count as absent), and
+  // a miss of k-slot i runs only if i < max_rank
+  const int32_t* idx;           // [T][k]
+  int max_rank, n_slots;
 };
 
 // Survivors of the first top-k level in the fused kernel: T * ceil(E/64) * k
@@ -125,10 +137,13 @@ __device__ __forceinline__ float wave_total(float v) {
 
 // UPW: G units (2 blocks) per wavefront, ceil(d_model / 64 / KA_WAVES); wavefront
 // w takes units w, w + KA_WAVES, ...  d_model <= 2048.
-// ROUTE: the workgroup first routes the T tokens itself (top-k over the
+// MODE kRoute: the workgroup first routes the T tokens itself (top-k over the
 // logits, slots from the slot table held in LDS) instead of reading the pair
-// slots; workgroups of the shared expert skip routing.
-template <int FMT, int UPW, bool ROUTE>
+// slots; workgroups of the shared expert skip routing.  MODE kMiss: a pair's
+// slot is its expert's slot in the host tier if the pair missed the GPU
+// cache and its rank is below the limit, else none; there is no shared
+// member.
+template <int FMT, int UPW, int MODE>
 __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
                                                                 const float* __restrict__ x) {
   const int js = blockIdx.x;
@@ -138,7 +153,14 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
   const int d = a.d;
   const int n = a.T * a.k;
   int sp = -1;   // slot of pair `lane`
-  if (!ROUTE) sp = lane < n ? a.slot[lane] : -1;
+  if (MODE == kPairs) sp = lane < n ? a.slot[lane] : -1;
+  if (MODE == kMiss) {
+    const int p = min(lane, n - 1);
+    const int gpu_slot = a.slot[p];
+    const int e = min(max(a.idx[p], 0), a.E - 1);
+    const int hs = a.table[e];
+    sp = lane < n && gpu_slot < 0 && p % a.k < a.max_rank && hs < a.n_slots ? hs : -1;
+  }
 
   // Every load below is unconditional, with indices clamped into range (the
   // surplus values are never used), so the compiler can count outstanding
@@ -153,7 +175,7 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
   }
   __builtin_amdgcn_sched_barrier(0);   // keep the issue order
 
-  if (ROUTE && u < n) {   // uniform per workgroup
+  if (MODE == kRoute && u < n) {   // uniform per workgroup
     __shared__ uint64_t s_grp[KA_WAVES * 64];
     __shared__ uint64_t s_cand[kFusedCand];
     __shared__ uint64_t s_top[MOE_MAX_DECODE_PAIRS];
@@ -352,6 +374,8 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
 
 // y = x + sum_{i: slot >= 0} w_i * P(t, i) + P(t, k), P(t, i) = sum over
 // slices of term i's partials (P(t, k): the shared expert, if any).
+// MISS: y += sum_{i in the miss set} w_i * P(t, i), the miss set as the ffn
+// kernel's miss mode selects it; no shared term.
 // Workgroup: 32 rows (128 bytes of a partial row: whole memory lines), one
 // wavefront per term (terms i, i+16, ...); lane = (row r, slice group g of
 // 2), group g sums its half of the slices in order, the two group sums meet
@@ -364,10 +388,12 @@ constexpr int KB_WAVES = 16;
 constexpr int KB_CHUNK = 16;
 static_assert(KB_GROUPS == 2, "the group sums meet in one exchange");
 
+template <bool MISS>
 __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
     const float* __restrict__ x, const int32_t* __restrict__ slot, const float* __restrict__ w,
     int T, int k, int d, int nslices, int has_shared, const float* __restrict__ part,
-    float* __restrict__ y) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ host_slot, int n_experts,
+    int max_rank, int n_slots, float* __restrict__ y) {
   extern __shared__ float red[];  // [k+1][KB_ROWS]
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -375,12 +401,17 @@ __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
   const int rr = lane % KB_ROWS, g = lane / KB_ROWS;
   const int r = blockIdx.x * KB_ROWS + rr;
   const int ti = min(lane, k - 1);
-  const int sp = slot[t * k + ti];               // lane i < k: slot of term i
+  int sp = slot[t * k + ti];                     // lane i < k: slot of term i
   const float wv = w[t * k + ti];                // lane i < k: weight of term i
-  const float xr = x[static_cast<int64_t>(t) * d + r];
+  if (MISS) {
+    const int hs = host_slot[min(max(idx[t * k + ti], 0), n_experts - 1)];
+    sp = sp < 0 && ti < max_rank && hs < n_slots ? hs : -1;
+  }
+  const float xr = MISS ? y[static_cast<int64_t>(t) * d + r] : x[static_cast<int64_t>(t) * d + r];
   const int per = (nslices + KB_GROUPS - 1) / KB_GROUPS;
   const int j0 = min(nslices, g * per), j1 = min(nslices, j0 + per);
   for (int i = wave; i < k + 1; i += KB_WAVES) {
+    if (i < k ? __builtin_amdgcn_readlane(sp, i) < 0 : !has_shared) continue;   // term unused
     const float* src = part + ((static_cast<int64_t>(t) * (k + 1) + i) * nslices) * d + r;
     float acc = 0.0f;
     for (int j = j0; j < j1; j += KB_CHUNK) {
@@ -409,14 +440,14 @@ size_t part_bytes(int d, int f, int T, int k) {
   return static_cast<size_t>(static_cast<int64_t>(T) * (k + 1) * (f / SLICE) * d * 4);
 }
 
-template <int FMT, bool ROUTE>
+template <int FMT, int MODE>
 hipError_t launch_ffn(const FfnArgs& a, const float* x, hipStream_t s) {
-  const dim3 grid(a.f / SLICE, a.T * a.k + 1);
+  const dim3 grid(a.f / SLICE, a.T * a.k + (MODE == kMiss ? 0 : 1));
   const int upw = (a.d / 64 + KA_WAVES - 1) / KA_WAVES;
   if (upw <= 1)
-    decode_ffn_kernel<FMT, 1, ROUTE><<<grid, KA_THREADS, 0, s>>>(a, x);
+    decode_ffn_kernel<FMT, 1, MODE><<<grid, KA_THREADS, 0, s>>>(a, x);
   else
-    decode_ffn_kernel<FMT, 2, ROUTE><<<grid, KA_THREADS, 0, s>>>(a, x);
+    decode_ffn_kernel<FMT, 2, MODE><<<grid, KA_THREADS, 0, s>>>(a, x);
   return hipGetLastError();
 }
 
@@ -438,12 +469,12 @@ FfnArgs ffn_args(const moe_layer& L, int T, const int32_t* slot, void* ws) {
   return a;
 }
 
-template <bool ROUTE>
+template <int MODE>
 hipError_t launch_ffn_fmt(int fmt, const FfnArgs& a, const float* x, hipStream_t s) {
   switch (fmt) {
-    case MOE_FMT_Q2S: return launch_ffn<MOE_FMT_Q2S, ROUTE>(a, x, s);
-    case MOE_FMT_Q2SM: return launch_ffn<MOE_FMT_Q2SM, ROUTE>(a, x, s);
-    case MOE_FMT_Q3G: return launch_ffn<MOE_FMT_Q3G, ROUTE>(a, x, s);
+    case MOE_FMT_Q2S: return launch_ffn<MOE_FMT_Q2S, MODE>(a, x, s);
+    case MOE_FMT_Q2SM: return launch_ffn<MOE_FMT_Q2SM, MODE>(a, x, s);
+    case MOE_FMT_Q3G: return launch_ffn<MOE_FMT_Q3G, MODE>(a, x, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -453,8 +484,20 @@ hipError_t launch_combine_partials(const moe_layer& L, const float* x, int T,
                                    float* y, hipStream_t s) {
   const dim3 grid(L.d_model / KB_ROWS, T);
   const size_t lds = static_cast<size_t>(L.top_k + 1) * KB_ROWS * 4;
-  decode_combine_kernel<<<grid, KB_WAVES * 64, lds, s>>>(
-      x, slot, w, T, L.top_k, L.d_model, L.d_ff / SLICE, L.shared_slot >= 0 ? 1 : 0, part, y);
+  decode_combine_kernel<false><<<grid, KB_WAVES * 64, lds, s>>>(
+      x, slot, w, T, L.top_k, L.d_model, L.d_ff / SLICE, L.shared_slot >= 0 ? 1 : 0, part,
+      nullptr, nullptr, 1, 0, 0, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_misses(const moe_layer& H, int T, const int32_t* idx,
+                                 const int32_t* slot, const float* w, const int32_t* host_slot,
+                                 int max_rank, const float* part, float* y, hipStream_t s) {
+  const dim3 grid(H.d_model / KB_ROWS, T);
+  const size_t lds = static_cast<size_t>(H.top_k + 1) * KB_ROWS * 4;
+  decode_combine_kernel<true><<<grid, KB_WAVES * 64, lds, s>>>(
+      nullptr, slot, w, T, H.top_k, H.d_model, H.d_ff / SLICE, 0, part, idx, host_slot,
+      H.n_experts, max_rank, H.n_slots, y);
   return hipGetLastError();
 }
 
@@ -469,7 +512,7 @@ hipError_t launch_decode(const moe_layer& L, const float* x, int T, const int32_
                          hipStream_t s) {
   (void)idx;
   const FfnArgs a = ffn_args(L, T, slot, ws);
-  const hipError_t e = launch_ffn_fmt<false>(L.fmt, a, x, s);
+  const hipError_t e = launch_ffn_fmt<kPairs>(L.fmt, a, x, s);
   if (e != hipSuccess) return e;
   return launch_combine_partials(L, x, T, slot, w, a.part, y, s);
 }
@@ -487,9 +530,25 @@ hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const 
   a.o_miss_expert = miss_expert;
   a.o_miss_pair = miss_pair;
   a.o_n_miss = n_miss;
-  const hipError_t e = launch_ffn_fmt<true>(L.fmt, a, x, s);
+  const hipError_t e = launch_ffn_fmt<kRoute>(L.fmt, a, x, s);
   if (e != hipSuccess) return e;
   return launch_combine_partials(L, x, T, slot, w, a.part, y, s);
+}
+
+hipError_t launch_decode_misses(const moe_layer& H, const void* host_pool_dev, const float* x,
+                                int T, const int32_t* idx, const int32_t* slot, const float* w,
+                                const int32_t* host_slot_of_expert, int max_rank, float* y,
+                                void* ws, hipStream_t s) {
+  FfnArgs a = ffn_args(H, T, slot, ws);
+  a.pool = static_cast<const uint8_t*>(host_pool_dev);
+  a.shared_slot = -1;
+  a.table = host_slot_of_expert;
+  a.idx = idx;
+  a.max_rank = max_rank;
+  a.n_slots = H.n_slots;
+  const hipError_t e = launch_ffn_fmt<kMiss>(H.fmt, a, x, s);
+  if (e != hipSuccess) return e;
+  return launch_combine_misses(H, T, idx, slot, w, host_slot_of_expert, max_rank, a.part, y, s);
 }
 
 }  // namespace bitffn

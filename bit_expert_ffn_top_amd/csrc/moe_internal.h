@@ -59,6 +59,12 @@ hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const 
                                const int32_t* slot_of_expert, int32_t* idx, float* w,
                                int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
                                int32_t* n_miss, float* y, void* ws, hipStream_t s);
+// Missed pairs of a decode step computed from a second pool (the host tier,
+// `host_pool_dev` its device-side address) and added into y.
+hipError_t launch_decode_misses(const moe_layer& H, const void* host_pool_dev, const float* x,
+                                int T, const int32_t* idx, const int32_t* slot, const float* w,
+                                const int32_t* host_slot_of_expert, int max_rank, float* y,
+                                void* ws, hipStream_t s);
 
 size_t prefill_workspace_bytes(int d, int f, int T, int k, int E);
 hipError_t launch_prefill(const moe_layer& L, const uint16_t* x_bf16, int T,

@@ -193,6 +193,46 @@ int moe_decode_layer(const moe_layer* L, const float* x, int T,
                      int32_t* miss_expert, int32_t* miss_pair, int32_t* n_miss,
                      float* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Miss execution and the per-layer join of a decode / verify step.  The
+ * chosen experts not resident in the GPU cache are computed from the host
+ * tier, a copy of the layer's experts in host memory, and added to the GPU
+ * part ("Strataとは？VRAM 12GBのGPUで…" (vramglass.com), section "その2":
+ * the misses run at the same time as the resident experts, from host memory,
+ * instead of being copied to the GPU; "FreeToken vs Strata", "共通の仕組み":
+ * both parts meet before the next layer).  Optionally misses of low rank are
+ * left out ("Strata" page, section "どう見るか": a setting that drops missed
+ * experts of low rank, which changes the output slightly).
+ *   H          host tier: same d_model, d_ff, n_experts, top_k and fmt as
+ *              the GPU layer; H->pool points to H->n_slots packed slots in
+ *              pinned host memory that this device can address (hipHostMalloc)
+ *              or in device memory; pageable memory gives MOE_EINVAL.
+ *              H->shared_slot must be -1 (the shared expert is resident).
+ *   x          fp32 [T][d_model], the layer input.
+ *   idx, w     int32 / fp32 [T][k], the routing of this step (rank order;
+ *              ids distinct within a token, as moe_route_topk gives them).
+ *   slot       int32 [T][k], the GPU slots of this step (-1 = miss).
+ *   host_slot_of_expert  int32 [n_experts], slot of each expert in H; a
+ *              value outside [0, H->n_slots) means not there, and such a
+ *              miss adds nothing.
+ *   max_rank   0..top_k: a miss in k-slot i runs only if i < max_rank
+ *              (top_k: every miss; 0: nothing is enqueued).  The weights
+ *              of the terms kept are not rescaled.
+ *   y          fp32 [T][d_model], in and out: on entry the GPU part (the y
+ *              of moe_expert_ffn_decode / moe_decode_layer for the same
+ *              step); on return
+ *   y[t] += sum_{i < max_rank: slot[t*k+i] < 0, h >= 0} w[t*k+i] * FFN_h(x[t]),
+ *              h = host_slot_of_expert[idx[t*k+i]], terms in k-slot order.
+ * Each distinct missed expert is read from the host tier once for all
+ * tokens that chose it, by the GPU's own loads (no copy engine, no host
+ * wait), so the call can sit in a captured graph after the GPU part.
+ * Limits as moe_expert_ffn_decode (T * top_k <= 64).  ws: at least
+ * moe_decode_workspace_bytes(H, T) bytes, 256-byte aligned (the GPU part's
+ * workspace may be reused once that part is done). */
+int moe_decode_misses(const moe_layer* H, const float* x, int T,
+                      const int32_t* idx, const int32_t* slot, const float* w,
+                      const int32_t* host_slot_of_expert, int max_rank,
+                      float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* (host) Workspace bytes that moe_expert_ffn_prefill needs for T tokens. */
 size_t moe_prefill_workspace_bytes(const moe_layer* L, int T);
 
