@@ -205,6 +205,85 @@ def cache_lookup(idx, slot_of_expert):
 
 
 # ---------------------------------------------------------------------------
+# cache admission and eviction
+# ---------------------------------------------------------------------------
+
+def cache_count(counts, idx):
+    """Usage counts: counts[e] plus the number of times expert e is chosen in
+    idx ([P1] table "VRAMのエキスパートの入れ替え": the cache starts from a
+    table of measured usage frequencies).  Returns a new uint32 array."""
+    out = np.asarray(counts, dtype=np.uint64).copy()
+    for e in np.asarray(idx).reshape(-1):
+        out[int(e)] += 1
+    return (out & 0xFFFFFFFF).astype(np.uint32)
+
+
+def cache_plan(counts, slot_of_expert, expert_of_slot, shared_slot, host_slot, host_n_slots,
+               max_swaps, decay_shift):
+    """Choose which experts enter and leave the GPU cache.
+
+    [P1] table "VRAMのエキスパートの入れ替え" and [P2] "その1": the cache holds
+    the most used experts and is updated as the conversation moves on;
+    [P4] "GPU・CPU・RAM・SSDの分担": the cache changes with the conversation.
+    The pages give no rule; the reading used:
+
+    * candidates: experts not resident (slot_of_expert < 0) with a copy in the
+      host tier (0 <= host_slot < host_n_slots) and a count above 0, best
+      first by (count descending, id ascending);
+    * victims: the cache's slots except the shared expert's, worst first by
+      (key ascending, slot ascending), where an empty slot
+      (expert_of_slot = -1) has key -1 and a full one its expert's count;
+    * the i-th candidate replaces the i-th victim while i < max_swaps and its
+      count is strictly above the victim's key (equal counts never swap);
+    * the evicted expert leaves the slot table at once
+      (slot_of_expert[old] = -1) and the slot is reserved for the newcomer
+      (expert_of_slot[slot] = new); the newcomer becomes visible only at
+      cache_commit, after its bytes have been copied;
+    * afterwards every count is shifted right by decay_shift, so that old
+      use fades (halving per update for a shift of 1).
+
+    Returns (counts, slot_of_expert, expert_of_slot, swaps) with swaps a list
+    of (slot, old expert or -1, new expert, host slot of the new expert).
+    """
+    cnt = np.asarray(counts, dtype=np.int64)
+    soe = np.asarray(slot_of_expert, dtype=np.int32).copy()
+    eos = np.asarray(expert_of_slot, dtype=np.int32).copy()
+    hs = np.asarray(host_slot, dtype=np.int64)
+    E = len(cnt)
+    cands = [e for e in range(E)
+             if soe[e] < 0 and 0 <= hs[e] < host_n_slots and cnt[e] > 0]
+    cands.sort(key=lambda e: (-cnt[e], e))
+    victims = []
+    for s in range(len(eos)):
+        if s == shared_slot:
+            continue
+        key = -1 if eos[s] < 0 else int(cnt[eos[s]])
+        victims.append((key, s))
+    victims.sort()
+    swaps = []
+    for i in range(min(max_swaps, len(cands), len(victims))):
+        e = cands[i]
+        key, s = victims[i]
+        if not cnt[e] > key:
+            break
+        old = int(eos[s])
+        if old >= 0:
+            soe[old] = -1
+        eos[s] = e
+        swaps.append((s, old, e, int(hs[e])))
+    out = (cnt >> int(decay_shift)).astype(np.uint32)
+    return out, soe, eos, swaps
+
+
+def cache_commit(slot_of_expert, swaps):
+    """The newcomers of a plan become visible: slot_of_expert[new] = slot."""
+    soe = np.asarray(slot_of_expert, dtype=np.int32).copy()
+    for s, _, e, _ in swaps:
+        soe[e] = s
+    return soe
+
+
+# ---------------------------------------------------------------------------
 # expert FFN and the layer
 # ---------------------------------------------------------------------------
 
