@@ -83,10 +83,11 @@ class DecodeChain:
     its y to a scratch buffer."""
 
     def __init__(self, torch, bf, shape, pools, T, dev, xs, tiers=None, host_table=None,
-                 max_rank=None):
+                 max_rank=None, counts=None):
         self.torch, self.bf = torch, bf
         self.T = T
         self.tiers, self.host_table, self.max_rank = tiers, host_table, max_rank
+        self.counts = counts
         self.layers = [bf.MoeLayer(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k, fmt,
                                    pool, shared_slot) for pool, _, shared_slot, fmt in pools]
         self.tables = [t for _, t, _, _ in pools]
@@ -114,6 +115,8 @@ class DecodeChain:
             if self.tiers is not None:
                 bf.decode_misses(self.tiers[l], self.xs[l], self.idx, self.slot, self.w,
                                  self.host_table, self.y, max_rank=self.max_rank, ws=self.ws)
+            if self.counts is not None:
+                bf.cache_count(self.idx, self.counts[l])
         return self.y
 
 
@@ -430,7 +433,135 @@ def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_gr
                         "kernel over the host link (no copy engine); one moe_decode_misses call "
                         "per layer after the GPU part, in the same graph")
     log(f"host tier: {res} ({time.perf_counter() - t0:.1f} s)")
-    del tiers, chain, chain_full
+    del chain, chain_full
+    res["adaptive"] = run_adaptive_cache(torch, np, bf, synth, shape, pools2, tiers, host_table,
+                                         xs, dev)
+    del tiers
+    return res
+
+
+def run_adaptive_cache(torch, np, bf, synth, shape, pools2, tiers, host_table, xs, dev,
+                       period=16, max_swaps=8, warm_steps=128, steps=64):
+    """Routing drifts to another conversation (a new popularity order per
+    layer), and the cache follows it: every token counts its experts, every
+    `period` tokens each layer plans up to `max_swaps` swaps (counts halve),
+    copies the newcomers from the host tier and commits them.  Whole layers
+    (GPU part + misses from the host tier).  Reported: the hit rate of the
+    original cache on the new routing, the hit rate after adapting (on
+    held-out tokens of the new routing), and tok/s of the timed steps with
+    the maintenance included."""
+    E, k, d = shape.n_experts, shape.top_k, shape.d_model
+    c2 = synth.WORKLOADS[2]
+    t0 = time.perf_counter()
+    drift = 1000                     # layer offset of the new popularity order
+
+    def logits_of(step):             # [48, 1, E], a fresh token per step
+        return torch.stack([synth.zipf_gumbel_logits(2, l + drift, 1, E, c2["zipf_s"],
+                                                     device=dev, step=step)
+                            for l in range(N_LAYERS)])
+
+    def hit_rate(tables, first_step, n):
+        hits = tot = 0
+        for st in range(first_step, first_step + n):
+            lg = logits_of(st).cpu().numpy()
+            for l in range(N_LAYERS):
+                idx = np.argsort(-lg[l], axis=1, kind="stable")[:, :k]
+                hits += int((tables[l][idx] >= 0).sum())
+                tot += idx.size
+        return hits / tot
+
+    tables = [t for _, t, _, _ in pools2]
+    held_out = 10_000
+    static_hit = hit_rate([t.cpu().numpy() for t in tables], held_out, 16)
+    eos = []
+    shared = []
+    for l in range(N_LAYERS):
+        _, shared_slot, slot_expert = synth.make_slot_table(2, l)
+        eos.append(torch.tensor(slot_expert, dtype=torch.int32, device=dev))
+        shared.append(shared_slot)
+    counts = [torch.zeros(E, dtype=torch.int32, device=dev) for _ in range(N_LAYERS)]
+    chain = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, tiers=tiers, host_table=host_table,
+                        counts=counts)
+    swaps = [torch.full((max_swaps, 4), -1, dtype=torch.int32, device=dev) for _ in range(N_LAYERS)]
+    n_sw = [torch.zeros(4, dtype=torch.int32, device=dev) for _ in range(N_LAYERS)]
+
+    def maintain():
+        for l in range(N_LAYERS):
+            bf.cache_plan(counts[l], tables[l], eos[l], shared[l], host_table, E, max_swaps, 1,
+                          swaps=swaps[l], n_swaps=n_sw[l])
+            bf.cache_fill(chain.layers[l], tiers[l], swaps[l], n_sw[l])
+            bf.cache_commit(tables[l], swaps[l], n_sw[l])
+
+    lg_buf = logits_of(0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        chain.step(lg_buf)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g_step, g_maint = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        chain.step(lg_buf)
+    with torch.cuda.graph(g_maint):
+        maintain()
+    for c in counts:
+        c.zero_()
+    torch.cuda.synchronize()
+    # inputs of every step resident in HBM before timing
+    all_lg = torch.stack([logits_of(st) for st in range(warm_steps + steps)])
+    swaps_done = 0
+
+    def run(first, n, count_swaps=False):
+        nonlocal swaps_done
+        for i in range(first, first + n):
+            lg_buf.copy_(all_lg[i])
+            g_step.replay()
+            if (i + 1) % period == 0:
+                g_maint.replay()
+                if count_swaps:
+                    torch.cuda.synchronize()
+                    swaps_done += sum(int(t[0]) for t in n_sw)
+
+    # the original cache on the new routing, no maintenance (same timed tokens)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(warm_steps, warm_steps + steps):
+        lg_buf.copy_(all_lg[i])
+        g_step.replay()
+    torch.cuda.synchronize()
+    dt_static = time.perf_counter() - t1
+    for c in counts:
+        c.zero_()
+    run(0, warm_steps, count_swaps=True)
+    warm_swaps = swaps_done
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    run(warm_steps, steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t1
+    adapted_hit = hit_rate([t.cpu().numpy() for t in tables], held_out, 16)
+    # reference point: a cache holding the 94 most popular experts of the new order
+    top_tabs = []
+    for l in range(N_LAYERS):
+        tab = np.full(E, -1, np.int32)
+        tab[synth.zipf_popularity(2, l + drift, E)[:94]] = 0
+        top_tabs.append(tab)
+    top_hit = hit_rate(top_tabs, held_out, 16)
+    res = {
+        "workload": f"routing moves to another popularity order; count every token, every "
+                    f"{period} tokens up to {max_swaps} swaps per layer (counts halve), newcomers "
+                    f"copied from the host tier by a kernel; whole layers with misses from the "
+                    f"host tier; timed after {warm_steps} adapting tokens",
+        "hit_rate_before": round(static_hit, 4),
+        "hit_rate_after": round(adapted_hit, 4),
+        "hit_rate_of_the_new_top_94": round(top_hit, 4),
+        "swaps_while_adapting": warm_swaps,
+        "tok_s": round(steps / dt, 2),
+        "ms_per_step": round(dt * 1e3 / steps, 5),
+        "tok_s_without_adapting": round(steps / dt_static, 2),
+    }
+    log(f"adaptive cache: {res} ({time.perf_counter() - t0:.1f} s)")
+    del g_step, g_maint, chain
     return res
 
 

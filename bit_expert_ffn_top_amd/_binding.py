@@ -52,6 +52,11 @@ SIGNATURES = {
                                   _vp, _vp, _c_sz, _vp]),
     "moe_decode_misses": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, _vp,
                                    _c_sz, _vp]),
+    "moe_cache_count": (_c_int, [_vp, _c_int, _c_int, _vp, _vp]),
+    "moe_cache_plan": (_c_int, [_vp, _c_int, _vp, _vp, _c_int, _c_int, _vp, _c_int, _c_int,
+                                _c_int, _vp, _vp, _vp]),
+    "moe_cache_fill": (_c_int, [_LP, _LP, _vp, _vp, _c_int, _vp]),
+    "moe_cache_commit": (_c_int, [_vp, _c_int, _vp, _vp, _c_int, _vp]),
     "moe_prefill_workspace_bytes": (_c_sz, [_LP, _c_int]),
     "moe_expert_ffn_prefill": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _c_sz, _vp]),
@@ -277,6 +282,53 @@ def decode_misses(tier: HostTier, x, idx, slot, w, host_slot_of_expert, y, max_r
                                    _ptr(host_slot_of_expert), r, _ptr(y), _ptr(ws), ws.numel(),
                                    _stream(stream)), "moe_decode_misses")
     return y
+
+
+def cache_count(idx, counts, stream=None):
+    """counts[e] += uses of expert e in idx (moe_cache_count).  counts: int32
+    tensor viewed as uint32 [E]."""
+    _dev(idx, torch.int32, "idx")
+    _dev(counts, torch.int32, "counts")
+    _check(lib().moe_cache_count(_ptr(idx), idx.numel(), counts.numel(), _ptr(counts),
+                                 _stream(stream)), "moe_cache_count")
+    return counts
+
+
+def cache_plan(counts, slot_of_expert, expert_of_slot, shared_slot, host_slot_of_expert,
+               host_n_slots, max_swaps, decay_shift=1, swaps=None, n_swaps=None, stream=None):
+    """Plan up to max_swaps swaps, updating the tables and decaying the
+    counts in place (moe_cache_plan).  Returns (swaps [max_swaps, 4], n_swaps [4])."""
+    for t, name in ((counts, "counts"), (slot_of_expert, "slot_of_expert"),
+                    (expert_of_slot, "expert_of_slot"), (host_slot_of_expert, "host_slot_of_expert")):
+        _dev(t, torch.int32, name)
+    dev = counts.device
+    swaps = torch.full((max_swaps, 4), -1, dtype=torch.int32, device=dev) if swaps is None else swaps
+    n_swaps = torch.zeros((4,), dtype=torch.int32, device=dev) if n_swaps is None else n_swaps
+    _check(lib().moe_cache_plan(_ptr(counts), counts.numel(), _ptr(slot_of_expert),
+                                _ptr(expert_of_slot), expert_of_slot.numel(), shared_slot,
+                                _ptr(host_slot_of_expert), host_n_slots, max_swaps, decay_shift,
+                                _ptr(swaps), _ptr(n_swaps), _stream(stream)), "moe_cache_plan")
+    return swaps, n_swaps
+
+
+def cache_fill(layer: MoeLayer, tier: HostTier, swaps, n_swaps, stream=None):
+    """Copy the planned experts from the host tier into the cache's slots
+    (moe_cache_fill)."""
+    _dev(swaps, torch.int32, "swaps")
+    _dev(n_swaps, torch.int32, "n_swaps")
+    L, H = layer.c_struct(), tier.c_struct()
+    _check(lib().moe_cache_fill(ctypes.byref(L), ctypes.byref(H), _ptr(swaps), _ptr(n_swaps),
+                                swaps.shape[0], _stream(stream)), "moe_cache_fill")
+
+
+def cache_commit(slot_of_expert, swaps, n_swaps, stream=None):
+    """Make the admitted experts visible in the slot table (moe_cache_commit)."""
+    _dev(slot_of_expert, torch.int32, "slot_of_expert")
+    _dev(swaps, torch.int32, "swaps")
+    _dev(n_swaps, torch.int32, "n_swaps")
+    _check(lib().moe_cache_commit(_ptr(slot_of_expert), slot_of_expert.numel(), _ptr(swaps),
+                                  _ptr(n_swaps), swaps.shape[0], _stream(stream)),
+           "moe_cache_commit")
 
 
 def prefill_workspace_bytes(layer: MoeLayer, T: int) -> int:

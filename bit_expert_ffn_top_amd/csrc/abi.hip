@@ -44,6 +44,21 @@ int check_layer(const moe_layer* L) {
   return MOE_OK;
 }
 
+// Device-side address of memory this device can read: pinned host memory
+// (hipHostMalloc) or device memory.  False for anything else (pageable host
+// memory), leaving no HIP error behind.
+bool device_address(const void* p, const void** out) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (!attr.devicePointer || (attr.type != hipMemoryTypeHost && attr.type != hipMemoryTypeDevice))
+    return false;
+  *out = attr.devicePointer;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,19 +186,67 @@ int moe_decode_misses(const moe_layer* H, const float* x, int T, const int32_t* 
   if (ws_bytes < bitffn::decode_workspace_bytes(H->d_model, H->d_ff, T, H->top_k))
     return MOE_ENOSPC;
   // The pool must be memory this device can address: pinned host memory
-  // (its device-side address is used) or device memory.  Pageable host
-  // memory is refused.
-  hipPointerAttribute_t attr;
-  if (hipPointerGetAttributes(&attr, H->pool) != hipSuccess) {
-    (void)hipGetLastError();   // leave no error behind for the next launch check
-    return MOE_EINVAL;
-  }
-  const void* pool_dev = attr.devicePointer;
-  if (!pool_dev || (attr.type != hipMemoryTypeHost && attr.type != hipMemoryTypeDevice))
-    return MOE_EINVAL;
+  // (its device-side address is used) or device memory.
+  const void* pool_dev = nullptr;
+  if (!device_address(H->pool, &pool_dev)) return MOE_EINVAL;
   if (max_rank == 0) return MOE_OK;   // no miss can run
   return hip_status(bitffn::launch_decode_misses(*H, pool_dev, x, T, idx, slot, w,
                                                  host_slot_of_expert, max_rank, y, ws, stream));
+}
+
+int moe_cache_count(const int32_t* idx, int n_pairs, int E, uint32_t* counts,
+                    hipStream_t stream) {
+  if (n_pairs < 0 || n_pairs >= (1 << 24) || E < 1 || E > MOE_MAX_EXPERTS) return MOE_EINVAL;
+  if (n_pairs == 0) return MOE_OK;
+  if (!idx || !counts) return MOE_EINVAL;
+  if (!aligned16(idx) || !aligned16(counts)) return MOE_EALIGN;
+  return hip_status(bitffn::launch_cache_count(idx, n_pairs, E, counts, stream));
+}
+
+int moe_cache_plan(uint32_t* counts, int E, int32_t* slot_of_expert, int32_t* expert_of_slot,
+                   int n_slots, int shared_slot, const int32_t* host_slot_of_expert,
+                   int host_n_slots, int max_swaps, int decay_shift, int32_t* swaps,
+                   int32_t* n_swaps, hipStream_t stream) {
+  if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_EINVAL;
+  if (n_slots < 1 || n_slots > MOE_MAX_CACHE_SLOTS) return MOE_EINVAL;
+  if (shared_slot < -1 || shared_slot >= n_slots || host_n_slots < 0) return MOE_EINVAL;
+  if (max_swaps < 1 || max_swaps > MOE_MAX_EXPERTS || decay_shift < 0 || decay_shift > 31)
+    return MOE_EINVAL;
+  if (!counts || !slot_of_expert || !expert_of_slot || !host_slot_of_expert || !swaps || !n_swaps)
+    return MOE_EINVAL;
+  if (!aligned16(counts) || !aligned16(slot_of_expert) || !aligned16(expert_of_slot) ||
+      !aligned16(host_slot_of_expert) || !aligned16(swaps) || !aligned16(n_swaps))
+    return MOE_EALIGN;
+  return hip_status(bitffn::launch_cache_plan(counts, E, slot_of_expert, expert_of_slot, n_slots,
+                                              shared_slot, host_slot_of_expert, host_n_slots,
+                                              max_swaps, decay_shift, swaps, n_swaps, stream));
+}
+
+int moe_cache_fill(const moe_layer* L, const moe_layer* H, const int32_t* swaps,
+                   const int32_t* n_swaps, int max_swaps, hipStream_t stream) {
+  int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  st = check_layer(H);
+  if (st != MOE_OK) return st;
+  if (L->fmt != H->fmt || L->d_model != H->d_model || L->d_ff != H->d_ff) return MOE_EFORMAT;
+  if (max_swaps < 1 || max_swaps > MOE_MAX_EXPERTS) return MOE_EINVAL;
+  if (!swaps || !n_swaps) return MOE_EINVAL;
+  if (!aligned16(swaps) || !aligned16(n_swaps)) return MOE_EALIGN;
+  const void* host_dev = nullptr;
+  if (!device_address(H->pool, &host_dev)) return MOE_EINVAL;
+  return hip_status(bitffn::launch_cache_fill(host_dev, H->n_slots, const_cast<void*>(L->pool),
+                                              L->n_slots, L->slot_bytes, swaps, n_swaps,
+                                              max_swaps, stream));
+}
+
+int moe_cache_commit(int32_t* slot_of_expert, int E, const int32_t* swaps,
+                     const int32_t* n_swaps, int max_swaps, hipStream_t stream) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || max_swaps < 1 || max_swaps > MOE_MAX_EXPERTS)
+    return MOE_EINVAL;
+  if (!slot_of_expert || !swaps || !n_swaps) return MOE_EINVAL;
+  if (!aligned16(slot_of_expert) || !aligned16(swaps) || !aligned16(n_swaps)) return MOE_EALIGN;
+  return hip_status(bitffn::launch_cache_commit(slot_of_expert, E, swaps, n_swaps, max_swaps,
+                                                stream));
 }
 
 size_t moe_prefill_workspace_bytes(const moe_layer* L, int T) {

@@ -66,6 +66,19 @@ hipError_t launch_decode_misses(const moe_layer& H, const void* host_pool_dev, c
                                 const int32_t* host_slot_of_expert, int max_rank, float* y,
                                 void* ws, hipStream_t s);
 
+// Expert-cache admission and eviction (cache_policy.hip).
+hipError_t launch_cache_count(const int32_t* idx, int n, int E, uint32_t* counts,
+                              hipStream_t s);
+hipError_t launch_cache_plan(uint32_t* counts, int E, int32_t* slot_of_expert,
+                             int32_t* expert_of_slot, int n_slots, int shared_slot,
+                             const int32_t* host_slot, int host_n_slots, int max_swaps,
+                             int decay_shift, int32_t* swaps, int32_t* n_swaps, hipStream_t s);
+hipError_t launch_cache_fill(const void* host_pool_dev, int host_n_slots, void* pool,
+                             int n_slots, int64_t slot_bytes, const int32_t* swaps,
+                             const int32_t* n_swaps, int max_swaps, hipStream_t s);
+hipError_t launch_cache_commit(int32_t* slot_of_expert, int E, const int32_t* swaps,
+                               const int32_t* n_swaps, int max_swaps, hipStream_t s);
+
 size_t prefill_workspace_bytes(int d, int f, int T, int k, int E);
 hipError_t launch_prefill(const moe_layer& L, const uint16_t* x_bf16, int T,
                           const int32_t* idx, const int32_t* slot, float* out_pairs,

@@ -92,6 +92,7 @@ extern "C" {
 #define MOE_MAX_TOPK 64
 #define MOE_MAX_DECODE_T 4
 #define MOE_MAX_DECODE_PAIRS 64
+#define MOE_MAX_CACHE_SLOTS 4096
 
 /* One MoE layer as it sits in device memory (host struct, read during the
  * call only). */
@@ -232,6 +233,69 @@ int moe_decode_misses(const moe_layer* H, const float* x, int T,
                       const int32_t* idx, const int32_t* slot, const float* w,
                       const int32_t* host_slot_of_expert, int max_rank,
                       float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert-cache admission and eviction.  The cache starts from a table of
+ * usage frequencies and is updated as the conversation moves on ("FreeToken
+ * vs Strata", comparison table, row "VRAMのエキスパートの入れ替え";
+ * vramglass.com page, "その1"; "Strata" page, "GPU・CPU・RAM・SSDの分担").
+ * The pages give no rule; these four calls implement one:
+ *   moe_cache_count   after each routing, count the uses of every expert;
+ *   moe_cache_plan    pick the swaps (best missing experts for the worst
+ *                     slots), evict at once, decay the counts;
+ *   moe_cache_fill    copy the admitted experts' bytes from the host tier
+ *                     into their slots (may run on another stream);
+ *   moe_cache_commit  make the admitted experts visible in the slot table.
+ * Between plan and commit an admitted expert is still a miss, so decode
+ * calls on the compute stream stay correct while the fill runs elsewhere;
+ * the fill must not start before the work that read the evicted slots is
+ * done, and the commit must follow the fill (events or one stream).
+ * All four are kernels: nothing waits on the host, so they can be captured
+ * in a graph. */
+
+/* counts uint32 [E] += the number of times each expert appears in idx int32
+ * [n_pairs] (ids outside [0, E) are ignored).  Counts wrap at 2^32.
+ * Limits: 0 <= n_pairs < 2^24, 1 <= E <= MOE_MAX_EXPERTS. */
+int moe_cache_count(const int32_t* idx, int n_pairs, int E, uint32_t* counts,
+                    hipStream_t stream);
+
+/* Plan up to max_swaps swaps.  slot_of_expert int32 [E] (slot or -1) and
+ * expert_of_slot int32 [n_slots] (expert id, -1 = empty, the shared slot
+ * holding anything) describe the cache and are updated in place; slot
+ * shared_slot (-1 = none) is never touched.  host_slot_of_expert int32 [E]:
+ * slot of each expert in the host tier (outside [0, host_n_slots) = none).
+ *   candidates: experts with slot_of_expert < 0, a host slot and a count
+ *     above 0, ranked by (count descending, id ascending);
+ *   victims: slots other than shared_slot, ranked by (count of the expert
+ *     held ascending, an empty slot or an id outside [0, E) counting as -1;
+ *     then slot ascending);
+ *   swap i (i = 0, 1, ...) puts candidate i into victim slot i while
+ *     i < max_swaps and the candidate's count is strictly larger.
+ * For each swap: slot_of_expert[old] = -1, expert_of_slot[slot] = new;
+ * swaps int32 [max_swaps][4] receives (slot, old expert or -1, new expert,
+ * its host slot) and n_swaps int32 [1] the number of swaps.  Then every
+ * count becomes count >> decay_shift.  The newcomers stay out of
+ * slot_of_expert until moe_cache_commit.
+ * Limits: 1 <= E <= MOE_MAX_EXPERTS, 1 <= n_slots <= MOE_MAX_CACHE_SLOTS,
+ * 1 <= max_swaps <= MOE_MAX_EXPERTS, 0 <= decay_shift <= 31.  One
+ * workgroup; the result is unique (every ranking is total). */
+int moe_cache_plan(uint32_t* counts, int E, int32_t* slot_of_expert,
+                   int32_t* expert_of_slot, int n_slots, int shared_slot,
+                   const int32_t* host_slot_of_expert, int host_n_slots,
+                   int max_swaps, int decay_shift, int32_t* swaps,
+                   int32_t* n_swaps, hipStream_t stream);
+
+/* Copy the planned experts: for i < n_swaps, slot swaps[4i] of L's pool
+ * receives the slot_bytes of slot swaps[4i+3] of H's pool.  L is the GPU
+ * cache (its pool is written); H the host tier (pinned host memory this
+ * device can address, or device memory; pageable memory gives MOE_EINVAL).
+ * Both must have the same fmt, d_model and d_ff.  Entries whose slots lie
+ * outside either pool are skipped.  max_swaps: as given to the plan. */
+int moe_cache_fill(const moe_layer* L, const moe_layer* H, const int32_t* swaps,
+                   const int32_t* n_swaps, int max_swaps, hipStream_t stream);
+
+/* slot_of_expert[swaps[4i+2]] = swaps[4i] for i < min(n_swaps, max_swaps). */
+int moe_cache_commit(int32_t* slot_of_expert, int E, const int32_t* swaps,
+                     const int32_t* n_swaps, int max_swaps, hipStream_t stream);
 
 /* (host) Workspace bytes that moe_expert_ffn_prefill needs for T tokens. */
 size_t moe_prefill_workspace_bytes(const moe_layer* L, int T);

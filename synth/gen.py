@@ -285,6 +285,11 @@ def _zipf_perm(cfg: int, layer: int, E: int) -> np.ndarray:
     return rng.permutation(E)  # perm[r] = expert holding popularity rank r+1
 
 
+def zipf_popularity(cfg: int, layer: int, E: int) -> np.ndarray:
+    """Expert ids by popularity, most used first, as zipf_gumbel_logits draws them."""
+    return _zipf_perm(cfg, layer, E).copy()
+
+
 def zipf_gumbel_logits(cfg: int, layer: int, T: int, E: int, s: float,
                        device="cpu", step: int = 0) -> torch.Tensor:
     """logit_e = -s*ln(rank(e)) + Gumbel(0,1): the top-k of these is a draw of

@@ -155,3 +155,57 @@ def test_combine_host_checks():
     assert lib.moe_combine(_p(), 1, 1, 64, 4, _p(), _p(), _p(), None, _p(), s) == -1   # bf16 alias
     assert lib.moe_combine(_p(4), 0, 1, 64, 4, _p(), _p(), _p(), None, _p(1 << 12), s) == -2
     assert lib.moe_combine(None, 0, 0, 64, 4, None, None, None, None, None, s) == 0
+
+
+def test_decode_misses_host_checks():
+    lib = _lib()
+    s = ctypes.c_void_p(0)
+    H = _layer(shared_slot=-1, n_slots=512)
+    need = lib.moe_decode_workspace_bytes(ctypes.byref(H), 1)
+    def call(H, T=1, max_rank=10, ws=need, y=_p(1 << 20)):
+        return lib.moe_decode_misses(ctypes.byref(H), _p(), T, _p(), _p(), _p(), _p(), max_rank,
+                                     y, _p(), ws, s)
+    assert call(_layer(shared_slot=3, n_slots=512)) == -1                   # shared slot in the tier
+    assert call(H, max_rank=11) == -1
+    assert call(H, max_rank=-1) == -1
+    assert call(H, T=5) == -1
+    assert call(H, ws=need - 1) == -4
+    assert call(H, y=_p()) == -1                                            # y aliases x
+    assert call(_layer(shared_slot=-1, fmt=9)) == -3
+
+
+def test_cache_policy_host_checks():
+    lib = _lib()
+    s = ctypes.c_void_p(0)
+    assert lib.moe_cache_count(_p(), 10, 0, _p(), s) == -1
+    assert lib.moe_cache_count(_p(), 10, 2000, _p(), s) == -1
+    assert lib.moe_cache_count(_p(), -1, 512, _p(), s) == -1
+    assert lib.moe_cache_count(None, 0, 512, None, s) == 0                  # nothing to count
+    assert lib.moe_cache_count(_p(4), 10, 512, _p(), s) == -2
+
+    def plan(E=512, n_slots=95, shared=94, max_swaps=8, shift=1, **kw):
+        a = dict(counts=_p(), soe=_p(), eos=_p(), hs=_p(), swaps=_p(), n=_p())
+        a.update(kw)
+        return lib.moe_cache_plan(a["counts"], E, a["soe"], a["eos"], n_slots, shared, a["hs"],
+                                  512, max_swaps, shift, a["swaps"], a["n"], s)
+    assert plan(E=0) == -1
+    assert plan(n_slots=0) == -1
+    assert plan(n_slots=5000) == -1
+    assert plan(shared=95) == -1
+    assert plan(max_swaps=0) == -1
+    assert plan(max_swaps=1025) == -1
+    assert plan(shift=32) == -1
+    assert plan(hs=None) == -1
+    assert plan(swaps=_p(8)) == -2
+
+    L = _layer()
+    H = _layer(n_slots=512, shared_slot=-1)
+    fill = lambda L, H, m=8, sw=_p(): lib.moe_cache_fill(ctypes.byref(L), ctypes.byref(H), sw, _p(),
+                                                         m, s)
+    assert fill(L, _layer(fmt=1, slot_bytes=synth.slot_bytes(1, 2048, 768))) == -3
+    assert fill(L, H, m=0) == -1
+    assert fill(L, H, sw=_p(4)) == -2
+    assert fill(L, _layer(pool=FAKE + 16)) == -2
+    assert lib.moe_cache_commit(_p(), 0, _p(), _p(), 8, s) == -1
+    assert lib.moe_cache_commit(_p(), 512, _p(), _p(), 0, s) == -1
+    assert lib.moe_cache_commit(_p(), 512, None, _p(), 8, s) == -1
