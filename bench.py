@@ -326,9 +326,16 @@ def run_extras(torch, np, bf, synth, pools, dev, args):
     }
     log(f"expert cache: {steps2 / dt:.1f} tok/s, hit rate {hits / tot:.3f} ({time.perf_counter() - t0:.1f} s)")
     del chain2
+    tiers, host_table = build_host_tiers(torch, bf, synth, shape, dev)
+    xs2 = [synth.make_x(2, l, 1, d, device=dev) for l in range(N_LAYERS)]
     out["expert_cache"].update(run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev,
-                                             steps2, n_graphs, tot - hits))
-    del pools2, logits2
+                                             steps2, n_graphs, tot - hits, tiers, host_table,
+                                             xs2))
+    out["prefill_streamed"] = run_prefill_streamed(torch, np, bf, synth, pools2, tiers, dev)
+    torch.cuda.empty_cache()
+    out["expert_cache"]["adaptive"] = run_adaptive_cache(torch, np, bf, synth, shape, pools2,
+                                                         tiers, host_table, xs2, dev)
+    del pools2, logits2, tiers
     torch.cuda.empty_cache()
 
     # ---------------- verify step ----------------
@@ -376,12 +383,9 @@ def run_extras(torch, np, bf, synth, pools, dev, args):
     return out
 
 
-def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_graphs, n_missed):
-    """The expert-cache workload as whole layers: after each layer's GPU
-    part, moe_decode_misses reads the missed experts from a pinned host copy
-    of that layer (all 512 experts) and joins them into y.  Timed with every
-    miss run and with misses of rank >= 5 left out; the change that leaving
-    them out makes to the layers' updates is reported too."""
+def build_host_tiers(torch, bf, synth, shape, dev):
+    """A pinned host copy of all 512 experts of each expert-cache layer, host
+    slot = expert id."""
     E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
     t0 = time.perf_counter()
     sb = synth.slot_bytes(synth.FMT_Q2SM, d, f)
@@ -397,7 +401,19 @@ def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_gr
     torch.cuda.synchronize()
     log(f"host tiers: {N_LAYERS} x {E} experts pinned ({N_LAYERS * E * sb / 1e9:.1f} GB) "
         f"in {time.perf_counter() - t0:.1f} s")
-    xs = [synth.make_x(2, l, 1, d, device=dev) for l in range(N_LAYERS)]
+    return tiers, host_table
+
+
+def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_graphs, n_missed,
+                  tiers, host_table, xs):
+    """The expert-cache workload as whole layers: after each layer's GPU
+    part, moe_decode_misses reads the missed experts from a pinned host copy
+    of that layer (all 512 experts) and joins them into y.  Timed with every
+    miss run and with misses of rank >= 5 left out; the change that leaving
+    them out makes to the layers' updates is reported too."""
+    E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
+    t0 = time.perf_counter()
+    sb = synth.slot_bytes(synth.FMT_Q2SM, d, f)
     res = {}
     misses_per_token = n_missed / n_graphs
     for name, r in (("full_layer", None), ("rank_limit_5", 5)):
@@ -434,9 +450,95 @@ def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_gr
                         "per layer after the GPU part, in the same graph")
     log(f"host tier: {res} ({time.perf_counter() - t0:.1f} s)")
     del chain, chain_full
-    res["adaptive"] = run_adaptive_cache(torch, np, bf, synth, shape, pools2, tiers, host_table,
-                                         xs, dev)
-    del tiers
+    return res
+
+
+def run_prefill_streamed(torch, np, bf, synth, pools2, tiers, dev):
+    """Prefill chunks of 8,192 tokens through 48 layers whose GPU cache
+    holds 94 of 512 experts: each layer is staged (moe_stage_layer: resident
+    experts copied device to device, the other 418 host to device) into one
+    of two staging pools on a copy stream, while the previous layer's
+    prefill runs on the compute stream."""
+    shape = synth.config_shape(4)
+    E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
+    T = synth.WORKLOADS[4]["T"]
+    sb = synth.slot_bytes(synth.FMT_Q2SM, d, f)
+    t0 = time.perf_counter()
+    caches = [bf.MoeLayer(d, f, E, k, fmt, pool, shared_slot) for pool, _, shared_slot, fmt in pools2]
+    tabs = [t.cpu().numpy() for _, t, _, _ in pools2]
+    host_slot = np.arange(E, dtype=np.int32)
+    n_res = [int((t >= 0).sum()) for t in tabs]
+    h2d = sum((E - r) * sb for r in n_res)
+    xs = [synth.make_x(4, l, T, d, device=dev, dtype=torch.bfloat16) for l in range(N_LAYERS)]
+    logits = [synth.make_logits(4, l, T, E, 1.5, device=dev) for l in range(N_LAYERS)]
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    slot = torch.empty((T, k), dtype=torch.int32, device=dev)
+    me = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    n_miss = torch.empty((4,), dtype=torch.int32, device=dev)
+    lws = torch.empty((max(bf.lookup_workspace_bytes(T, k, E), 256),), dtype=torch.uint8, device=dev)
+    out_pairs = torch.empty((T * k, d), dtype=torch.float32, device=dev)
+    pair_pos = torch.empty((T, k), dtype=torch.int32, device=dev)
+    offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    out_sh = torch.empty((T, d), dtype=torch.float32, device=dev)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+    staging = [torch.empty((E + 1, sb), dtype=torch.uint8, device=dev) for _ in range(2)]
+    staged = [bf.MoeLayer(d, f, E, k, synth.FMT_Q2SM, st, E) for st in staging]
+    pws = torch.empty((bf.prefill_workspace_bytes(staged[0], T),), dtype=torch.uint8, device=dev)
+    ident = torch.arange(E, dtype=torch.int32, device=dev)
+    up = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+
+    def one_step(stage=True, compute=True):
+        ev_up = [torch.cuda.Event() for _ in range(N_LAYERS)]
+        ev_done = [torch.cuda.Event() for _ in range(N_LAYERS)]
+        up.wait_stream(comp)
+        for l in range(N_LAYERS):
+            if stage:
+                with torch.cuda.stream(up):
+                    if l >= 2 and compute:
+                        up.wait_event(ev_done[l - 2])
+                    bf.stage_layer(caches[l], tabs[l], tiers[l], host_slot, staging[l % 2],
+                                   stream=up)
+                    ev_up[l].record(up)
+                if compute:
+                    comp.wait_event(ev_up[l])
+            if compute:
+                bf.route_topk(logits[l], k, idx=idx, w=w)
+                bf.cache_lookup(idx, ident, slot=slot, miss_expert=me, n_miss=n_miss, ws=lws,
+                                want_pairs=False)
+                bf.expert_ffn_prefill(staged[l % 2], xs[l], idx, slot, out_pairs=out_pairs,
+                                      pair_pos=pair_pos, expert_offsets=offs, out_shared=out_sh,
+                                      ws=pws)
+                bf.combine(xs[l], out_pairs, pair_pos, w, out_sh, y=y)
+                ev_done[l].record(comp)
+        comp.wait_stream(up)
+
+    def timed(**kw):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        one_step(**kw)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t1
+
+    one_step()                                    # warm-up
+    dt = timed()
+    dt_stage = timed(compute=False)
+    dt_compute = timed(stage=False)               # on whatever the staging pools hold
+    res = {
+        "workload": "prefill chunk: 8,192 bf16 tokens through 48 layers of the expert-cache "
+                    "shape (94 of 512 experts + shared resident per layer, the rest in pinned "
+                    "host memory); each layer staged into one of two pools on a copy stream "
+                    "while the previous layer computes",
+        "tok_s": round(T / dt, 1),
+        "ms_per_layer": round(dt * 1e3 / N_LAYERS, 3),
+        "staging_only_ms_per_layer": round(dt_stage * 1e3 / N_LAYERS, 3),
+        "compute_only_ms_per_layer": round(dt_compute * 1e3 / N_LAYERS, 3),
+        "host_to_device_GB_per_layer": round(h2d / N_LAYERS / 1e9, 3),
+        "host_to_device_GBps": round(h2d / dt / 1e9, 1),
+        "overlap": round(max(dt_stage, dt_compute) / dt, 3),
+    }
+    log(f"prefill streamed: {res} ({time.perf_counter() - t0:.1f} s)")
     return res
 
 

@@ -57,6 +57,7 @@ SIGNATURES = {
                                 _c_int, _vp, _vp, _vp]),
     "moe_cache_fill": (_c_int, [_LP, _LP, _vp, _vp, _c_int, _vp]),
     "moe_cache_commit": (_c_int, [_vp, _c_int, _vp, _vp, _c_int, _vp]),
+    "moe_stage_layer": (_c_int, [_LP, _vp, _LP, _vp, _vp, _c_sz, _vp]),
     "moe_prefill_workspace_bytes": (_c_sz, [_LP, _c_int]),
     "moe_expert_ffn_prefill": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _c_sz, _vp]),
@@ -329,6 +330,24 @@ def cache_commit(slot_of_expert, swaps, n_swaps, stream=None):
     _check(lib().moe_cache_commit(_ptr(slot_of_expert), slot_of_expert.numel(), _ptr(swaps),
                                   _ptr(n_swaps), swaps.shape[0], _stream(stream)),
            "moe_cache_commit")
+
+
+def stage_layer(cache: MoeLayer, slot_of_expert, tier: HostTier, host_slot_of_expert, staging,
+                stream=None):
+    """Copy every expert of the layer into `staging` in expert order
+    (moe_stage_layer).  slot_of_expert / host_slot_of_expert: host int32
+    arrays [n_experts]; staging: device uint8 [(n_experts + 1), slot_bytes].
+    Returns the MoeLayer that reads the staged pool."""
+    import numpy as np
+    soe = np.ascontiguousarray(np.asarray(slot_of_expert, dtype=np.int32))
+    hs = np.ascontiguousarray(np.asarray(host_slot_of_expert, dtype=np.int32))
+    _dev(staging, torch.uint8, "staging")
+    C, H = cache.c_struct(), tier.c_struct()
+    _check(lib().moe_stage_layer(ctypes.byref(C), soe.ctypes.data, ctypes.byref(H), hs.ctypes.data,
+                                 _ptr(staging), staging.numel(), _stream(stream)),
+           "moe_stage_layer")
+    return MoeLayer(cache.d_model, cache.d_ff, cache.n_experts, cache.top_k, cache.fmt, staging,
+                    cache.n_experts if cache.shared_slot >= 0 else -1)
 
 
 def prefill_workspace_bytes(layer: MoeLayer, T: int) -> int:

@@ -249,6 +249,32 @@ int moe_cache_commit(int32_t* slot_of_expert, int E, const int32_t* swaps,
                                                 stream));
 }
 
+int moe_stage_layer(const moe_layer* C, const int32_t* slot_of_expert, const moe_layer* H,
+                    const int32_t* host_slot_of_expert, void* staging, size_t staging_bytes,
+                    hipStream_t stream) {
+  int st = check_layer(C);
+  if (st != MOE_OK) return st;
+  st = check_layer(H);
+  if (st != MOE_OK) return st;
+  if (C->fmt != H->fmt || C->d_model != H->d_model || C->d_ff != H->d_ff) return MOE_EFORMAT;
+  if (C->n_experts != H->n_experts) return MOE_EINVAL;
+  if (!slot_of_expert || !host_slot_of_expert || !staging) return MOE_EINVAL;
+  if (!aligned256(staging)) return MOE_EALIGN;
+  const int E = C->n_experts;
+  if (staging_bytes < static_cast<size_t>(E + 1) * static_cast<size_t>(C->slot_bytes))
+    return MOE_ENOSPC;
+  for (int e = 0; e < E; ++e) {   // every expert needs a source
+    const int cs = slot_of_expert[e], hs = host_slot_of_expert[e];
+    const bool in_cache = cs >= 0 && cs < C->n_slots && cs != C->shared_slot;
+    const bool in_host = hs >= 0 && hs < H->n_slots;
+    if (!in_cache && (cs >= 0 || !in_host)) return MOE_EINVAL;
+  }
+  const void* host_dev = nullptr;
+  if (!device_address(H->pool, &host_dev)) return MOE_EINVAL;
+  return hip_status(bitffn::launch_stage_layer(*C, slot_of_expert, H->pool, host_slot_of_expert,
+                                               staging, stream));
+}
+
 size_t moe_prefill_workspace_bytes(const moe_layer* L, int T) {
   if (check_layer(L) != MOE_OK || T < 1 || T > 65536) return 0;
   return bitffn::prefill_workspace_bytes(L->d_model, L->d_ff, T, L->top_k, L->n_experts);

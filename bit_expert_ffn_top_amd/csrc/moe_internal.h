@@ -79,6 +79,13 @@ hipError_t launch_cache_fill(const void* host_pool_dev, int host_n_slots, void* 
 hipError_t launch_cache_commit(int32_t* slot_of_expert, int E, const int32_t* swaps,
                                const int32_t* n_swaps, int max_swaps, hipStream_t s);
 
+// Copies of a whole layer into a staging pool in expert order (stage.hip).
+// slot_of_expert and host_slot_of_expert are host arrays; every expert has a
+// source (checked by the caller).
+hipError_t launch_stage_layer(const moe_layer& C, const int32_t* slot_of_expert,
+                              const void* host_pool, const int32_t* host_slot_of_expert,
+                              void* staging, hipStream_t s);
+
 size_t prefill_workspace_bytes(int d, int f, int T, int k, int E);
 hipError_t launch_prefill(const moe_layer& L, const uint16_t* x_bf16, int T,
                           const int32_t* idx, const int32_t* slot, float* out_pairs,

@@ -297,6 +297,32 @@ int moe_cache_fill(const moe_layer* L, const moe_layer* H, const int32_t* swaps,
 int moe_cache_commit(int32_t* slot_of_expert, int E, const int32_t* swaps,
                      const int32_t* n_swaps, int max_swaps, hipStream_t stream);
 
+/* Stage a whole layer for a prefill chunk ("Strata" page,
+ * "GPU・CPU・RAM・SSDの分担": long inputs are processed 8,192 tokens at a
+ * time while the next layer's experts travel to the GPU over PCIe).
+ * Copies every expert's packed slot into `staging` in expert order: slot e
+ * holds expert e (e < n_experts), slot n_experts the shared expert of C (if
+ * C->shared_slot >= 0).  Resident experts (slot_of_expert[e] in C's pool)
+ * are copied device to device, the others from H's pool at
+ * host_slot_of_expert[e].  Copies go through the DMA engines
+ * (hipMemcpyAsync on `stream`), consecutive source slots merged, so on a
+ * stream of their own they overlap the compute kernels of the previous
+ * layer.  Then moe_expert_ffn_prefill runs on a layer whose pool is
+ * `staging` (n_slots = n_experts + 1, shared_slot = n_experts) with the
+ * identity slot table, and gives the same bits as with the experts in any
+ * other slots.
+ *   C: the GPU cache of the layer; H: its host tier (pinned host memory or
+ *   device memory; same fmt, d_model, d_ff, n_experts).
+ *   slot_of_expert, host_slot_of_expert: (host) int32 [n_experts]; every
+ *   expert must be resident in C (not in the shared slot) or have a host
+ *   slot in H, else MOE_EINVAL and nothing is copied.
+ *   staging: device memory of at least (n_experts + 1) * slot_bytes bytes,
+ *   256-byte aligned.  The caller orders the copies after the last kernel
+ *   that read `staging` and before the prefill that reads it. */
+int moe_stage_layer(const moe_layer* C, const int32_t* slot_of_expert,
+                    const moe_layer* H, const int32_t* host_slot_of_expert,
+                    void* staging, size_t staging_bytes, hipStream_t stream);
+
 /* (host) Workspace bytes that moe_expert_ffn_prefill needs for T tokens. */
 size_t moe_prefill_workspace_bytes(const moe_layer* L, int T);
 

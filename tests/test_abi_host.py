@@ -209,3 +209,32 @@ def test_cache_policy_host_checks():
     assert lib.moe_cache_commit(_p(), 0, _p(), _p(), 8, s) == -1
     assert lib.moe_cache_commit(_p(), 512, _p(), _p(), 0, s) == -1
     assert lib.moe_cache_commit(_p(), 512, None, _p(), 8, s) == -1
+
+
+def test_stage_layer_host_checks():
+    lib = _lib()
+    s = ctypes.c_void_p(0)
+    import numpy as np
+    E = 512
+    C = _layer(n_slots=95, shared_slot=94)
+    H = _layer(n_slots=512, shared_slot=-1)
+    soe = np.full(E, -1, np.int32)
+    soe[:94] = np.arange(94)
+    hs = np.arange(E, dtype=np.int32)
+    sb = synth.slot_bytes(2, 2048, 768)
+    def call(C=C, H=H, soe=soe, hs=hs, nbytes=(E + 1) * sb, st=_p()):
+        return lib.moe_stage_layer(ctypes.byref(C), soe.ctypes.data, ctypes.byref(H),
+                                   hs.ctypes.data, st, nbytes, s)
+    assert call(nbytes=E * sb) == -4
+    assert call(st=_p(16)) == -2
+    assert call(H=_layer(n_slots=512, shared_slot=-1, n_experts=500)) == -1
+    assert call(H=_layer(fmt=1, slot_bytes=synth.slot_bytes(1, 2048, 768))) == -3
+    bad = hs.copy()
+    bad[200] = -1                                     # expert 200: neither tier
+    assert call(hs=bad) == -1
+    bad = hs.copy()
+    bad[200] = 512                                    # host slot out of range
+    assert call(hs=bad) == -1
+    bad = soe.copy()
+    bad[300] = 94                                     # the shared slot is no expert's home
+    assert call(soe=bad, hs=np.where(np.arange(E) == 300, -1, hs).astype(np.int32)) == -1
