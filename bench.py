@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=2)
+    ap.add_argument("--cache-only", action="store_true",
+                    help="run only the expert-cache workloads (host tier, staged prefill, "
+                         "adaptive cache; for profiling); prints their object")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill workload (for profiling); prints its object")
     ap.add_argument("--counters", action="store_true",
@@ -218,6 +221,11 @@ def main():
     dev = torch.device("cuda:0")
     shape = synth.config_shape(1)
     E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
+    if args.cache_only:
+        print(json.dumps(run_extras(torch, np, bf, synth, None, dev, args, cache_only=True)),
+              flush=True)
+        return
+
     t_gen = time.perf_counter()
     pools = build_pools(torch, synth, 1, lambda l: synth.FMT_Q2SM, dev)
     torch.cuda.synchronize()
@@ -294,7 +302,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def run_extras(torch, np, bf, synth, pools, dev, args):
+def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
     out = {}
     shape = synth.config_shape(1)
     E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
@@ -337,6 +345,8 @@ def run_extras(torch, np, bf, synth, pools, dev, args):
                                                          tiers, host_table, xs2, dev)
     del pools2, logits2, tiers
     torch.cuda.empty_cache()
+    if cache_only:
+        return out
 
     # ---------------- verify step ----------------
     t0 = time.perf_counter()
