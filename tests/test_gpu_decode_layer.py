@@ -128,3 +128,48 @@ def test_decode_layer_ties_nan_and_empty_cache():
     none = np.full(shape.n_experts, -1, np.int32)
     _, slot = _compare(L, x, lg.to(dev), table=none)
     assert (slot < 0).all()
+
+
+def test_decode_layer_workspace_reuse():
+    """One workspace through many calls of different T, each call bitwise
+    equal to the three separate calls; graph replays equal the eager call."""
+    import bit_expert_ffn_top_amd as bf
+    dev = need_gpu()
+    shape = synth.LayerShape(200, 8, 512, 256, True)
+    L = GpuLayer(0, 12, shape, synth.FMT_Q2SM, dev)
+    tab = L.table_dev(dev)
+    k = shape.top_k
+    ws = torch.empty((bf.decode_workspace_bytes(L.layer_obj, 4),), dtype=torch.uint8, device=dev)
+    for step, T in enumerate((4, 1, 3, 1, 4, 2)):
+        x = synth.make_x(0, 12, T, shape.d_model, step=step).to(dev)
+        logits = synth.make_logits(0, 12, T, shape.n_experts, 1.0, step=step).to(dev)
+        y, *_ = bf.decode_layer(L.layer_obj, x, logits, tab, ws=ws)
+        ry, *_ = _separate(L, x, logits, k, tab, dev)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ry), (step, T)
+    # captured: replays equal the eager call
+    T = 2
+    x = synth.make_x(0, 12, T, shape.d_model, step=9).to(dev)
+    logits = synth.make_logits(0, 12, T, shape.n_experts, 1.0, step=9).to(dev)
+    out = dict(idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+               w=torch.empty((T, k), dtype=torch.float32, device=dev),
+               slot=torch.empty((T, k), dtype=torch.int32, device=dev),
+               miss_expert=torch.empty((T * k,), dtype=torch.int32, device=dev),
+               miss_pair=torch.empty((T * k,), dtype=torch.int32, device=dev),
+               n_miss=torch.empty((4,), dtype=torch.int32, device=dev),
+               y=torch.empty((T, shape.d_model), dtype=torch.float32, device=dev))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bf.decode_layer(L.layer_obj, x, logits, tab, ws=ws, **out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = out["y"].clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bf.decode_layer(L.layer_obj, x, logits, tab, ws=ws, **out)
+    for _ in range(3):
+        out["y"].fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out["y"], eager)
