@@ -2,11 +2,19 @@
 //   y[t] = x[t] + sum_i w[t,i] * rows[pair_pos[t,i]] + shared[t]
 // One thread per 4 consecutive columns of one token; the k terms are added in
 // i order with fused multiply-adds, the shared row last.  A missed pair
-// (pair_pos < 0) contributes nothing.
+// (pair_pos < 0) contributes nothing.  The pair rows are read once and y is
+// written once, both with nontemporal accesses (streamed past the caches).
 #include "moe_internal.h"
 
 namespace bitffn {
 namespace {
+
+typedef float nf4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const nf4 v = __builtin_nontemporal_load(reinterpret_cast<const nf4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 
 template <bool XBF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ x, int T, int d,
@@ -36,7 +44,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ x
   // then all its row loads (a missed pair re-reads a row of the batch that is
   // present, so that every load is unconditional and in bounds, and is
   // skipped), then the fused multiply-adds in i order
-  constexpr int KC = 16;
+  constexpr int KC = 10;
   for (int i0 = 0; i0 < k; i0 += KC) {
     int p[KC];
     float wi[KC];
@@ -54,7 +62,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ x
     if (any < 0) continue;   // the token's whole batch missed (uniform per wavefront)
 #pragma unroll
     for (int j = 0; j < KC; ++j)
-      r[j] = *reinterpret_cast<const float4*>(rows + static_cast<int64_t>(p[j] >= 0 ? p[j] : any) * d + c);
+      r[j] = load_stream(rows + static_cast<int64_t>(p[j] >= 0 ? p[j] : any) * d + c);
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
       if (p[j] >= 0) {
@@ -72,7 +80,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ x
     acc.z += r.z;
     acc.w += r.w;
   }
-  *reinterpret_cast<float4*>(y + static_cast<int64_t>(t) * d + c) = acc;
+  const nf4 out = {acc.x, acc.y, acc.z, acc.w};
+  __builtin_nontemporal_store(out, reinterpret_cast<nf4*>(y + static_cast<int64_t>(t) * d + c));
 }
 
 }  // namespace

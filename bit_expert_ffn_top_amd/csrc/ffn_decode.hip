@@ -29,6 +29,26 @@
 namespace bitffn {
 namespace {
 
+// Expert weights are streamed once per call: nontemporal loads keep them out
+// of the caches that x, the logits and the slot table are read through.
+typedef uint32_t nu4 __attribute__((ext_vector_type(4)));
+typedef uint32_t nu2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 stream_u4(const uint8_t* p) {
+  const nu4 v = __builtin_nontemporal_load(reinterpret_cast<const nu4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 stream_u2(const uint8_t* p) {
+  const nu2 v = __builtin_nontemporal_load(reinterpret_cast<const nu2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t stream_u32(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ uint32_t stream_u16(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+}
+
 // x is read-only for the whole kernel: reading it through the constant address
 // space lets its wavefront-uniform loads become scalar loads.
 typedef const __attribute__((address_space(4))) float cfloat;
@@ -220,10 +240,10 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
 #pragma unroll
   for (int i = 0; i < UPW; ++i) {
     const int64_t unit = static_cast<int64_t>(min(wave + KA_WAVES * i, nu - 1)) * R + grow;
-    gc[i] = *reinterpret_cast<const uint4*>(base + a.G.codes + unit * 16);
-    gs[i] = *reinterpret_cast<const uint32_t*>(base + a.G.scale + unit * 4);
-    if (FMT == MOE_FMT_Q2SM) gm[i] = *reinterpret_cast<const uint32_t*>(base + a.G.min + unit * 4);
-    if (FMT == MOE_FMT_Q3G) gh[i] = *reinterpret_cast<const uint2*>(base + a.G.hi + unit * 8);
+    gc[i] = stream_u4(base + a.G.codes + unit * 16);
+    gs[i] = stream_u32(base + a.G.scale + unit * 4);
+    if (FMT == MOE_FMT_Q2SM) gm[i] = stream_u32(base + a.G.min + unit * 4);
+    if (FMT == MOE_FMT_Q3G) gh[i] = stream_u2(base + a.G.hi + unit * 8);
   }
   __builtin_amdgcn_sched_barrier(0);
   const int ndr = (d - tid + KA_THREADS - 1) / KA_THREADS;   // D rows of this thread
@@ -232,10 +252,10 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
 #pragma unroll
   for (int i = 0; i < MAX_DROWS; ++i) {
     const int64_t unit = static_cast<int64_t>(js) * d + min(tid + KA_THREADS * i, d - 1);
-    dc[i] = *reinterpret_cast<const uint2*>(base + a.D.codes + unit * 8);
-    ds[i] = *reinterpret_cast<const uint16_t*>(base + a.D.scale + unit * 2);
-    if (FMT == MOE_FMT_Q2SM) dm[i] = *reinterpret_cast<const uint16_t*>(base + a.D.min + unit * 2);
-    if (FMT == MOE_FMT_Q3G) dh[i] = *reinterpret_cast<const uint32_t*>(base + a.D.hi + unit * 4);
+    dc[i] = stream_u2(base + a.D.codes + unit * 8);
+    ds[i] = stream_u16(base + a.D.scale + unit * 2);
+    if (FMT == MOE_FMT_Q2SM) dm[i] = stream_u16(base + a.D.min + unit * 2);
+    if (FMT == MOE_FMT_Q3G) dh[i] = stream_u32(base + a.D.hi + unit * 4);
   }
 
   __shared__ float red[KA_WAVES][64];

@@ -232,16 +232,17 @@ __device__ __forceinline__ BlockRaw load_b(BufRsrc rs, const Planes& P, uint32_t
   // step is two units
   const int64_t sblk = GATEUP ? static_cast<int64_t>(ks) * 4 * f : static_cast<int64_t>(ks) * 2 * d;
   BlockRaw r;
+  // weight blocks are read once: cache policy 2 = nontemporal
   const auto c = __builtin_amdgcn_raw_buffer_load_b64(rs, vb * 8,
-                                                      static_cast<int>(P.codes + sblk * 8), 0);
+                                                      static_cast<int>(P.codes + sblk * 8), 2);
   r.codes = make_uint2(c[0], c[1]);
   r.scale = __builtin_amdgcn_raw_buffer_load_b16(rs, vb * 2, static_cast<int>(P.scale + sblk * 2),
-                                                 0);
+                                                 2);
   r.min = FMT == MOE_FMT_Q2SM ? __builtin_amdgcn_raw_buffer_load_b16(
-                                    rs, vb * 2, static_cast<int>(P.min + sblk * 2), 0)
+                                    rs, vb * 2, static_cast<int>(P.min + sblk * 2), 2)
                               : 0u;
   r.hi = FMT == MOE_FMT_Q3G
-             ? __builtin_amdgcn_raw_buffer_load_b32(rs, vb * 4, static_cast<int>(P.hi + sblk * 4), 0)
+             ? __builtin_amdgcn_raw_buffer_load_b32(rs, vb * 4, static_cast<int>(P.hi + sblk * 4), 2)
              : 0u;
   return r;
 }
