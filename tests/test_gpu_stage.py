@@ -155,3 +155,29 @@ def test_stage_refuses_expert_without_source():
         bf.stage_layer(Lr.cache, Lr.slot_of_expert, Lr.tier, Lr.host_slot, staging[:16])
     torch.cuda.synchronize()
     assert not staging.any()                              # nothing was copied
+
+
+def test_stage_full_size_bitwise():
+    """The prefill workload's layer (E=512 + shared, d=2048, d_ff=768, Q2SM,
+    T=8192): 94 experts resident, the other 418 staged from pinned host
+    memory; the prefill on the staged pool equals the all-resident one bit
+    for bit (pair rows, shared rows, y)."""
+    import bit_expert_ffn_top_amd as bf
+    dev = need_gpu()
+    shape = synth.config_shape(4)
+    T = synth.WORKLOADS[4]["T"]
+    E, k = shape.n_experts, shape.top_k
+    Lr = TwoTierLayer(5, shape, synth.FMT_Q2SM, 94, dev, seed=7)
+    sb = Lr.packed.shape[1]
+    staging = torch.empty((E + 1, sb), dtype=torch.uint8, device=dev)
+    S = bf.stage_layer(Lr.cache, Lr.slot_of_expert, Lr.tier, Lr.host_slot, staging)
+    x = synth.make_x(4, 5, T, shape.d_model, device=dev, dtype=torch.bfloat16)
+    logits = synth.make_logits(4, 5, T, E, 1.5, device=dev)
+    ident = torch.arange(E, dtype=torch.int32, device=dev)
+    got = _prefill(bf, S, x, logits, ident, k)
+    torch.cuda.synchronize()
+    assert torch.equal(staging, Lr.packed)
+    ref = _prefill(bf, Lr.full, x, logits, torch.tensor(Lr.full_table, device=dev), k)
+    torch.cuda.synchronize()
+    for g, r in zip(got, ref):
+        assert torch.equal(g, r)
