@@ -401,7 +401,9 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
 // 2), group g sums its half of the slices in order, the two group sums meet
 // as g0 + g1, and wavefront 0 adds the terms in k-slot order, shared last.
 // No load depends on another: x, w, the pair slots and every partial are
-// requested up front.
+// requested up front (terms without partials are loaded and not used; in the
+// miss mode the terms outside the miss set are skipped, since the reads of
+// that mode cross the host link).
 constexpr int KB_ROWS = 32;
 constexpr int KB_GROUPS = 64 / KB_ROWS;
 constexpr int KB_WAVES = 16;
@@ -422,16 +424,20 @@ __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
   const int r = blockIdx.x * KB_ROWS + rr;
   const int ti = min(lane, k - 1);
   int sp = slot[t * k + ti];                     // lane i < k: slot of term i
-  const float wv = w[t * k + ti];                // lane i < k: weight of term i
+  float wv = w[t * k + ti];                      // lane i < k: weight of term i
   if (MISS) {
     const int hs = host_slot[min(max(idx[t * k + ti], 0), n_experts - 1)];
     sp = sp < 0 && ti < max_rank && hs < n_slots ? hs : -1;
   }
   const float xr = MISS ? y[static_cast<int64_t>(t) * d + r] : x[static_cast<int64_t>(t) * d + r];
+  // sp and wv are read across lanes inside branches only some lanes take:
+  // pinned here, with every lane active, so their definitions stay outside
+  opaque(sp);
+  opaque(wv);
   const int per = (nslices + KB_GROUPS - 1) / KB_GROUPS;
   const int j0 = min(nslices, g * per), j1 = min(nslices, j0 + per);
   for (int i = wave; i < k + 1; i += KB_WAVES) {
-    if (i < k ? __builtin_amdgcn_readlane(sp, i) < 0 : !has_shared) continue;   // term unused
+    if (MISS && (i < k ? __builtin_amdgcn_readlane(sp, i) < 0 : !has_shared)) continue;
     const float* src = part + ((static_cast<int64_t>(t) * (k + 1) + i) * nslices) * d + r;
     float acc = 0.0f;
     for (int j = j0; j < j1; j += KB_CHUNK) {
