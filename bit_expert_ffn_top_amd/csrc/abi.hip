@@ -288,6 +288,8 @@ int moe_expert_ffn_prefill(const moe_layer* L, const uint16_t* x_bf16, int T, co
   if (st != MOE_OK) return st;
   if (T < 1 || T > 65536) return MOE_EINVAL;
   if (L->d_model % 128 != 0 || L->d_ff % 64 != 0) return MOE_EINVAL;
+  // the GEMMs address x and h through 32-bit buffer offsets
+  if (static_cast<int64_t>(T) * (L->top_k + 1) * L->d_ff * 2 >= (int64_t{1} << 32)) return MOE_EINVAL;
   if (!x_bf16 || !idx || !slot || !out_pairs || !pair_pos || !expert_offsets || !ws)
     return MOE_EINVAL;
   if (out_shared && L->shared_slot < 0) return MOE_EINVAL;

@@ -546,7 +546,7 @@ __global__ __launch_bounds__(PTHREADS) void prefill_gemm_kernel(
     ProdCtx c;
     c.p = tid - NCONS;
     c.nK = nK;
-    // x is [T][d]; H is [T*k + T][f] (the host keeps it under 4 GiB)
+    // x is [T][d]; H is [T*k + T][f], under 4 GiB (checked by the entry point)
     c.a_rs = buf_rsrc(a_src, GATEUP ? static_cast<uint32_t>(g.T) * d * 2
                                     : static_cast<uint32_t>(g.T * (g.k + 1)) * f * 2);
     const int lane = c.p & 63, pw = c.p >> 6;

@@ -338,7 +338,8 @@ size_t moe_prefill_workspace_bytes(const moe_layer* L, int T);
  *   out_shared fp32 [T][d_model] = FFN_shared(x[t]) (NULL if no shared
  *   expert is wanted; must be NULL when shared_slot < 0).
  * moe_combine then forms y.  Limits: 1 <= T <= 65536, d_model a multiple
- * of 128, d_ff a multiple of 64.
+ * of 128, d_ff a multiple of 64, T * (top_k + 1) * d_ff * 2 < 2^32 (the bf16
+ * h rows the GEMMs address with 32-bit offsets).
  * ws: at least moe_prefill_workspace_bytes(L, T) bytes, 256-byte aligned. */
 int moe_expert_ffn_prefill(const moe_layer* L, const uint16_t* x_bf16, int T,
                            const int32_t* idx, const int32_t* slot,

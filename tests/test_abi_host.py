@@ -144,6 +144,8 @@ def test_prefill_host_checks():
     assert call(_layer(shared_slot=-1)) == -1                               # shared out, no shared
     L64 = _layer(d_model=64, slot_bytes=synth.slot_bytes(2, 64, 768))
     assert call(L64, ws=1 << 40) == -1                                      # d not a multiple of 128
+    big = _layer(top_k=64, d_ff=4096, slot_bytes=synth.slot_bytes(2, 2048, 4096))
+    assert call(big, T=65536, ws=1 << 40) == -1                            # h past 4 GiB
 
 
 def test_combine_host_checks():

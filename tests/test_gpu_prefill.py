@@ -51,6 +51,10 @@ CASES = [
     ("q2s_T130_noshared", synth.LayerShape(64, 4, 256, 128, False), synth.FMT_Q2S, 130),
     ("q3g_T77", synth.LayerShape(32, 6, 256, 192, True), synth.FMT_Q3G, 77),
     ("q2sm_T1", synth.LayerShape(64, 4, 256, 128, True), synth.FMT_Q2SM, 1),
+    # smallest and largest sizes the prefill accepts: d_model 128 / d_ff 64,
+    # and d_model 2048 / d_ff 4096 (64 down K steps, 16 gate/up column jobs)
+    ("q2s_d128_f64", synth.LayerShape(16, 3, 128, 64, True), synth.FMT_Q2S, 50),
+    ("q2sm_d2048_f4096", synth.LayerShape(6, 2, 2048, 4096, True), synth.FMT_Q2SM, 70),
 ]
 
 
