@@ -23,6 +23,11 @@
 // Arithmetic per block: codes become fp16 pairs (c + q) by mask-and-OR with
 // an exponent, each multiplied into fp32 by v_fma_mix; the block's offset sum
 // and scale/min are applied once per block.
+//
+// Modes of the ffn kernel: the pair slots given (moe_expert_ffn_decode), the
+// routing done inside every workgroup (moe_decode_layer), or the missed pairs
+// only, with their slots in a second pool such as pinned host memory
+// (moe_decode_misses, whose combine adds into y).
 #include "moe_internal.h"
 #include "route_device.h"
 
