@@ -60,7 +60,8 @@ def parse():
                     help="run only the prefill workload (for profiling); prints its object")
     ap.add_argument("--counters", action="store_true",
                     help="counter pass for rocprofv3 --pmc: eager decode layer calls plus one "
-                         "device copy of COPY_BYTES for calibration; prints no result line")
+                         "device copy of COPY_BYTES for calibration; prints no result line "
+                         "(with --prefill-only: the prefill workload, then the copy)")
     return ap.parse_args()
 
 
@@ -189,12 +190,18 @@ def counter_pass(torch, bf, synth, chain, logits_sets, dev):
     for g in range(2):
         chain.step(logits_sets[g])
     torch.cuda.synchronize()
+    calibration_copy(torch, dev)
+    log(f"counter pass: {2 * len(chain.layers)} decode layer calls, copy of {COPY_BYTES} bytes")
+
+
+def calibration_copy(torch, dev):
+    """One device-to-device copy of COPY_BYTES: the known traffic that HBM
+    counters are scaled by."""
     src = torch.empty((COPY_BYTES // 4,), dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"counter pass: {2 * len(chain.layers)} decode layer calls, copy of {COPY_BYTES} bytes")
 
 
 def decode_bytes_per_call(synth, shape, fmt, T, n_union):
@@ -233,6 +240,8 @@ def main():
 
     if args.prefill_only:
         print(json.dumps({"prefill": run_prefill(torch, np, bf, synth, pools, dev, args)}), flush=True)
+        if args.counters:
+            calibration_copy(torch, dev)
         return
 
     # ---------------- decode (headline) ----------------

@@ -298,6 +298,21 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier of the GEMM steps.  It waits for this wavefront's LDS
+// reads and writes (lgkmcnt 0) and for nothing else: the barrier with a
+// workgroup fence also waits for every outstanding load that writes LDS (the
+// rows requested for a later step) and for the epilogue's global stores, so
+// that each step would pay their latency.  The loads that must have landed
+// are waited for explicitly (wait_vm) by the producers before they arrive
+// here.  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt: no wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // One producer step ks: the token rows of step ks+2 are requested into the A
 // buffer that step ks-1 used, the weight blocks of step ks+3 into `load`, the
 // blocks of step ks+1 (`use`, requested two steps earlier) are dequantized
@@ -320,7 +335,7 @@ __device__ __forceinline__ void produce_step(const ProdCtx& c, const Planes& P, 
     wait_vm<2 * NB + 8>();
   else
     wait_vm<2 * NB>();
-  __syncthreads();
+  step_barrier();
 }
 
 template <int FMT, bool GATEUP>
@@ -340,7 +355,7 @@ __device__ __forceinline__ void produce_job(const ProdCtx& c, const Planes& P, i
     wait_vm<3 * NB + 8>();
   else
     wait_vm<3 * NB>();
-  __syncthreads();
+  step_barrier();
   int ks = 0;
   for (; ks + 1 < c.nK; ks += 2) {
     produce_step<FMT, GATEUP>(c, P, d, f, abuf, bbuf, ks, R0, R0);
@@ -439,11 +454,11 @@ __device__ __forceinline__ void consume_job(int nK, int lane, int cq, int rows, 
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  __syncthreads();   // step 0 is in buffers 0
+  step_barrier();   // step 0 is in buffers 0
   for (int ks = 0; ks < nK; ++ks) {
     if (NT > 0)
       mfma_step<NT>(acc, abuf + (ks % A_BUFS) * A_TILE, bbuf + (ks & 1) * B_TILE, lane, RH, cq);
-    __syncthreads();
+    step_barrier();
   }
   if (NT == 0) return;
 
