@@ -38,6 +38,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_layer_e512_k10_d2048_f768_
 DECODE_SOURCES = ["bit_expert_ffn_top_amd/csrc/ffn_decode.hip",
                   "bit_expert_ffn_top_amd/csrc/moe_common.h",
                   "bit_expert_ffn_top_amd/csrc/route_device.h"]
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                                    "prefill_e512_k10_d2048_f768_q2sm_t8192_traffic.txt")
+PREFILL_SOURCES = ["bit_expert_ffn_top_amd/csrc/ffn_prefill.hip",
+                   "bit_expert_ffn_top_amd/csrc/cache_lookup.hip",
+                   "bit_expert_ffn_top_amd/csrc/moe_common.h",
+                   "bit_expert_ffn_top_amd/csrc/route_device.h"]
 
 
 def log(*a):
@@ -166,18 +172,19 @@ def sources_digest(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per moe_decode_layer call from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy); None when the file
-    is missing or the decode kernels' sources changed since it was taken."""
+def measured_traffic(path=TRAFFIC_FILE, sources=DECODE_SOURCES):
+    """HBM bytes per call from a committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, calibrated on a plain copy); None when the file is missing or
+    the kernels' sources changed since it was taken.  Defaults: one
+    moe_decode_layer call of the decode workload."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     key, val = line.split(":", 1)
                     kv[key.strip()] = val.strip()
-        if kv.get("sources_sha256_16") != sources_digest(DECODE_SOURCES):
+        if kv.get("sources_sha256_16") != sources_digest(sources):
             return None
         return int(float(kv["bytes_per_call"]))
     except (OSError, KeyError, ValueError):
@@ -745,7 +752,8 @@ def run_prefill(torch, np, bf, synth, pools, dev, args):
         "roofline": {
             "kernel": "moe_expert_ffn_prefill (grouping + gate/up + down GEMMs)",
             "bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SOURCES),
             "avg_call_ms": round(call_ms, 4), "flops_per_call": flops,
         },
     }
