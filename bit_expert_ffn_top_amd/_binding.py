@@ -120,6 +120,22 @@ def _dev(t: torch.Tensor, dtype, name: str):
     return t
 
 
+def _shape(t: torch.Tensor, shape, name: str):
+    """t must have exactly this shape (None: any extent).  Checked before the
+    device checks, so that a wrong size is reported as such."""
+    if t.dim() != len(shape) or any(s is not None and a != s for a, s in zip(t.shape, shape)):
+        parts = ["*" if s is None else str(s) for s in shape]
+        want = "(" + ", ".join(parts) + ("," if len(parts) == 1 else "") + ")"
+        raise ValueError(f"{name}: shape {want} expected, got {tuple(t.shape)}")
+    return t
+
+
+def _at_least(t: torch.Tensor, n: int, name: str):
+    if t.numel() < n:
+        raise ValueError(f"{name}: at least {n} elements expected, got {t.numel()}")
+    return t
+
+
 @dataclasses.dataclass
 class MoeLayer:
     """One layer's packed expert pool in device memory."""
@@ -149,12 +165,15 @@ def slot_bytes(fmt: int, d_model: int, d_ff: int) -> int:
 
 
 def route_topk(logits: torch.Tensor, k: int, idx=None, w=None, stream=None):
+    _shape(logits, (None, None), "logits")
     _dev(logits, torch.float32, "logits")
     T, E = logits.shape
     if idx is None:
         idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     if w is None:
         w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _dev(_shape(idx, (T, k), "idx"), torch.int32, "idx")
+    _dev(_shape(w, (T, k), "w"), torch.float32, "w")
     _check(lib().moe_route_topk(_ptr(logits), T, E, k, _ptr(idx), _ptr(w), _stream(stream)),
            "moe_route_topk")
     return idx, w
@@ -166,6 +185,8 @@ def lookup_workspace_bytes(T: int, k: int, E: int) -> int:
 
 def cache_lookup(idx: torch.Tensor, slot_of_expert: torch.Tensor, slot=None, miss_expert=None,
                  miss_pair=None, n_miss=None, ws=None, want_pairs=True, stream=None):
+    _shape(idx, (None, None), "idx")
+    _shape(slot_of_expert, (None,), "slot_of_expert")
     _dev(idx, torch.int32, "idx")
     _dev(slot_of_expert, torch.int32, "slot_of_expert")
     T, k = idx.shape
@@ -177,6 +198,11 @@ def cache_lookup(idx: torch.Tensor, slot_of_expert: torch.Tensor, slot=None, mis
     if want_pairs and miss_pair is None:
         miss_pair = torch.full((max(n, 1),), -1, dtype=torch.int32, device=dev)
     n_miss = torch.zeros((4,), dtype=torch.int32, device=dev) if n_miss is None else n_miss
+    _dev(_shape(slot, (T, k), "slot"), torch.int32, "slot")
+    _dev(_at_least(miss_expert, n, "miss_expert"), torch.int32, "miss_expert")
+    if miss_pair is not None:
+        _dev(_at_least(miss_pair, n, "miss_pair"), torch.int32, "miss_pair")
+    _dev(_at_least(n_miss, 2, "n_miss"), torch.int32, "n_miss")
     need = lookup_workspace_bytes(T, k, E)
     if need and ws is None:
         ws = torch.empty((need,), dtype=torch.uint8, device=dev)
@@ -193,14 +219,15 @@ def decode_workspace_bytes(layer: MoeLayer, T: int) -> int:
 
 
 def expert_ffn_decode(layer: MoeLayer, x, idx, slot, w, y=None, ws=None, stream=None):
-    _dev(x, torch.float32, "x")
+    _dev(_shape(x, (None, layer.d_model), "x"), torch.float32, "x")
+    T = x.shape[0]
     for name, t, dt in (("idx", idx, torch.int32), ("slot", slot, torch.int32),
                         ("w", w, torch.float32)):
-        _dev(t, dt, name)
-    T = x.shape[0]
+        _dev(_shape(t, (T, layer.top_k), name), dt, name)
     L = layer.c_struct()
     if y is None:
         y = torch.empty_like(x)
+    _dev(_shape(y, tuple(x.shape), "y"), torch.float32, "y")
     if ws is None:
         ws = torch.empty((decode_workspace_bytes(layer, T),), dtype=torch.uint8, device=x.device)
     _check(lib().moe_expert_ffn_decode(ctypes.byref(L), _ptr(x), T, _ptr(idx), _ptr(slot),
@@ -214,11 +241,12 @@ def decode_layer(layer: MoeLayer, x, logits, slot_of_expert, idx=None, w=None, s
                  want_pairs=True, stream=None):
     """Route, look up and run one decode layer (moe_decode_layer).
     Returns (y, idx, w, slot, miss_expert, miss_pair, n_miss)."""
-    _dev(x, torch.float32, "x")
-    _dev(logits, torch.float32, "logits")
-    _dev(slot_of_expert, torch.int32, "slot_of_expert")
+    _dev(_shape(x, (None, layer.d_model), "x"), torch.float32, "x")
     T = x.shape[0]
     k = layer.top_k
+    _dev(_shape(logits, (T, layer.n_experts), "logits"), torch.float32, "logits")
+    _dev(_shape(slot_of_expert, (layer.n_experts,), "slot_of_expert"), torch.int32,
+         "slot_of_expert")
     dev = x.device
     n = T * k
     idx = torch.empty((T, k), dtype=torch.int32, device=dev) if idx is None else idx
@@ -230,6 +258,14 @@ def decode_layer(layer: MoeLayer, x, logits, slot_of_expert, idx=None, w=None, s
         miss_pair = torch.full((n,), -1, dtype=torch.int32, device=dev)
     n_miss = torch.zeros((4,), dtype=torch.int32, device=dev) if n_miss is None else n_miss
     y = torch.empty_like(x) if y is None else y
+    for name, t, dt in (("idx", idx, torch.int32), ("w", w, torch.float32),
+                        ("slot", slot, torch.int32)):
+        _dev(_shape(t, (T, k), name), dt, name)
+    _dev(_at_least(miss_expert, n, "miss_expert"), torch.int32, "miss_expert")
+    if miss_pair is not None:
+        _dev(_at_least(miss_pair, n, "miss_pair"), torch.int32, "miss_pair")
+    _dev(_at_least(n_miss, 2, "n_miss"), torch.int32, "n_miss")
+    _dev(_shape(y, tuple(x.shape), "y"), torch.float32, "y")
     if ws is None:
         ws = torch.empty((decode_workspace_bytes(layer, T),), dtype=torch.uint8, device=dev)
     L = layer.c_struct()
@@ -267,13 +303,18 @@ def decode_misses(tier: HostTier, x, idx, slot, w, host_slot_of_expert, y, max_r
                   ws=None, stream=None):
     """Add the missed pairs of a decode step, computed from the host tier,
     into y (moe_decode_misses).  y holds the GPU part on entry.  Returns y."""
+    _shape(x, (None, tier.d_model), "x")
+    T = x.shape[0]
+    k = tier.top_k
+    for t, shp, name in ((idx, (T, k), "idx"), (slot, (T, k), "slot"), (w, (T, k), "w"),
+                         (host_slot_of_expert, (tier.n_experts,), "host_slot_of_expert"),
+                         (y, (T, tier.d_model), "y")):
+        _shape(t, shp, name)
     for t, dt, name in ((x, torch.float32, "x"), (idx, torch.int32, "idx"),
                         (slot, torch.int32, "slot"), (w, torch.float32, "w"),
                         (host_slot_of_expert, torch.int32, "host_slot_of_expert"),
                         (y, torch.float32, "y")):
         _dev(t, dt, name)
-    T = x.shape[0]
-    k = tier.top_k
     r = k if max_rank is None else int(max_rank)
     L = tier.c_struct()
     if ws is None:
@@ -289,7 +330,7 @@ def cache_count(idx, counts, stream=None):
     """counts[e] += uses of expert e in idx (moe_cache_count).  counts: int32
     tensor viewed as uint32 [E]."""
     _dev(idx, torch.int32, "idx")
-    _dev(counts, torch.int32, "counts")
+    _dev(_shape(counts, (None,), "counts"), torch.int32, "counts")
     _check(lib().moe_cache_count(_ptr(idx), idx.numel(), counts.numel(), _ptr(counts),
                                  _stream(stream)), "moe_cache_count")
     return counts
@@ -299,12 +340,19 @@ def cache_plan(counts, slot_of_expert, expert_of_slot, shared_slot, host_slot_of
                host_n_slots, max_swaps, decay_shift=1, swaps=None, n_swaps=None, stream=None):
     """Plan up to max_swaps swaps, updating the tables and decaying the
     counts in place (moe_cache_plan).  Returns (swaps [max_swaps, 4], n_swaps [4])."""
+    E = counts.numel()
+    for t, name in ((counts, "counts"), (slot_of_expert, "slot_of_expert"),
+                    (host_slot_of_expert, "host_slot_of_expert")):
+        _shape(t, (E,), name)
+    _shape(expert_of_slot, (None,), "expert_of_slot")
     for t, name in ((counts, "counts"), (slot_of_expert, "slot_of_expert"),
                     (expert_of_slot, "expert_of_slot"), (host_slot_of_expert, "host_slot_of_expert")):
         _dev(t, torch.int32, name)
     dev = counts.device
     swaps = torch.full((max_swaps, 4), -1, dtype=torch.int32, device=dev) if swaps is None else swaps
     n_swaps = torch.zeros((4,), dtype=torch.int32, device=dev) if n_swaps is None else n_swaps
+    _dev(_shape(swaps, (max_swaps, 4), "swaps"), torch.int32, "swaps")
+    _dev(_at_least(n_swaps, 1, "n_swaps"), torch.int32, "n_swaps")
     _check(lib().moe_cache_plan(_ptr(counts), counts.numel(), _ptr(slot_of_expert),
                                 _ptr(expert_of_slot), expert_of_slot.numel(), shared_slot,
                                 _ptr(host_slot_of_expert), host_n_slots, max_swaps, decay_shift,
@@ -315,8 +363,8 @@ def cache_plan(counts, slot_of_expert, expert_of_slot, shared_slot, host_slot_of
 def cache_fill(layer: MoeLayer, tier: HostTier, swaps, n_swaps, stream=None):
     """Copy the planned experts from the host tier into the cache's slots
     (moe_cache_fill)."""
-    _dev(swaps, torch.int32, "swaps")
-    _dev(n_swaps, torch.int32, "n_swaps")
+    _dev(_shape(swaps, (None, 4), "swaps"), torch.int32, "swaps")
+    _dev(_at_least(n_swaps, 1, "n_swaps"), torch.int32, "n_swaps")
     L, H = layer.c_struct(), tier.c_struct()
     _check(lib().moe_cache_fill(ctypes.byref(L), ctypes.byref(H), _ptr(swaps), _ptr(n_swaps),
                                 swaps.shape[0], _stream(stream)), "moe_cache_fill")
@@ -324,9 +372,9 @@ def cache_fill(layer: MoeLayer, tier: HostTier, swaps, n_swaps, stream=None):
 
 def cache_commit(slot_of_expert, swaps, n_swaps, stream=None):
     """Make the admitted experts visible in the slot table (moe_cache_commit)."""
-    _dev(slot_of_expert, torch.int32, "slot_of_expert")
-    _dev(swaps, torch.int32, "swaps")
-    _dev(n_swaps, torch.int32, "n_swaps")
+    _dev(_shape(slot_of_expert, (None,), "slot_of_expert"), torch.int32, "slot_of_expert")
+    _dev(_shape(swaps, (None, 4), "swaps"), torch.int32, "swaps")
+    _dev(_at_least(n_swaps, 1, "n_swaps"), torch.int32, "n_swaps")
     _check(lib().moe_cache_commit(_ptr(slot_of_expert), slot_of_expert.numel(), _ptr(swaps),
                                   _ptr(n_swaps), swaps.shape[0], _stream(stream)),
            "moe_cache_commit")
@@ -341,6 +389,9 @@ def stage_layer(cache: MoeLayer, slot_of_expert, tier: HostTier, host_slot_of_ex
     import numpy as np
     soe = np.ascontiguousarray(np.asarray(slot_of_expert, dtype=np.int32))
     hs = np.ascontiguousarray(np.asarray(host_slot_of_expert, dtype=np.int32))
+    for a, name in ((soe, "slot_of_expert"), (hs, "host_slot_of_expert")):
+        if a.shape != (cache.n_experts,):
+            raise ValueError(f"{name}: shape ({cache.n_experts},) expected, got {a.shape}")
     _dev(staging, torch.uint8, "staging")
     C, H = cache.c_struct(), tier.c_struct()
     _check(lib().moe_stage_layer(ctypes.byref(C), soe.ctypes.data, ctypes.byref(H), hs.ctypes.data,
@@ -358,11 +409,11 @@ def prefill_workspace_bytes(layer: MoeLayer, T: int) -> int:
 def expert_ffn_prefill(layer: MoeLayer, x_bf16, idx, slot, out_pairs=None, pair_pos=None,
                        expert_offsets=None, out_shared=None, with_shared=True, ws=None,
                        stream=None):
-    _dev(x_bf16, torch.bfloat16, "x_bf16")
-    _dev(idx, torch.int32, "idx")
-    _dev(slot, torch.int32, "slot")
+    _dev(_shape(x_bf16, (None, layer.d_model), "x_bf16"), torch.bfloat16, "x_bf16")
     T, d = x_bf16.shape
-    k = idx.shape[1]
+    k = layer.top_k
+    _dev(_shape(idx, (T, k), "idx"), torch.int32, "idx")
+    _dev(_shape(slot, (T, k), "slot"), torch.int32, "slot")
     dev = x_bf16.device
     if out_pairs is None:
         out_pairs = torch.empty((T * k, d), dtype=torch.float32, device=dev)
@@ -376,6 +427,13 @@ def expert_ffn_prefill(layer: MoeLayer, x_bf16, idx, slot, out_pairs=None, pair_
         out_shared = None
     if ws is None:
         ws = torch.empty((prefill_workspace_bytes(layer, T),), dtype=torch.uint8, device=dev)
+    _dev(_shape(out_pairs, (T * k, d), "out_pairs"), torch.float32, "out_pairs")
+    _dev(_shape(pair_pos, (T, k), "pair_pos"), torch.int32, "pair_pos")
+    _dev(_shape(expert_offsets, (layer.n_experts + 1,), "expert_offsets"), torch.int32,
+         "expert_offsets")
+    if out_shared is not None:
+        _dev(_shape(out_shared, (T, d), "out_shared"), torch.float32, "out_shared")
+    _dev(ws, torch.uint8, "ws")
     L = layer.c_struct()
     _check(lib().moe_expert_ffn_prefill(ctypes.byref(L), _ptr(x_bf16), T, _ptr(idx), _ptr(slot),
                                         _ptr(out_pairs), _ptr(pair_pos), _ptr(expert_offsets),
@@ -391,11 +449,18 @@ def combine(x, rows, pair_pos, w, shared=None, y=None, stream=None):
         x_dtype = DTYPE_BF16
     else:
         raise ValueError("x must be float32 or bfloat16")
-    _dev(x, x.dtype, "x")
+    _dev(_shape(x, (None, None), "x"), x.dtype, "x")
     T, d = x.shape
     k = pair_pos.shape[1] if pair_pos is not None else 0
+    if k:
+        _dev(_shape(pair_pos, (T, k), "pair_pos"), torch.int32, "pair_pos")
+        _dev(_shape(w, (T, k), "w"), torch.float32, "w")
+        _dev(_shape(rows, (None, d), "rows"), torch.float32, "rows")
+    if shared is not None:
+        _dev(_shape(shared, (T, d), "shared"), torch.float32, "shared")
     if y is None:
         y = torch.empty((T, d), dtype=torch.float32, device=x.device)
+    _dev(_shape(y, (T, d), "y"), torch.float32, "y")
     _check(lib().moe_combine(_ptr(x), x_dtype, T, d, k, _ptr(rows), _ptr(pair_pos), _ptr(w),
                              _ptr(shared), _ptr(y), _stream(stream)), "moe_combine")
     return y
