@@ -23,6 +23,8 @@
 // same XCD (job j runs on workgroup j mod grid, and workgroups are spread
 // over the 8 XCDs in turn), so the gathered x rows are shared through that
 // XCD's L2.
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace bitffn {
@@ -635,18 +637,28 @@ PrefillWs prefill_ws(void* ws, int d, int f, int T, int k, int E) {
   return w;
 }
 
+// Compute units of the current device, looked up once per device (devices
+// beyond the table are asked every time).
+constexpr int kMaxDevices = 64;
+
+int device_cus() {
+  static std::atomic<int> cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  hipDeviceProp_t prop;
+  const int c = hipGetDeviceProperties(&prop, dev) == hipSuccess ? prop.multiProcessorCount : 256;
+  if (dev >= 0 && dev < kMaxDevices) cus[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
 // Persistent grid: one workgroup per CU, a multiple of 8 so that job j and
 // workgroup j mod grid share an XCD.
 int prefill_grid(int64_t max_jobs) {
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
-      n_cu = 256;
-    else
-      n_cu = prop.multiProcessorCount;
-  }
+  const int n_cu = device_cus();
   int64_t grid = (max_jobs + 7) / 8 * 8;
   const int64_t cap = (n_cu + 7) / 8 * 8;
   if (grid > cap) grid = cap;
@@ -657,13 +669,19 @@ template <int FMT, bool GATEUP>
 hipError_t launch_gemm(const GroupInfo& g, int64_t max_jobs, const moe_layer& L, Planes P,
                        const uint16_t* a, uint16_t* h, float* out_pairs, float* out_shared,
                        hipStream_t s) {
-  static bool lds_set = false;   // per instantiation
-  if (!lds_set) {
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_gemm_kernel<FMT, GATEUP>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(PREFILL_LDS));
+  // the dynamic LDS limit is raised once per instantiation and device
+  // (devices beyond the table every time)
+  static std::atomic<uint64_t> lds_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < kMaxDevices ? uint64_t{1} << dev : 0;
+  if (bit == 0 || !(lds_set.load(std::memory_order_relaxed) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_gemm_kernel<FMT, GATEUP>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(PREFILL_LDS));
     if (e != hipSuccess) return e;
-    lds_set = true;
+    lds_set.fetch_or(bit, std::memory_order_relaxed);
   }
   prefill_gemm_kernel<FMT, GATEUP><<<prefill_grid(max_jobs), PTHREADS, PREFILL_LDS, s>>>(
       static_cast<const uint8_t*>(L.pool), L.slot_bytes, P, L.d_model, L.d_ff, g, a, h, out_pairs,
