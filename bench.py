@@ -769,15 +769,17 @@ def cpu_baseline(np, synth, pools, shape):
     except Exception:  # noqa: BLE001
         cores = 1
     E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
+    n_tok = 2
     inputs = []
-    for l in range(N_LAYERS):          # device -> host copies stay outside the timing
-        pool, table_dev, shared_slot, fmt = pools[l]
-        table = table_dev.cpu().numpy()
-        logits = synth.make_logits(1, l, 1, E, 1.5, step=0).numpy()
-        chosen = set(table[np.argsort(-logits[0], kind="stable")[:k]].tolist())
-        host = {s: pool[s].cpu().numpy() for s in chosen | {shared_slot}}
-        x = synth.make_x(1, l, 1, d).double().numpy()
-        inputs.append((x, logits, table, host, shared_slot, fmt))
+    for step in range(n_tok):          # device -> host copies stay outside the timing
+        for l in range(N_LAYERS):
+            pool, table_dev, shared_slot, fmt = pools[l]
+            table = table_dev.cpu().numpy()
+            logits = synth.make_logits(1, l, 1, E, 1.5, step=step).numpy()
+            chosen = set(table[np.argsort(-logits[0], kind="stable")[:k]].tolist())
+            host = {s: pool[s].cpu().numpy() for s in chosen | {shared_slot}}
+            x = synth.make_x(1, l, 1, d).double().numpy()
+            inputs.append((x, logits, table, host, shared_slot, fmt))
     t0 = time.perf_counter()
     for x, logits, table, host, shared_slot, fmt in inputs:
         idx, w = oracle.route_topk(logits, k)
@@ -785,10 +787,11 @@ def cpu_baseline(np, synth, pools, shape):
         oracle.layer_decode(x, idx, slot, w,
                             lambda s: oracle.unpack_expert(host[s], fmt, d, f), shared_slot)
     dt = time.perf_counter() - t0
-    return {"value": round(1.0 / dt, 5), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 NumPy oracle, one token through all {N_LAYERS} decode layers over the "
-                      f"same packed pools as the timed workload, logits drawn on the host (route, "
-                      f"lookup, unpack of the 11 chosen slots, FFNs, combine)",
+    return {"value": round(n_tok / dt, 5), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, {n_tok} tokens (two logit draws) through all {N_LAYERS} "
+                      f"decode layers over the same packed pools as the timed workload, logits "
+                      f"drawn on the host (route, lookup, unpack of the 11 chosen slots, FFNs, "
+                      f"combine)",
             "seconds": round(dt, 2)}
 
 
