@@ -93,9 +93,10 @@ class DecodeChain:
     its y to a scratch buffer."""
 
     def __init__(self, torch, bf, shape, pools, T, dev, xs, tiers=None, host_table=None,
-                 max_rank=None, counts=None):
+                 max_rank=None, counts=None, acc=False):
         self.torch, self.bf = torch, bf
         self.T = T
+        self.acc = acc
         self.tiers, self.host_table, self.max_rank = tiers, host_table, max_rank
         self.counts = counts
         self.layers = [bf.MoeLayer(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k, fmt,
@@ -112,12 +113,30 @@ class DecodeChain:
         self.ws = torch.empty((ws,), dtype=torch.uint8, device=dev)
         self.xs = xs
         self.y = torch.empty((T, d), dtype=torch.float32, device=dev)
+        if acc:
+            # layer l adds into buffer l % 3 and clears (l + 1) % 3; with a
+            # multiple of 3 layers the last one clears buffer 0 for the next step
+            assert len(self.layers) % 3 == 0 and tiers is None and counts is None
+            self.accs = [torch.zeros((bf.ACC_BUFS, T, d), dtype=torch.float32, device=dev)
+                         for _ in range(3)]
 
     def step(self, logits):
         """logits [n_layers, T, E].  One moe_decode_layer call per layer:
         route, look up, expert FFN, combine; with host tiers, then one
-        moe_decode_misses call that adds the missed experts."""
+        moe_decode_misses call that adds the missed experts.  acc: one
+        moe_decode_layer_acc call per layer, each forming the previous
+        layer's y, and a finish call for the last layer's y."""
         bf = self.bf
+        if self.acc:
+            n = len(self.layers)
+            for l, L in enumerate(self.layers):
+                prev = (self.xs[l - 1], self.accs[(l - 1) % 3], self.y) if l else None
+                bf.decode_layer_acc(L, self.xs[l], logits[l], self.tables[l], self.accs[l % 3],
+                                    acc_clear=self.accs[(l + 1) % 3], prev=prev, idx=self.idx,
+                                    w=self.w, slot=self.slot, miss_expert=self.miss_e,
+                                    miss_pair=self.miss_p, n_miss=self.n_miss)
+            bf.decode_acc_finish(self.xs[n - 1], self.accs[(n - 1) % 3], y=self.y)
+            return self.y
         for l, L in enumerate(self.layers):
             bf.decode_layer(L, self.xs[l], logits[l], self.tables[l], idx=self.idx, w=self.w,
                             slot=self.slot, miss_expert=self.miss_e, miss_pair=self.miss_p,
@@ -253,7 +272,7 @@ def main():
 
     # ---------------- decode (headline) ----------------
     xs = [synth.make_x(1, l, 1, d, device=dev) for l in range(N_LAYERS)]
-    chain = DecodeChain(torch, bf, shape, pools, 1, dev, xs)
+    chain = DecodeChain(torch, bf, shape, pools, 1, dev, xs, acc=True)
     n_graphs = args.graphs
     logits_sets = [torch.stack([synth.make_logits(1, l, 1, E, 1.5, device=dev, step=g)
                                 for l in range(N_LAYERS)]) for g in range(n_graphs)]
@@ -266,6 +285,13 @@ def main():
     ms_step = dt * 1e3 / args.steps
     log(f"decode: {tok_s:.1f} tok/s, {ms_step * 1e3:.1f} us/token ({ms_step * 1e3 / N_LAYERS:.2f} us/layer)")
     del graphs
+    # the same step with the two-kernel layer call (FFN kernel + combine kernel)
+    chain2k = DecodeChain(torch, bf, shape, pools, 1, dev, xs)
+    dt2, _, graphs = time_graph_steps(torch, chain2k, logits_sets, args.steps, args.warmup,
+                                      n_graphs)
+    tok_s_2k = args.steps / dt2
+    log(f"decode, two kernels per layer: {tok_s_2k:.1f} tok/s")
+    del graphs, chain2k
     call_us = ev_ms * 1e3 / (args.steps * N_LAYERS)
     bytes_call = decode_bytes_per_call(synth, shape, synth.FMT_Q2SM, 1, k + 1)
     ach = bytes_call / (call_us * 1e-6) / 1e9
@@ -295,8 +321,10 @@ def main():
         "token_hbm_GBps_algorithmic": round(token_bytes * tok_s / 1e9, 1),
         "token_frac_of_hbm_peak": round(token_bytes * tok_s / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
-            "kernel": "moe_decode_layer call = decode_ffn_kernel (routing + gate/up + SiLU + "
-                      "partial down) + decode_combine_kernel, one call per layer",
+            "kernel": "moe_decode_layer_acc call = decode_ffn_kernel in accumulate mode (routing "
+                      "+ gate/up + SiLU + down + weighted atomic adds into 8 buffers; its side "
+                      "workgroups clear the next buffers and form the previous layer's y), one "
+                      "call per layer, plus one finish kernel per token for the last layer's y",
             "bound": "hbm",
             "achieved": round(ach, 1),
             "peak": HBM_PEAK_GBS,
@@ -306,6 +334,7 @@ def main():
             "avg_call_us": round(call_us, 3),
             "bytes_per_call": bytes_call,
         },
+        "two_kernel_layer_tok_s": round(tok_s_2k, 2),
     }
 
     extra = {}

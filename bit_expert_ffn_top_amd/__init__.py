@@ -4,8 +4,10 @@ The computation lives in libbitffn_moe.so (HIP kernels behind the C ABI of
 include/bitffn_moe.h); this package is its thin Python binding.
 """
 from ._binding import (  # noqa: F401
-    DTYPE_BF16, DTYPE_F32, FMT_Q2S, FMT_Q2SM, FMT_Q3G, HostTier, MoeError, MoeLayer, abi_version,
-    cache_commit, cache_count, cache_fill, cache_lookup, cache_plan, combine, decode_layer,
-    decode_misses, decode_workspace_bytes, expert_ffn_decode, expert_ffn_prefill, lib, lib_path,
-    lookup_workspace_bytes, prefill_workspace_bytes, route_topk, slot_bytes, stage_layer,
+    ACC_BUFS, DTYPE_BF16, DTYPE_F32, FMT_Q2S, FMT_Q2SM, FMT_Q3G, HostTier, MoeError, MoeLayer,
+    abi_version,
+    cache_commit, cache_count, cache_fill, cache_lookup, cache_plan, combine, decode_acc_finish,
+    decode_layer, decode_layer_acc, decode_misses, decode_workspace_bytes, expert_ffn_decode,
+    expert_ffn_prefill, lib, lib_path, lookup_workspace_bytes, prefill_workspace_bytes,
+    route_topk, slot_bytes, stage_layer,
 )

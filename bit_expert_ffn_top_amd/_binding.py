@@ -50,6 +50,9 @@ SIGNATURES = {
     "moe_expert_ffn_decode": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
     "moe_decode_layer": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _c_sz, _vp]),
+    "moe_decode_layer_acc": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_decode_acc_finish": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp]),
     "moe_decode_misses": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, _vp,
                                    _c_sz, _vp]),
     "moe_cache_count": (_c_int, [_vp, _c_int, _c_int, _vp, _vp]),
@@ -274,6 +277,72 @@ def decode_layer(layer: MoeLayer, x, logits, slot_of_expert, idx=None, w=None, s
                                   _ptr(miss_expert), _ptr(miss_pair), _ptr(n_miss), _ptr(y),
                                   _ptr(ws), ws.numel(), _stream(stream)), "moe_decode_layer")
     return y, idx, w, slot, miss_expert, miss_pair, n_miss
+
+
+ACC_BUFS = 8   # accumulation buffers of moe_decode_layer_acc
+
+
+def decode_layer_acc(layer: MoeLayer, x, logits, slot_of_expert, acc_out, acc_clear=None,
+                     prev=None, idx=None, w=None, slot=None, miss_expert=None, miss_pair=None,
+                     n_miss=None, want_pairs=True, stream=None):
+    """One decode layer with its weighted terms added into acc_out (fp32
+    [8, T, d_model], zero on entry) instead of forming y
+    (moe_decode_layer_acc).  acc_clear: a buffer of the same shape set to
+    zero.  prev: (prev_x, prev_acc, prev_y) of the previous call, whose y this
+    call forms.  Returns (idx, w, slot, miss_expert, miss_pair, n_miss)."""
+    _dev(_shape(x, (None, layer.d_model), "x"), torch.float32, "x")
+    T = x.shape[0]
+    k = layer.top_k
+    acc_shape = (ACC_BUFS, T, layer.d_model)
+    _dev(_shape(logits, (T, layer.n_experts), "logits"), torch.float32, "logits")
+    _dev(_shape(slot_of_expert, (layer.n_experts,), "slot_of_expert"), torch.int32,
+         "slot_of_expert")
+    _dev(_shape(acc_out, acc_shape, "acc_out"), torch.float32, "acc_out")
+    if acc_clear is not None:
+        _dev(_shape(acc_clear, acc_shape, "acc_clear"), torch.float32, "acc_clear")
+    prev_x = prev_acc = prev_y = None
+    if prev is not None:
+        prev_x, prev_acc, prev_y = prev
+        _dev(_shape(prev_x, tuple(x.shape), "prev_x"), torch.float32, "prev_x")
+        _dev(_shape(prev_acc, acc_shape, "prev_acc"), torch.float32, "prev_acc")
+        _dev(_shape(prev_y, tuple(x.shape), "prev_y"), torch.float32, "prev_y")
+    dev = x.device
+    n = T * k
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev) if idx is None else idx
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    slot = torch.empty((T, k), dtype=torch.int32, device=dev) if slot is None else slot
+    if miss_expert is None:
+        miss_expert = torch.full((n,), -1, dtype=torch.int32, device=dev)
+    if want_pairs and miss_pair is None:
+        miss_pair = torch.full((n,), -1, dtype=torch.int32, device=dev)
+    n_miss = torch.zeros((4,), dtype=torch.int32, device=dev) if n_miss is None else n_miss
+    for name, t, dt in (("idx", idx, torch.int32), ("w", w, torch.float32),
+                        ("slot", slot, torch.int32)):
+        _dev(_shape(t, (T, k), name), dt, name)
+    _dev(_at_least(miss_expert, n, "miss_expert"), torch.int32, "miss_expert")
+    if miss_pair is not None:
+        _dev(_at_least(miss_pair, n, "miss_pair"), torch.int32, "miss_pair")
+    _dev(_at_least(n_miss, 2, "n_miss"), torch.int32, "n_miss")
+    L = layer.c_struct()
+    _check(lib().moe_decode_layer_acc(ctypes.byref(L), _ptr(x), T, _ptr(logits),
+                                      _ptr(slot_of_expert), _ptr(idx), _ptr(w), _ptr(slot),
+                                      _ptr(miss_expert), _ptr(miss_pair), _ptr(n_miss),
+                                      _ptr(acc_out), _ptr(acc_clear), _ptr(prev_x),
+                                      _ptr(prev_acc), _ptr(prev_y), _stream(stream)),
+           "moe_decode_layer_acc")
+    return idx, w, slot, miss_expert, miss_pair, n_miss
+
+
+def decode_acc_finish(x, acc, y=None, stream=None):
+    """y = x + acc[0] + ... + acc[7] (moe_decode_acc_finish).  Returns y."""
+    _dev(_shape(x, (None, None), "x"), torch.float32, "x")
+    T, d = x.shape
+    _dev(_shape(acc, (ACC_BUFS, T, d), "acc"), torch.float32, "acc")
+    y = torch.empty_like(x) if y is None else y
+    _dev(_shape(y, (T, d), "y"), torch.float32, "y")
+    _check(lib().moe_decode_acc_finish(_ptr(x), _ptr(acc), T, d, _ptr(y), _stream(stream)),
+           "moe_decode_acc_finish")
+    return y
 
 
 @dataclasses.dataclass

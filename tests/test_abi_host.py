@@ -240,3 +240,31 @@ def test_stage_layer_host_checks():
     bad = soe.copy()
     bad[300] = 94                                     # the shared slot is no expert's home
     assert call(soe=bad, hs=np.where(np.arange(E) == 300, -1, hs).astype(np.int32)) == -1
+
+
+def test_decode_layer_acc_host_checks():
+    lib = _lib()
+    s = ctypes.c_void_p(0)
+    L = _layer()
+
+    def call(L=L, T=1, acc=_p(1 << 20), clear=None, px=None, pacc=None, py=None, x=_p()):
+        return lib.moe_decode_layer_acc(ctypes.byref(L), x, T, _p(), _p(), _p(), _p(), _p(), _p(),
+                                        None, _p(), acc, clear, px, pacc, py, s)
+
+    assert call(T=0) == -1
+    assert call(T=5) == -1
+    assert call(_layer(top_k=20), T=4) == -1                          # T*k > 64
+    assert call(acc=None) == -1                                       # no acc_out
+    assert call(px=_p(1 << 21)) == -1                                 # prev: all or none
+    assert call(px=_p(1 << 21), pacc=_p(1 << 22)) == -1
+    assert call(clear=_p(1 << 20)) == -1                              # acc_out == acc_clear
+    assert call(px=_p(1 << 21), pacc=_p(1 << 20), py=_p(1 << 23)) == -1   # acc_out == prev_acc
+    assert call(acc=_p((1 << 20) + 4)) == -2                          # misaligned
+    assert call(_layer(fmt=7)) == -3
+    fin = lambda T=1, d=2048, acc=_p(1 << 20): lib.moe_decode_acc_finish(_p(), acc, T, d, _p(), s)
+    assert fin(T=0) == -1
+    assert fin(T=5) == -1
+    assert fin(d=2050) == -1
+    assert fin(d=7) == -1
+    assert fin(acc=None) == -1
+    assert fin(acc=_p(4)) == -2
