@@ -357,7 +357,8 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
     c2 = synth.WORKLOADS[2]
     pools2 = build_pools(torch, synth, 2, lambda l: synth.FMT_Q2SM, dev)
     chain2 = DecodeChain(torch, bf, shape, pools2, 1, dev,
-                         [synth.make_x(2, l, 1, d, device=dev) for l in range(N_LAYERS)])
+                         [synth.make_x(2, l, 1, d, device=dev) for l in range(N_LAYERS)],
+                         acc=True)
     n_graphs = min(args.graphs, 8)
     logits2 = [torch.stack([synth.zipf_gumbel_logits(2, l, 1, E, c2["zipf_s"], device=dev, step=g)
                             for l in range(N_LAYERS)]) for g in range(n_graphs)]
@@ -373,7 +374,8 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
             tot += idx.size
     out["expert_cache"] = {
         "workload": "decode batch 1, 48 stacked layers, 94 of 512 experts + shared resident per layer, "
-                    "Zipf(1.1) routing; GPU computes the resident part and emits the miss list",
+                    "Zipf(1.1) routing; GPU computes the resident part and emits the miss list "
+                    "(one moe_decode_layer_acc call per layer)",
         "tok_s": round(steps2 / dt, 2), "ms_per_step": round(dt * 1e3 / steps2, 5),
         "hit_rate": round(hits / tot, 4),
     }
@@ -404,6 +406,8 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
             pool = synth.make_layer_pool(3, l, slot_expert, device=dev, fmt=synth.FMT_Q3G, batch=64)
             pools3.append((pool, torch.tensor(table, dtype=torch.int32, device=dev), shared_slot,
                            synth.FMT_Q3G))
+    # two kernels per layer here: at T = 4 the accumulate mode's four times as
+    # many atomic adds made the step slower (391 against 424 steps/s)
     chain3 = DecodeChain(torch, bf, shape, pools3, 4, dev,
                          [synth.make_x(3, l, 4, d, device=dev) for l in range(N_LAYERS)])
     logits3 = [torch.stack([synth.make_logits(3, l, 4, E, 1.5, device=dev, step=g)
@@ -423,7 +427,8 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
     sps = steps3 / dt
     out["verify"] = {
         "workload": "verify step: 1 real + 3 draft tokens routed independently through 48 layers "
-                    "alternating Q2SM / Q3G; each distinct chosen expert read once per step",
+                    "alternating Q2SM / Q3G; each distinct chosen expert read once per step "
+                    "(one moe_decode_layer call per layer)",
         "steps_per_s": round(sps, 2), "token_positions_per_s": round(4 * sps, 2),
         "ms_per_step": round(dt * 1e3 / steps3, 5), "mean_union_experts": round(mean_u, 2),
         "hbm_GBps_algorithmic": round(step_bytes * sps / 1e9, 1),
