@@ -36,7 +36,21 @@ class MoeLayerC(ctypes.Structure):
     ]
 
 
+class MoeStackLayerC(ctypes.Structure):
+    _fields_ = [
+        ("pool", ctypes.c_void_p), ("slot_bytes", ctypes.c_int64),
+        ("n_slots", ctypes.c_int32), ("fmt", ctypes.c_int32),
+        ("shared_slot", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("slot_of_expert", ctypes.c_void_p), ("logits", ctypes.c_void_p),
+        ("addend", ctypes.c_void_p), ("y", ctypes.c_void_p),
+        ("idx", ctypes.c_void_p), ("w", ctypes.c_void_p), ("slot", ctypes.c_void_p),
+        ("miss_expert", ctypes.c_void_p), ("miss_pair", ctypes.c_void_p),
+        ("n_miss", ctypes.c_void_p),
+    ]
+
+
 _LP = ctypes.POINTER(MoeLayerC)
+_SLP = ctypes.POINTER(MoeStackLayerC)
 SIGNATURES = {
     "moe_abi_version": (_c_int, []),
     "moe_status_str": (ctypes.c_char_p, [_c_int]),
@@ -50,6 +64,10 @@ SIGNATURES = {
     "moe_expert_ffn_decode": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
     "moe_decode_layer": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _c_sz, _vp]),
+    "moe_decode_stack_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int,
+                                                 _c_int]),
+    "moe_decode_stack": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _SLP, _vp,
+                                  _c_int, _vp, _c_sz, _vp]),
     "moe_decode_layer_acc": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_decode_acc_finish": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp]),
@@ -277,6 +295,106 @@ def decode_layer(layer: MoeLayer, x, logits, slot_of_expert, idx=None, w=None, s
                                   _ptr(miss_expert), _ptr(miss_pair), _ptr(n_miss), _ptr(y),
                                   _ptr(ws), ws.numel(), _stream(stream)), "moe_decode_layer")
     return y, idx, w, slot, miss_expert, miss_pair, n_miss
+
+
+STACK_ROUTE_AFTER_X = 1
+MAX_STACK_LAYERS = 16
+
+
+def decode_stack_workspace_bytes(d_model, d_ff, n_experts, top_k, T, n_layers) -> int:
+    return int(lib().moe_decode_stack_workspace_bytes(d_model, d_ff, n_experts, top_k, T,
+                                                      n_layers))
+
+
+def new_stack_workspace(layers, T: int, n_layers: Optional[int] = None, device=None):
+    """A zeroed workspace for decode_stack over these layers (all with the
+    shape of layers[0])."""
+    L0 = layers[0]
+    n = len(layers) if n_layers is None else n_layers
+    nb = decode_stack_workspace_bytes(L0.d_model, L0.d_ff, L0.n_experts, L0.top_k, T, n)
+    if nb == 0:
+        raise ValueError("decode_stack: sizes out of range")
+    return torch.zeros((nb,), dtype=torch.uint8, device=L0.pool.device if device is None else device)
+
+
+def decode_stack(layers, x, logits, tables, addends=None, ys=None, routing=False, ws=None,
+                 route_after_x=False, stream=None):
+    """Decode / verify through a stack of layers in one call (moe_decode_stack).
+
+    layers: list of MoeLayer (same d_model, d_ff, n_experts, top_k; formats may
+    differ); x fp32 [T, d_model]; logits fp32 [L, T, E] (or a list of [T, E]);
+    tables: list of int32 [E] slot tables; addends: None or fp32 [L, T, d]
+    (entry 0 unused).  ys: fp32 [L, T, d] outputs (allocated if None).  With
+    routing=True also returns idx, w, slot [L, T, k], miss_expert, miss_pair
+    [L, T*k] and n_miss [L, 4].  Returns a dict."""
+    nl = len(layers)
+    if nl < 1:
+        raise ValueError("decode_stack: at least one layer")
+    L0 = layers[0]
+    d, f, E, k = L0.d_model, L0.d_ff, L0.n_experts, L0.top_k
+    for Lx in layers:
+        if (Lx.d_model, Lx.d_ff, Lx.n_experts, Lx.top_k) != (d, f, E, k):
+            raise ValueError("decode_stack: every layer needs the same d_model, d_ff, n_experts, top_k")
+    _dev(_shape(x, (None, d), "x"), torch.float32, "x")
+    T = x.shape[0]
+    dev = x.device
+    if len(logits) != nl or len(tables) != nl:
+        raise ValueError("decode_stack: one logits tensor and one table per layer")
+    for l in range(nl):
+        _dev(_shape(logits[l], (T, E), f"logits[{l}]"), torch.float32, f"logits[{l}]")
+        _dev(_shape(tables[l], (E,), f"tables[{l}]"), torch.int32, f"tables[{l}]")
+    if addends is not None:
+        if len(addends) != nl:
+            raise ValueError("decode_stack: one addend per layer")
+        for l in range(nl):
+            _dev(_shape(addends[l], (T, d), f"addends[{l}]"), torch.float32, f"addends[{l}]")
+    if ys is None:
+        ys = torch.empty((nl, T, d), dtype=torch.float32, device=dev)
+    _dev(_shape(ys, (nl, T, d), "ys"), torch.float32, "ys")
+    out = {"y": ys}
+    if routing:
+        # per-layer rows padded to 16 bytes (every pointer must be 16-byte aligned)
+        n = T * k
+        pad = (n + 3) // 4 * 4
+
+        def rows(dtype, fill):
+            buf = torch.full((nl, pad), fill, dtype=dtype, device=dev)
+            return buf[:, :n]
+
+        out["idx"] = rows(torch.int32, 0).unflatten(1, (T, k))
+        out["w"] = rows(torch.float32, 0).unflatten(1, (T, k))
+        out["slot"] = rows(torch.int32, 0).unflatten(1, (T, k))
+        out["miss_expert"] = rows(torch.int32, -1)
+        out["miss_pair"] = rows(torch.int32, -1)
+        out["n_miss"] = torch.zeros((nl, 4), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = new_stack_workspace(layers, T)
+    _dev(ws, torch.uint8, "ws")
+    arr = (MoeStackLayerC * nl)()
+    for l, Lx in enumerate(layers):
+        _dev(Lx.pool, torch.uint8, "pool")
+        n_slots, sb = Lx.pool.shape
+        c = arr[l]
+        c.pool, c.slot_bytes, c.n_slots, c.fmt = Lx.pool.data_ptr(), sb, n_slots, Lx.fmt
+        c.shared_slot, c.reserved = Lx.shared_slot, 0
+        c.slot_of_expert, c.logits = tables[l].data_ptr(), logits[l].data_ptr()
+        c.addend = addends[l].data_ptr() if (addends is not None and l > 0) else None
+        c.y = ys[l].data_ptr()
+        if routing:
+            c.idx, c.w, c.slot = (out["idx"][l].data_ptr(), out["w"][l].data_ptr(),
+                                  out["slot"][l].data_ptr())
+            c.miss_expert, c.miss_pair = out["miss_expert"][l].data_ptr(), out["miss_pair"][l].data_ptr()
+            c.n_miss = out["n_miss"][l].data_ptr()
+    flags = STACK_ROUTE_AFTER_X if route_after_x else 0
+    _check(lib().moe_decode_stack(d, f, E, k, T, nl, arr, _ptr(x), flags, _ptr(ws), ws.numel(),
+                                  _stream(stream)), "moe_decode_stack")
+    out["ws"] = ws
+    return out
+
+
+def stack_error(ws: torch.Tensor) -> int:
+    """The workspace's error word (reads device memory; synchronizes)."""
+    return int(ws[:4].view(torch.int32).cpu()[0])
 
 
 ACC_BUFS = 8   # accumulation buffers of moe_decode_layer_acc

@@ -169,6 +169,53 @@ int moe_decode_layer(const moe_layer* L, const float* x, int T, const float* log
                                                 miss_expert, miss_pair, n_miss, y, ws, stream));
 }
 
+size_t moe_decode_stack_workspace_bytes(int d_model, int d_ff, int n_experts, int top_k, int T,
+                                        int n_layers) {
+  if (!valid_dims(MOE_FMT_Q2SM, d_model, d_ff)) return 0;
+  if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS || top_k < 1 || top_k > MOE_MAX_TOPK ||
+      top_k > n_experts)
+    return 0;
+  if (T < 1 || T > MOE_MAX_DECODE_T || T * top_k > MOE_MAX_DECODE_PAIRS || n_layers < 1) return 0;
+  return bitffn::decode_stack_workspace_bytes(d_model, d_ff, T, top_k, n_layers);
+}
+
+int moe_decode_stack(int d_model, int d_ff, int n_experts, int top_k, int T, int n_layers,
+                     const moe_stack_layer* layers, const float* x, int flags, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dims(MOE_FMT_Q2SM, d_model, d_ff)) return MOE_EINVAL;
+  if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS || top_k < 1 || top_k > MOE_MAX_TOPK ||
+      top_k > n_experts)
+    return MOE_EINVAL;
+  if (T < 1 || T > MOE_MAX_DECODE_T || T * top_k > MOE_MAX_DECODE_PAIRS) return MOE_EINVAL;
+  if (n_layers < 1 || (flags & ~MOE_STACK_ROUTE_AFTER_X) != 0) return MOE_EINVAL;
+  if (!layers || !x || !ws) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned256(ws)) return MOE_EALIGN;
+  if (ws_bytes < bitffn::decode_stack_workspace_bytes(d_model, d_ff, T, top_k, n_layers))
+    return MOE_ENOSPC;
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_stack_layer& S = layers[l];
+    if (!valid_fmt(S.fmt)) return MOE_EFORMAT;
+    if (S.slot_bytes != bitffn::slot_layout(S.fmt, d_model, d_ff).total) return MOE_EFORMAT;
+    if (S.n_slots < 1 || S.shared_slot < -1 || S.shared_slot >= S.n_slots || S.reserved != 0)
+      return MOE_EINVAL;
+    if (!S.pool || !S.slot_of_expert || !S.logits) return MOE_EINVAL;
+    if (l + 1 == n_layers && !S.y) return MOE_EINVAL;
+    const int routing = (S.idx ? 1 : 0) + (S.w ? 1 : 0) + (S.slot ? 1 : 0);
+    if (routing != 0 && routing != 3) return MOE_EINVAL;
+    if ((S.miss_expert != nullptr) != (S.n_miss != nullptr)) return MOE_EINVAL;
+    if (S.miss_pair && !S.miss_expert) return MOE_EINVAL;
+    if (!aligned256(S.pool)) return MOE_EALIGN;
+    const void* ptrs[] = {S.slot_of_expert, S.logits, S.addend, S.y, S.idx, S.w, S.slot,
+                          S.miss_expert, S.miss_pair, S.n_miss};
+    for (const void* q : ptrs)
+      if (q && !aligned16(q)) return MOE_EALIGN;
+    if (S.y && static_cast<const void*>(S.y) == static_cast<const void*>(x)) return MOE_EINVAL;
+  }
+  const bitffn::StackDims D{d_model, d_ff, n_experts, top_k, T};
+  return hip_status(bitffn::launch_decode_stack(D, n_layers, layers, x, nullptr, nullptr, nullptr,
+                                                flags, ws, stream));
+}
+
 int moe_decode_layer_acc(const moe_layer* L, const float* x, int T, const float* logits,
                          const int32_t* slot_of_expert, int32_t* idx, float* w, int32_t* slot,
                          int32_t* miss_expert, int32_t* miss_pair, int32_t* n_miss,

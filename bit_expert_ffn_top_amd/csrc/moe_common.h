@@ -1,9 +1,12 @@
 // Shared definitions for the gfx950 kernels of the routed-expert MoE layer.
 //
 // Slot layout (one packed expert): matrix G (2*d_ff x d_model, gate row j at
-// 2j, up row j at 2j+1) then D (d_model x d_ff).  Each matrix is row-major in
-// 32-weight blocks stored as planes (codes, [hi], scale, [min]), every plane
-// starting 256-byte aligned from the slot start.
+// 2j, up row j at 2j+1) then D (d_model x d_ff), each cut into 32-weight
+// blocks along its rows and stored unit-major: a unit is U consecutive blocks
+// of one row (U = 2 for G, 1 for D), and unit c of row r (R rows) has index
+// c*R + r, so one unit of consecutive rows is contiguous.  Each matrix is a
+// sequence of planes (codes, [hi], scale, [min]) holding its units in index
+// order, every plane starting 256-byte aligned from the slot start.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -83,6 +86,22 @@ __device__ __forceinline__ void opaque(T& v) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// v + (v of another lane of the same row of 16 lanes), DPP control CTRL
+template <int CTRL>
+__device__ __forceinline__ float add_dpp_ctrl(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                 0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each row of 16 lanes, complete in every lane of the row (a fixed
+// tree: pairs, quads, then rotations by 4 and 8).
+__device__ __forceinline__ float row16_sum_dpp(float v) {
+  v = add_dpp_ctrl<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = add_dpp_ctrl<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = add_dpp_ctrl<0x124>(v);   // row_ror:4
+  return add_dpp_ctrl<0x128>(v);   // row_ror:8
+}
 
 // ---------------------------------------------------------------------------
 // code extraction into fp16 pairs

@@ -94,6 +94,17 @@ hipError_t launch_stage_layer(const moe_layer& C, const int32_t* slot_of_expert,
                               const void* host_pool, const int32_t* host_slot_of_expert,
                               void* staging, hipStream_t s);
 
+// Decode through a stack of layers in one persistent kernel per
+// MOE_MAX_STACK_LAYERS layers (decode_stack.hip).  in_slot (with in_idx,
+// in_w) given: one layer whose routing is given instead of computed.
+struct StackDims {
+  int d, f, E, k, T;
+};
+size_t decode_stack_workspace_bytes(int d, int f, int T, int k, int n_layers);
+hipError_t launch_decode_stack(const StackDims& D, int n_layers, const moe_stack_layer* layers,
+                               const float* x, const int32_t* in_idx, const int32_t* in_slot,
+                               const float* in_w, int flags, void* ws, hipStream_t s);
+
 size_t prefill_workspace_bytes(int d, int f, int T, int k, int E);
 hipError_t launch_prefill(const moe_layer& L, const uint16_t* x_bf16, int T,
                           const int32_t* idx, const int32_t* slot, float* out_pairs,
