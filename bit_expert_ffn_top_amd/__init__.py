@@ -8,8 +8,7 @@ from ._binding import (  # noqa: F401
     abi_version,
     cache_commit, cache_count, cache_fill, cache_lookup, cache_plan, combine, decode_acc_finish,
     decode_layer, decode_layer_acc, decode_misses, decode_stack, decode_stack_workspace_bytes,
-    decode_workspace_bytes, expert_ffn_decode, MAX_STACK_LAYERS, new_stack_workspace,
-    stack_error, STACK_ROUTE_AFTER_X,
+    decode_workspace_bytes, expert_ffn_decode, new_stack_workspace,
     expert_ffn_prefill, lib, lib_path, lookup_workspace_bytes, prefill_workspace_bytes,
     route_topk, slot_bytes, stage_layer,
 )

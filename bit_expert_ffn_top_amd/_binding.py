@@ -64,10 +64,9 @@ SIGNATURES = {
     "moe_expert_ffn_decode": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
     "moe_decode_layer": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _c_sz, _vp]),
-    "moe_decode_stack_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int,
-                                                 _c_int]),
+    "moe_decode_stack_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_decode_stack": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _SLP, _vp,
-                                  _c_int, _vp, _c_sz, _vp]),
+                                  _vp, _c_sz, _vp]),
     "moe_decode_layer_acc": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_decode_acc_finish": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp]),
@@ -297,28 +296,21 @@ def decode_layer(layer: MoeLayer, x, logits, slot_of_expert, idx=None, w=None, s
     return y, idx, w, slot, miss_expert, miss_pair, n_miss
 
 
-STACK_ROUTE_AFTER_X = 1
-MAX_STACK_LAYERS = 16
+def decode_stack_workspace_bytes(d_model, d_ff, n_experts, top_k, T) -> int:
+    return int(lib().moe_decode_stack_workspace_bytes(d_model, d_ff, n_experts, top_k, T))
 
 
-def decode_stack_workspace_bytes(d_model, d_ff, n_experts, top_k, T, n_layers) -> int:
-    return int(lib().moe_decode_stack_workspace_bytes(d_model, d_ff, n_experts, top_k, T,
-                                                      n_layers))
-
-
-def new_stack_workspace(layers, T: int, n_layers: Optional[int] = None, device=None):
-    """A zeroed workspace for decode_stack over these layers (all with the
-    shape of layers[0])."""
+def new_stack_workspace(layers, T: int, device=None):
+    """A workspace for decode_stack over layers of the shape of layers[0]."""
     L0 = layers[0]
-    n = len(layers) if n_layers is None else n_layers
-    nb = decode_stack_workspace_bytes(L0.d_model, L0.d_ff, L0.n_experts, L0.top_k, T, n)
+    nb = decode_stack_workspace_bytes(L0.d_model, L0.d_ff, L0.n_experts, L0.top_k, T)
     if nb == 0:
         raise ValueError("decode_stack: sizes out of range")
-    return torch.zeros((nb,), dtype=torch.uint8, device=L0.pool.device if device is None else device)
+    return torch.empty((nb,), dtype=torch.uint8, device=L0.pool.device if device is None else device)
 
 
 def decode_stack(layers, x, logits, tables, addends=None, ys=None, routing=False, ws=None,
-                 route_after_x=False, stream=None):
+                 stream=None):
     """Decode / verify through a stack of layers in one call (moe_decode_stack).
 
     layers: list of MoeLayer (same d_model, d_ff, n_experts, top_k; formats may
@@ -385,16 +377,10 @@ def decode_stack(layers, x, logits, tables, addends=None, ys=None, routing=False
                                   out["slot"][l].data_ptr())
             c.miss_expert, c.miss_pair = out["miss_expert"][l].data_ptr(), out["miss_pair"][l].data_ptr()
             c.n_miss = out["n_miss"][l].data_ptr()
-    flags = STACK_ROUTE_AFTER_X if route_after_x else 0
-    _check(lib().moe_decode_stack(d, f, E, k, T, nl, arr, _ptr(x), flags, _ptr(ws), ws.numel(),
+    _check(lib().moe_decode_stack(d, f, E, k, T, nl, arr, _ptr(x), _ptr(ws), ws.numel(),
                                   _stream(stream)), "moe_decode_stack")
     out["ws"] = ws
     return out
-
-
-def stack_error(ws: torch.Tensor) -> int:
-    """The workspace's error word (reads device memory; synchronizes)."""
-    return int(ws[:4].view(torch.int32).cpu()[0])
 
 
 ACC_BUFS = 8   # accumulation buffers of moe_decode_layer_acc

@@ -169,29 +169,27 @@ int moe_decode_layer(const moe_layer* L, const float* x, int T, const float* log
                                                 miss_expert, miss_pair, n_miss, y, ws, stream));
 }
 
-size_t moe_decode_stack_workspace_bytes(int d_model, int d_ff, int n_experts, int top_k, int T,
-                                        int n_layers) {
+size_t moe_decode_stack_workspace_bytes(int d_model, int d_ff, int n_experts, int top_k, int T) {
   if (!valid_dims(MOE_FMT_Q2SM, d_model, d_ff)) return 0;
   if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS || top_k < 1 || top_k > MOE_MAX_TOPK ||
       top_k > n_experts)
     return 0;
-  if (T < 1 || T > MOE_MAX_DECODE_T || T * top_k > MOE_MAX_DECODE_PAIRS || n_layers < 1) return 0;
-  return bitffn::decode_stack_workspace_bytes(d_model, d_ff, T, top_k, n_layers);
+  if (T < 1 || T > MOE_MAX_DECODE_T || T * top_k > MOE_MAX_DECODE_PAIRS) return 0;
+  return bitffn::decode_stack_workspace_bytes(d_model, d_ff, T, top_k);
 }
 
 int moe_decode_stack(int d_model, int d_ff, int n_experts, int top_k, int T, int n_layers,
-                     const moe_stack_layer* layers, const float* x, int flags, void* ws,
-                     size_t ws_bytes, hipStream_t stream) {
+                     const moe_stack_layer* layers, const float* x, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
   if (!valid_dims(MOE_FMT_Q2SM, d_model, d_ff)) return MOE_EINVAL;
   if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS || top_k < 1 || top_k > MOE_MAX_TOPK ||
       top_k > n_experts)
     return MOE_EINVAL;
   if (T < 1 || T > MOE_MAX_DECODE_T || T * top_k > MOE_MAX_DECODE_PAIRS) return MOE_EINVAL;
-  if (n_layers < 1 || (flags & ~MOE_STACK_ROUTE_AFTER_X) != 0) return MOE_EINVAL;
+  if (n_layers < 1) return MOE_EINVAL;
   if (!layers || !x || !ws) return MOE_EINVAL;
   if (!aligned16(x) || !aligned256(ws)) return MOE_EALIGN;
-  if (ws_bytes < bitffn::decode_stack_workspace_bytes(d_model, d_ff, T, top_k, n_layers))
-    return MOE_ENOSPC;
+  if (ws_bytes < bitffn::decode_stack_workspace_bytes(d_model, d_ff, T, top_k)) return MOE_ENOSPC;
   for (int l = 0; l < n_layers; ++l) {
     const moe_stack_layer& S = layers[l];
     if (!valid_fmt(S.fmt)) return MOE_EFORMAT;
@@ -212,8 +210,7 @@ int moe_decode_stack(int d_model, int d_ff, int n_experts, int top_k, int T, int
     if (S.y && static_cast<const void*>(S.y) == static_cast<const void*>(x)) return MOE_EINVAL;
   }
   const bitffn::StackDims D{d_model, d_ff, n_experts, top_k, T};
-  return hip_status(bitffn::launch_decode_stack(D, n_layers, layers, x, nullptr, nullptr, nullptr,
-                                                flags, ws, stream));
+  return hip_status(bitffn::launch_decode_stack(D, n_layers, layers, x, ws, stream));
 }
 
 int moe_decode_layer_acc(const moe_layer* L, const float* x, int T, const float* logits,

@@ -499,7 +499,8 @@ __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
     const float* __restrict__ x, const int32_t* __restrict__ slot, const float* __restrict__ w,
     int T, int k, int d, int nslices, int has_shared, const float* __restrict__ part,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ host_slot, int n_experts,
-    int max_rank, int n_slots, float* __restrict__ y) {
+    int max_rank, int n_slots, float* __restrict__ y, float* __restrict__ xnext,
+    const float* __restrict__ addend) {
   extern __shared__ float red[];  // [k+1][KB_ROWS]
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -543,7 +544,10 @@ __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
       acc = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), i)),
                  red[i * KB_ROWS + rr], acc);
   if (has_shared) acc += red[k * KB_ROWS + rr];
-  y[static_cast<int64_t>(t) * d + r] = acc;
+  const int64_t o = static_cast<int64_t>(t) * d + r;
+  if (y) y[o] = acc;
+  // the next layer's input, when the step continues: y + addend
+  if (xnext) xnext[o] = addend ? acc + addend[o] : acc;
 }
 
 size_t part_bytes(int d, int f, int T, int k) {
@@ -592,12 +596,13 @@ hipError_t launch_ffn_fmt(int fmt, const FfnArgs& a, const float* x, hipStream_t
 
 hipError_t launch_combine_partials(const moe_layer& L, const float* x, int T,
                                    const int32_t* slot, const float* w, const float* part,
-                                   float* y, hipStream_t s) {
+                                   float* y, hipStream_t s, float* xnext = nullptr,
+                                   const float* addend = nullptr) {
   const dim3 grid(L.d_model / KB_ROWS, T);
   const size_t lds = static_cast<size_t>(L.top_k + 1) * KB_ROWS * 4;
   decode_combine_kernel<false><<<grid, KB_WAVES * 64, lds, s>>>(
       x, slot, w, T, L.top_k, L.d_model, L.d_ff / SLICE, L.shared_slot >= 0 ? 1 : 0, part,
-      nullptr, nullptr, 1, 0, 0, y);
+      nullptr, nullptr, 1, 0, 0, y, xnext, addend);
   return hipGetLastError();
 }
 
@@ -608,7 +613,7 @@ hipError_t launch_combine_misses(const moe_layer& H, int T, const int32_t* idx,
   const size_t lds = static_cast<size_t>(H.top_k + 1) * KB_ROWS * 4;
   decode_combine_kernel<true><<<grid, KB_WAVES * 64, lds, s>>>(
       nullptr, slot, w, T, H.top_k, H.d_model, H.d_ff / SLICE, 0, part, idx, host_slot,
-      H.n_experts, max_rank, H.n_slots, y);
+      H.n_experts, max_rank, H.n_slots, y, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -631,7 +636,8 @@ hipError_t launch_decode(const moe_layer& L, const float* x, int T, const int32_
 hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const float* logits,
                                const int32_t* slot_of_expert, int32_t* idx, float* w,
                                int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
-                               int32_t* n_miss, float* y, void* ws, hipStream_t s) {
+                               int32_t* n_miss, float* y, void* ws, hipStream_t s, float* xnext,
+                               const float* addend) {
   FfnArgs a = ffn_args(L, T, nullptr, ws);
   a.logits = logits;
   a.table = slot_of_expert;
@@ -643,7 +649,7 @@ hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const 
   a.o_n_miss = n_miss;
   const hipError_t e = launch_ffn_fmt<kRoute>(L.fmt, a, x, s);
   if (e != hipSuccess) return e;
-  return launch_combine_partials(L, x, T, slot, w, a.part, y, s);
+  return launch_combine_partials(L, x, T, slot, w, a.part, y, s, xnext, addend);
 }
 
 hipError_t launch_decode_layer_acc(const moe_layer& L, const float* x, int T, const float* logits,

@@ -54,11 +54,14 @@ hipError_t launch_decode(const moe_layer& L, const float* x, int T, const int32_
                          hipStream_t s);
 
 // Route, look up and run the decode layer in two launches (routing runs in
-// every FFN workgroup; workgroup (0, 0) writes the routing outputs).
+// every FFN workgroup; workgroup (0, 0) writes the routing outputs).  y may be
+// null if xnext is given; xnext (optional) receives y + addend (addend
+// optional), the next layer's input in a decode step.
 hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const float* logits,
                                const int32_t* slot_of_expert, int32_t* idx, float* w,
                                int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
-                               int32_t* n_miss, float* y, void* ws, hipStream_t s);
+                               int32_t* n_miss, float* y, void* ws, hipStream_t s,
+                               float* xnext = nullptr, const float* addend = nullptr);
 // Missed pairs of a decode step computed from a second pool (the host tier,
 // `host_pool_dev` its device-side address) and added into y.
 hipError_t launch_decode_layer_acc(const moe_layer& L, const float* x, int T, const float* logits,
@@ -94,16 +97,14 @@ hipError_t launch_stage_layer(const moe_layer& C, const int32_t* slot_of_expert,
                               const void* host_pool, const int32_t* host_slot_of_expert,
                               void* staging, hipStream_t s);
 
-// Decode through a stack of layers in one persistent kernel per
-// MOE_MAX_STACK_LAYERS layers (decode_stack.hip).  in_slot (with in_idx,
-// in_w) given: one layer whose routing is given instead of computed.
+// Decode through a stack of layers, one moe_decode_layer step per layer whose
+// combine also forms the next layer's input (decode_stack.hip).
 struct StackDims {
   int d, f, E, k, T;
 };
-size_t decode_stack_workspace_bytes(int d, int f, int T, int k, int n_layers);
+size_t decode_stack_workspace_bytes(int d, int f, int T, int k);
 hipError_t launch_decode_stack(const StackDims& D, int n_layers, const moe_stack_layer* layers,
-                               const float* x, const int32_t* in_idx, const int32_t* in_slot,
-                               const float* in_w, int flags, void* ws, hipStream_t s);
+                               const float* x, void* ws, hipStream_t s);
 
 size_t prefill_workspace_bytes(int d, int f, int T, int k, int E);
 hipError_t launch_prefill(const moe_layer& L, const uint16_t* x_bf16, int T,

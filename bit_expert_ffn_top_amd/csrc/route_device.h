@@ -133,6 +133,87 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ logits, int
   topk_select<MAXIT>(lg, T, E, k, s, [] {});
 }
 
+// k-th largest of one 32-bit value per lane (k <= 64): the largest tau with
+// at least k values >= tau, found bit by bit with ballot counts.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k) {
+  uint32_t tau = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    if (__popcll(__ballot(v >= cand)) >= k) tau = cand;
+  }
+  return tau;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// k rounds of the wavefront's largest remaining key (lane-local maximum, then
+// a butterfly of 64-bit maxima); the winner is removed.  top[r] = key of rank r.
+template <int NJ>
+__device__ __forceinline__ void wave_topk_rounds(uint64_t (&key)[NJ], int k, uint64_t* top) {
+  const int lane = threadIdx.x & 63;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int j = 1; j < NJ; ++j) best = key[j] > best ? key[j] : best;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint64_t o = __shfl_xor(best, off, 64);
+      best = o > best ? o : best;
+    }
+    if (lane == 0) top[r] = best;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) key[j] = key[j] == best ? 0ull : key[j];   // keys are never 0
+  }
+}
+
+// Top-k keys of one token in one whole wavefront: lane l holds the keys of
+// experts 64j + l (j < NJ; key = orderable value << 32 | ~id, 0 for experts
+// >= E, below every real key).  A bound first: tau0, the k-th largest of the
+// 64 lane maxima (by value), has at least k keys whose value is >= tau0, so
+// the top k are among them.  Those candidates (usually a little over k) are
+// gathered one per lane and ranked among themselves by (value desc, id asc);
+// the first k, in rank order, go to top[0..k).  When more than 64 keys pass
+// the bound (many equal values), k rounds of the largest remaining key are
+// taken instead.  scratch: 64 uint64 of LDS for this wavefront.  Same keys,
+// same order as ranking every key.
+template <int NJ>
+__device__ __forceinline__ void wave_topk_keys(uint64_t (&key)[NJ], int k, uint64_t* top,
+                                               uint64_t* scratch) {
+  const int lane = threadIdx.x & 63;
+  uint64_t m = key[0];
+#pragma unroll
+  for (int j = 1; j < NJ; ++j) m = key[j] > m ? key[j] : m;
+  const uint32_t tau0 = wave_kth_largest(static_cast<uint32_t>(m >> 32), k);
+  const uint64_t below = (1ull << lane) - 1ull;
+  int n_c = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) n_c += __popcll(__ballot(static_cast<uint32_t>(key[j] >> 32) >= tau0));
+  if (n_c <= 64) {
+    int pos = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const bool c = static_cast<uint32_t>(key[j] >> 32) >= tau0;
+      const uint64_t sel = __ballot(c);
+      if (c) scratch[pos + __popcll(sel & below)] = key[j];
+      pos += __popcll(sel);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t mine = lane < n_c ? scratch[lane] : 0ull;
+    int rank = 0;
+    for (int q = 0; q < n_c; ++q) rank += readlane_u64(mine, q) > mine ? 1 : 0;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < n_c && rank < k) top[rank] = mine;
+  } else {
+    wave_topk_rounds<NJ>(key, k, top);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Routing weights of one token from its top keys (called by one whole
 // wavefront; lane r < k gets choice r): w_r = exp(l_r - l_0) / sum_j exp(l_j - l_0),
 // summed in a fixed xor tree.

@@ -201,16 +201,16 @@ int moe_decode_layer(const moe_layer* L, const float* x, int T,
  * checked in the same pass, the weights read once for all of them).
  * For l = 0 .. n_layers-1, with T = 1..4 tokens routed independently:
  *   x_0 = x,   x_l = y_{l-1} + layers[l].addend   (addend NULL: + 0)
- *   y_l = what moe_decode_layer computes for layer l from x_l, its logits
- *         and its slot table (resident chosen experts in k-slot order, the
- *         shared expert last; misses left out and listed).
+ *   y_l = moe_decode_layer's y for layer l from x_l, its logits and its slot
+ *         table (resident chosen experts in k-slot order, the shared expert
+ *         last; misses left out and listed), bit for bit.
  * The addend stands for whatever the caller's model adds to the residual
  * between two MoE layers; the call itself only chains y into the next x.
- * Every layer's expert FFN sums run in a fixed order that does not depend on
- * the other tokens of the step: a token's y_l has the same bits at T = 1 and
- * as one of T = 4 tokens, and two calls on the same inputs give the same bits.
- * (The order differs from moe_expert_ffn_decode's, so the two agree to fp32
- * rounding, not bitwise.)
+ * Per layer the call runs moe_decode_layer's two kernels; the second also
+ * forms x_{l+1}, and layer l+1's kernels start once it is complete.  Every
+ * sum has a fixed order that does not depend on the other tokens of the
+ * step: a token's y_l has the same bits at T = 1 and as one of T = 4 tokens,
+ * and two calls on the same inputs give the same bits.
  *   layers    (host) array of n_layers descriptors, read during the call:
  *             pool, slot_bytes, n_slots, fmt (may differ between layers),
  *             shared_slot as in moe_layer; slot_of_expert int32 [n_experts];
@@ -221,26 +221,11 @@ int moe_decode_layer(const moe_layer* L, const float* x, int T,
  *             moe_cache_lookup (miss_expert and n_miss together or neither;
  *             miss_pair may be NULL).
  *   x         fp32 [T][d_model], the first layer's input.
- *   flags     MOE_STACK_ROUTE_AFTER_X: route layer l only once x_l is
- *             complete.  Without it, layer l+1's routing (its logits are an
- *             input) runs while the kernel waits inside layer l.
  * Limits: as moe_decode_layer (T * top_k <= 64, n_experts <= 1024, d_model a
  * multiple of 64 up to 2048, d_ff a multiple of 32 up to 4096),
  * 1 <= n_layers.  Outputs may not overlap x or any input.
- * Execution: one kernel launch per MOE_MAX_STACK_LAYERS layers, with one
- * workgroup on every compute unit, all resident at once (cooperative
- * launch); the workgroups meet at two barriers per layer.  Work that
- * occupies compute units at the same time delays the call; a device that
- * cannot hold the grid gives MOE_EHIP.
- * ws: at least moe_decode_stack_workspace_bytes() bytes, 256-byte aligned,
- * zero before its first use.  It keeps barrier state from call to call, so
- * calls that share a workspace must be ordered (one stream) and must not
- * overlap.  Its first uint32 is an error word: non-zero after a call means a
- * barrier wait gave up (every later wait of the call then returns at once),
- * the outputs are not valid, and the workspace must be zeroed again. */
-#define MOE_MAX_STACK_LAYERS 16
-#define MOE_STACK_ROUTE_AFTER_X 1
-
+ * ws: at least moe_decode_stack_workspace_bytes() bytes, 256-byte aligned;
+ * its contents on entry do not matter. */
 typedef struct moe_stack_layer {
   const void* pool;
   int64_t slot_bytes;
@@ -261,12 +246,11 @@ typedef struct moe_stack_layer {
 } moe_stack_layer;
 
 /* (host) Workspace bytes of moe_decode_stack (0 for sizes it does not take). */
-size_t moe_decode_stack_workspace_bytes(int d_model, int d_ff, int n_experts, int top_k, int T,
-                                        int n_layers);
+size_t moe_decode_stack_workspace_bytes(int d_model, int d_ff, int n_experts, int top_k, int T);
 
 int moe_decode_stack(int d_model, int d_ff, int n_experts, int top_k, int T, int n_layers,
-                     const moe_stack_layer* layers, const float* x, int flags, void* ws,
-                     size_t ws_bytes, hipStream_t stream);
+                     const moe_stack_layer* layers, const float* x, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
 
 /* moe_decode_layer with the combine split in two, so that a step of several
  * layers runs one kernel per layer (same pages and definitions as

@@ -4,9 +4,9 @@ Per layer the routing outputs must equal the oracle's (indices, slots and miss
 lists exactly, weights to 1e-6) and y the oracle's layer output within the fp32
 bar, each layer fed the input the kernel formed (x_l = y_{l-1} + addend_l,
 recomputed here in fp32 from the returned y, so errors do not compound).
-Bitwise properties: reruns, the route-after-x flag, each token of a 4-token
-step against the same token alone, many layers (several launches) against
-one layer per call, graph replays against the eager call.
+Bitwise properties: reruns, each token of a 4-token step against the same
+token alone, many layers in one call against one layer per call, one layer
+against moe_decode_layer, graph replays against the eager call.
 """
 import numpy as np
 import pytest
@@ -33,7 +33,6 @@ def _run(layers, x, logits, tables, adds, **kw):
     out = bf.decode_stack([L.layer_obj for L in layers], x, logits, tables, addends=adds,
                           routing=True, **kw)
     torch.cuda.synchronize()
-    assert bf.stack_error(out["ws"]) == 0
     return out
 
 
@@ -121,8 +120,8 @@ def test_stack_full_size(T, fmts):
 
 
 def test_stack_bitwise_properties():
-    """Reruns and the route-after-x flag give the same bits; each token of a
-    4-token step has the bits it gets alone; a fresh workspace too."""
+    """Reruns (a workspace reused, one filled with garbage) give the same
+    bits; each token of a 4-token step has the bits it gets alone."""
     import bit_expert_ffn_top_amd as bf
     dev = need_gpu()
     shape = synth.LayerShape(200, 8, 512, 256, True)
@@ -134,7 +133,8 @@ def test_stack_bitwise_properties():
     a = _run(layers, x, logits, tables, adds)
     ws = a["ws"]
     b = _run(layers, x, logits, tables, adds, ws=ws)
-    c = _run(layers, x, logits, tables, adds, route_after_x=True, ws=ws)
+    ws.fill_(0xA5)
+    c = _run(layers, x, logits, tables, adds, ws=ws)
     for key in ("y", "idx", "w", "slot", "n_miss"):
         assert torch.equal(a[key], b[key]), key
         assert torch.equal(a[key], c[key]), key
@@ -148,7 +148,7 @@ def test_stack_bitwise_properties():
 
 
 def test_stack_many_layers_equals_one_layer_calls():
-    """18 layers (two launches) against 18 one-layer calls chained here with
+    """18 layers in one call against 18 one-layer calls chained here with
     the same fp32 additions: the same bits."""
     import bit_expert_ffn_top_amd as bf
     dev = need_gpu()
@@ -172,8 +172,8 @@ def test_stack_many_layers_equals_one_layer_calls():
 
 
 def test_stack_against_decode_layer():
-    """One layer: within the fp32 bar of moe_decode_layer (a different sum
-    order), with identical routing outputs."""
+    """One layer: the bits of moe_decode_layer (the same two kernels), with
+    identical routing outputs."""
     import bit_expert_ffn_top_amd as bf
     dev = need_gpu()
     shape = synth.LayerShape(512, 10, 1024, 384, True)
@@ -186,7 +186,7 @@ def test_stack_against_decode_layer():
     torch.cuda.synchronize()
     assert torch.equal(out["idx"][0], idx) and torch.equal(out["w"][0], w)
     assert torch.equal(out["slot"][0], slot) and torch.equal(out["n_miss"][0][:2], nm[:2])
-    check_close(out["y"][0].cpu().numpy(), y.cpu().double().numpy(), x.cpu().numpy())
+    assert torch.equal(out["y"][0], y)
 
 
 def test_stack_graph_replays():
@@ -223,4 +223,31 @@ def test_stack_graph_replays():
         got = ys.clone()
         eager = _run(layers, x, list(lg), tables, adds)
         assert torch.equal(got, eager["y"]), step
-    assert bf.stack_error(ws) == 0
+
+
+@pytest.mark.parametrize("E,k", [(300, 12), (512, 10), (1024, 16), (64, 16)])
+def test_stack_routing_edge_cases(E, k):
+    """Equal logits (ties go to the smaller expert id, more than 64 keys tied
+    at the bound), NaN (ranks as -inf), -0.0 against +0.0, infinities, and two
+    halves of 512 experts: routing outputs equal the oracle's, y within the bar."""
+    dev = need_gpu()
+    shape = synth.LayerShape(E, k, 128, 64, True)
+    layers, tabs = _layers(0, shape, (synth.FMT_Q2SM, synth.FMT_Q3G), 0.9, dev)
+    tables = [torch.tensor(t, dtype=torch.int32, device=dev) for t in tabs]
+    T = 4
+    x, _, adds = _inputs(0, shape, T, 2, dev, sigma=1.0, step=2)
+    lg = torch.zeros((T, E))
+    lg[0] = 1.0                                    # all equal: ids 0..k-1
+    lg[1, ::7] = 2.0                               # ties spread over groups and halves
+    lg[1, 5] = float("nan")
+    lg[2, :E // 3] = -1.0
+    lg[2, E // 3:E // 3 + 10] = -0.0
+    lg[2, E // 2:E // 2 + 5] = 0.0
+    lg[2, E - 1] = float("inf")
+    lg[3] = torch.arange(E, dtype=torch.float32).flip(0) % 17
+    lg2 = synth.make_logits(0, 9, T, E, 1.5)
+    lg2[1, 3] = float("-inf")
+    logits = [lg.to(dev), lg2.to(dev)]
+    out = _run(layers, x, logits, tables, adds)
+    _check_against_oracle(layers, x, logits, adds, out, tabs)
+    assert list(out["idx"][0][0].cpu().numpy()) == list(range(k))
