@@ -6,11 +6,14 @@ Headline (one JSON line on stdout): MoE decode tokens/s for batch 1 through
 48 stacked layers shaped like the pages' model (512 experts per layer, top-10
 plus one shared expert, d_model 2048, d_ff 768, every expert resident,
 2-bit scale+min blocks at 3.0 bits per weight).  A step is one token through
-all 48 layers: router top-k, cache lookup and the decode FFN with its
-routing-weighted combine (one moe_decode_layer call per layer), with fresh
-router logits for every token and layer and each layer's own seeded input
-x.  Inputs are seeded synthetic tensors, resident in HBM before timing
-starts.  Steps are replayed from HIP graphs.
+all 48 layers in one moe_decode_stack call: per layer router top-k, cache
+lookup, the decode FFN and its routing-weighted combine, whose output plus a
+per-layer addend is the next layer's input (x_{l+1} = y_l + a_{l+1}; the
+addends stand in for the rest of the model between two MoE layers and are
+chosen so that each layer's input stays near its own seeded draw).  Router
+logits are fresh for every token and layer.  Inputs are seeded synthetic
+tensors, resident in HBM before timing starts.  Steps are replayed from HIP
+graphs.
 
 Extra objects on the same line: the decode kernel's roofline (HBM), the
 expert-cache workload (94 of 512 experts resident, about 72% hits), the
@@ -36,6 +39,7 @@ N_LAYERS = 48
 COPY_BYTES = 512 << 20         # calibration copy of the counter pass
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_layer_e512_k10_d2048_f768_q2sm_traffic.txt")
 DECODE_SOURCES = ["bit_expert_ffn_top_amd/csrc/ffn_decode.hip",
+                  "bit_expert_ffn_top_amd/csrc/decode_stack.hip",
                   "bit_expert_ffn_top_amd/csrc/moe_common.h",
                   "bit_expert_ffn_top_amd/csrc/route_device.h"]
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
@@ -85,20 +89,65 @@ def build_pools(torch, synth, cfg, fmt_of_layer, dev, n_layers=N_LAYERS, residen
     return out
 
 
-class DecodeChain:
-    """48 layers of decode for T tokens, with preallocated buffers, so that a
-    whole step can be captured in a graph.  Each layer reads its own seeded
-    input x_l (a stand-in for the normalised residual stream: with no norm
-    between layers, y = x + MoE(x) fed back grows without bound) and writes
-    its y to a scratch buffer."""
+class StackStep:
+    """Steps of T tokens through a stack of layers, one moe_decode_stack call
+    each, with preallocated buffers so that a step can be captured in a
+    graph.  Step g uses logit set g and addend set g; only the last layer's y
+    is written (with routing=True every layer's routing outputs and miss
+    lists are written too)."""
 
-    def __init__(self, torch, bf, shape, pools, T, dev, xs, tiers=None, host_table=None,
-                 max_rank=None, counts=None, acc=False):
+    def __init__(self, torch, bf, shape, pools, T, dev, x0, logit_sets, routing=False):
         self.torch, self.bf = torch, bf
         self.T = T
-        self.acc = acc
+        self.layers = [bf.MoeLayer(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k, fmt,
+                                   pool, shared_slot) for pool, _, shared_slot, fmt in pools]
+        self.tables = [t for _, t, _, _ in pools]
+        self.x0 = x0
+        self.logit_sets = logit_sets
+        self.add_sets = None
+        self.routing = routing
+        self.ws = bf.new_stack_workspace(self.layers, T)
+        self.y = torch.empty((T, shape.d_model), dtype=torch.float32, device=dev)
+
+    def set_addends(self, xs):
+        """Addends that keep layer l's input near xs[l] for every logit set:
+        a_l = xs[l] - y_{l-1}, y_{l-1} the output of layer l-1 run alone on
+        xs[l-1] (one-layer moe_decode_stack calls)."""
+        torch, bf = self.torch, self.bf
+        self.add_sets = []
+        for lg in self.logit_sets:
+            adds = [torch.zeros_like(self.x0)]
+            for l in range(1, len(self.layers)):
+                y = bf.decode_stack([self.layers[l - 1]], xs[l - 1], [lg[l - 1]],
+                                    [self.tables[l - 1]], ys=torch.empty_like(self.x0),
+                                    ws=self.ws)["y"]
+                adds.append((xs[l] - y).contiguous())
+            self.add_sets.append(torch.stack(adds))
+        torch.cuda.synchronize()
+
+    def step(self, g):
+        out = self.bf.decode_stack(self.layers, self.x0, self.logit_sets[g], self.tables,
+                                   addends=self.add_sets[g], ys=self.y, ws=self.ws,
+                                   routing=self.routing)
+        if self.routing:
+            self.routing_out = out
+        return self.y
+
+
+class DecodeChain:
+    """48 layers of decode for T tokens, one moe_decode_layer call per layer
+    (plus moe_decode_misses from a host tier and cache counting when given),
+    with preallocated buffers, so that a whole step can be captured in a
+    graph.  Each layer reads its own seeded input x_l and writes its y to a
+    scratch buffer."""
+
+    def __init__(self, torch, bf, shape, pools, T, dev, xs, logit_sets, tiers=None,
+                 host_table=None, max_rank=None, counts=None):
+        self.torch, self.bf = torch, bf
+        self.T = T
         self.tiers, self.host_table, self.max_rank = tiers, host_table, max_rank
         self.counts = counts
+        self.logit_sets = logit_sets
         self.layers = [bf.MoeLayer(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k, fmt,
                                    pool, shared_slot) for pool, _, shared_slot, fmt in pools]
         self.tables = [t for _, t, _, _ in pools]
@@ -113,30 +162,13 @@ class DecodeChain:
         self.ws = torch.empty((ws,), dtype=torch.uint8, device=dev)
         self.xs = xs
         self.y = torch.empty((T, d), dtype=torch.float32, device=dev)
-        if acc:
-            # layer l adds into buffer l % 3 and clears (l + 1) % 3; with a
-            # multiple of 3 layers the last one clears buffer 0 for the next step
-            assert len(self.layers) % 3 == 0 and tiers is None and counts is None
-            self.accs = [torch.zeros((bf.ACC_BUFS, T, d), dtype=torch.float32, device=dev)
-                         for _ in range(3)]
 
-    def step(self, logits):
-        """logits [n_layers, T, E].  One moe_decode_layer call per layer:
-        route, look up, expert FFN, combine; with host tiers, then one
-        moe_decode_misses call that adds the missed experts.  acc: one
-        moe_decode_layer_acc call per layer, each forming the previous
-        layer's y, and a finish call for the last layer's y."""
+    def step(self, g):
+        """One moe_decode_layer call per layer (route, look up, expert FFN,
+        combine) on logit set g; with host tiers, then one moe_decode_misses
+        call that adds the missed experts."""
         bf = self.bf
-        if self.acc:
-            n = len(self.layers)
-            for l, L in enumerate(self.layers):
-                prev = (self.xs[l - 1], self.accs[(l - 1) % 3], self.y) if l else None
-                bf.decode_layer_acc(L, self.xs[l], logits[l], self.tables[l], self.accs[l % 3],
-                                    acc_clear=self.accs[(l + 1) % 3], prev=prev, idx=self.idx,
-                                    w=self.w, slot=self.slot, miss_expert=self.miss_e,
-                                    miss_pair=self.miss_p, n_miss=self.n_miss)
-            bf.decode_acc_finish(self.xs[n - 1], self.accs[(n - 1) % 3], y=self.y)
-            return self.y
+        logits = self.logit_sets[g]
         for l, L in enumerate(self.layers):
             bf.decode_layer(L, self.xs[l], logits[l], self.tables[l], idx=self.idx, w=self.w,
                             slot=self.slot, miss_expert=self.miss_e, miss_pair=self.miss_p,
@@ -149,8 +181,9 @@ class DecodeChain:
         return self.y
 
 
-def time_graph_steps(torch, chain, logits_sets, steps, warmup, n_graphs):
-    """Capture n_graphs token steps (each its own logits) and replay them.
+def time_graph_steps(torch, chain, steps, warmup, n_graphs):
+    """Capture n_graphs token steps (chain.step(g), each its own inputs) and
+    replay them in turn.
     Returns (wall seconds, event milliseconds) over the timed replays; the
     events are recorded on the stream the graphs run on."""
     graphs = []
@@ -158,13 +191,13 @@ def time_graph_steps(torch, chain, logits_sets, steps, warmup, n_graphs):
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         for g in range(min(3, n_graphs)):       # warm the allocator and the code paths
-            chain.step(logits_sets[g])
+            chain.step(g)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     for g in range(n_graphs):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            chain.step(logits_sets[g])
+            chain.step(g)
         graphs.append(graph)
     torch.cuda.synchronize()
     for i in range(warmup):
@@ -192,10 +225,11 @@ def sources_digest(paths):
 
 
 def measured_traffic(path=TRAFFIC_FILE, sources=DECODE_SOURCES):
-    """HBM bytes per call from a committed counter summary (FETCH_SIZE +
-    WRITE_SIZE, calibrated on a plain copy); None when the file is missing or
-    the kernels' sources changed since it was taken.  Defaults: one
-    moe_decode_layer call of the decode workload."""
+    """HBM bytes per unit from a committed counter summary (FETCH_SIZE +
+    WRITE_SIZE per dispatch, scaled by what the counters read for a plain
+    copy of known size); None when the file is missing or the kernels'
+    sources changed since it was taken.  Defaults: one layer of the decode
+    step (its route+FFN kernel and its combine kernel)."""
     try:
         kv = {}
         with open(path) as f:
@@ -210,14 +244,14 @@ def measured_traffic(path=TRAFFIC_FILE, sources=DECODE_SOURCES):
         return None
 
 
-def counter_pass(torch, bf, synth, chain, logits_sets, dev):
-    """Eager decode layer calls, then one device copy of COPY_BYTES (the
+def counter_pass(torch, bf, synth, chain, dev):
+    """Two eager decode steps, then one device copy of COPY_BYTES (the
     counters' calibration); run under rocprofv3 --pmc."""
     for g in range(2):
-        chain.step(logits_sets[g])
+        chain.step(g)
     torch.cuda.synchronize()
     calibration_copy(torch, dev)
-    log(f"counter pass: {2 * len(chain.layers)} decode layer calls, copy of {COPY_BYTES} bytes")
+    log(f"counter pass: {2 * len(chain.layers)} decode layers, copy of {COPY_BYTES} bytes")
 
 
 def calibration_copy(torch, dev):
@@ -230,12 +264,13 @@ def calibration_copy(torch, dev):
     torch.cuda.synchronize()
 
 
-def decode_bytes_per_call(synth, shape, fmt, T, n_union):
-    """Algorithmic HBM bytes of one moe_decode_layer call: the packed bytes of
-    every distinct resident expert chosen (plus the shared one) read once,
-    x and the router logits and slot table read, y written."""
+def stack_layer_bytes(synth, shape, fmt, T, n_union):
+    """Algorithmic HBM bytes of one layer of a decode step: the packed bytes
+    of every distinct resident expert chosen (plus the shared one) read once;
+    the layer's input x, the addend, the router logits and the slot table
+    read; the next input written."""
     sb = synth.slot_bytes(fmt, shape.d_model, shape.d_ff)
-    return (n_union * sb + 2 * T * shape.d_model * 4 + T * shape.n_experts * 4
+    return (n_union * sb + 3 * T * shape.d_model * 4 + T * shape.n_experts * 4
             + shape.n_experts * 4)
 
 
@@ -271,32 +306,27 @@ def main():
         return
 
     # ---------------- decode (headline) ----------------
-    xs = [synth.make_x(1, l, 1, d, device=dev) for l in range(N_LAYERS)]
-    chain = DecodeChain(torch, bf, shape, pools, 1, dev, xs, acc=True)
     n_graphs = args.graphs
-    logits_sets = [torch.stack([synth.make_logits(1, l, 1, E, 1.5, device=dev, step=g)
-                                for l in range(N_LAYERS)]) for g in range(n_graphs)]
+    xs = [synth.make_x(1, l, 1, d, device=dev) for l in range(N_LAYERS)]
+    logit_sets = [torch.stack([synth.make_logits(1, l, 1, E, 1.5, device=dev, step=g)
+                               for l in range(N_LAYERS)]) for g in range(n_graphs)]
+    chain = StackStep(torch, bf, shape, pools, 1, dev, xs[0], logit_sets)
+    chain.set_addends(xs)
     if args.counters:
-        counter_pass(torch, bf, synth, chain, logits_sets, dev)
+        counter_pass(torch, bf, synth, chain, dev)
         return
-    dt, ev_ms, graphs = time_graph_steps(torch, chain, logits_sets, args.steps, args.warmup,
-                                         n_graphs)
+    dt, ev_ms, graphs = time_graph_steps(torch, chain, args.steps, args.warmup, n_graphs)
+    if not bool(torch.isfinite(chain.y).all()):
+        raise RuntimeError("decode step: non-finite output")
     tok_s = args.steps / dt
     ms_step = dt * 1e3 / args.steps
     log(f"decode: {tok_s:.1f} tok/s, {ms_step * 1e3:.1f} us/token ({ms_step * 1e3 / N_LAYERS:.2f} us/layer)")
     del graphs
-    # the same step with the two-kernel layer call (FFN kernel + combine kernel)
-    chain2k = DecodeChain(torch, bf, shape, pools, 1, dev, xs)
-    dt2, _, graphs = time_graph_steps(torch, chain2k, logits_sets, args.steps, args.warmup,
-                                      n_graphs)
-    tok_s_2k = args.steps / dt2
-    log(f"decode, two kernels per layer: {tok_s_2k:.1f} tok/s")
-    del graphs, chain2k
-    call_us = ev_ms * 1e3 / (args.steps * N_LAYERS)
-    bytes_call = decode_bytes_per_call(synth, shape, synth.FMT_Q2SM, 1, k + 1)
-    ach = bytes_call / (call_us * 1e-6) / 1e9
-    log(f"decode layer call: {call_us:.2f} us avg (events), {ach:.0f} GB/s algorithmic")
-    token_bytes = N_LAYERS * bytes_call
+    layer_us = ev_ms * 1e3 / (args.steps * N_LAYERS)
+    bytes_layer = stack_layer_bytes(synth, shape, synth.FMT_Q2SM, 1, k + 1)
+    ach = bytes_layer / (layer_us * 1e-6) / 1e9
+    log(f"decode layer: {layer_us:.2f} us avg (events), {ach:.0f} GB/s algorithmic")
+    token_bytes = N_LAYERS * bytes_layer
     result = {
         "metric": "MoE decode tok/s (48 layers, bs=1)",
         "value": round(tok_s, 2),
@@ -311,9 +341,10 @@ def main():
         "dtype": "f32 (2-bit scale+min weight blocks)",
         "data": "synthetic (seeded; weights ~N(0,0.02) block-quantized, x ~N(0,1), logits ~N(0,1.5) fresh per token and layer)",
         "config": {
-            "workload": "decode, batch 1, 48 stacked MoE layers: E=512 routed (top-10) + 1 shared expert, "
-                        "d_model=2048, d_ff=768, all experts resident under a seeded slot permutation, "
-                        "Q2SM blocks (3.0 bits/weight)",
+            "workload": "decode, batch 1, 48 stacked MoE layers chained through their outputs: "
+                        "E=512 routed (top-10) + 1 shared expert, d_model=2048, d_ff=768, all "
+                        "experts resident under a seeded slot permutation, Q2SM blocks "
+                        "(3.0 bits/weight)",
             "tokens_per_step": 1, "layers": N_LAYERS, "experts_per_layer": E, "top_k": k,
             "shared_experts": 1, "d_model": d, "d_ff": f, "format": "Q2SM",
         },
@@ -321,20 +352,19 @@ def main():
         "token_hbm_GBps_algorithmic": round(token_bytes * tok_s / 1e9, 1),
         "token_frac_of_hbm_peak": round(token_bytes * tok_s / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {
-            "kernel": "moe_decode_layer_acc call = decode_ffn_kernel in accumulate mode (routing "
-                      "+ gate/up + SiLU + down + weighted atomic adds into 8 buffers; its side "
-                      "workgroups clear the next buffers and form the previous layer's y), one "
-                      "call per layer, plus one finish kernel per token for the last layer's y",
+            "kernel": "one layer of moe_decode_stack: decode_ffn_kernel (routing + gate/up + "
+                      "SiLU + down partials) then decode_combine_kernel (fixed-order sum, "
+                      "y + addend into the next layer's input); the unit is the layer, timed "
+                      "over the graph replays",
             "bound": "hbm",
             "achieved": round(ach, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
-            "avg_call_us": round(call_us, 3),
-            "bytes_per_call": bytes_call,
+            "avg_layer_us": round(layer_us, 3),
+            "bytes_per_layer": bytes_layer,
         },
-        "two_kernel_layer_tok_s": round(tok_s_2k, 2),
     }
 
     extra = {}
@@ -356,14 +386,14 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
     t0 = time.perf_counter()
     c2 = synth.WORKLOADS[2]
     pools2 = build_pools(torch, synth, 2, lambda l: synth.FMT_Q2SM, dev)
-    chain2 = DecodeChain(torch, bf, shape, pools2, 1, dev,
-                         [synth.make_x(2, l, 1, d, device=dev) for l in range(N_LAYERS)],
-                         acc=True)
     n_graphs = min(args.graphs, 8)
     logits2 = [torch.stack([synth.zipf_gumbel_logits(2, l, 1, E, c2["zipf_s"], device=dev, step=g)
                             for l in range(N_LAYERS)]) for g in range(n_graphs)]
+    xs2 = [synth.make_x(2, l, 1, d, device=dev) for l in range(N_LAYERS)]
+    chain2 = StackStep(torch, bf, shape, pools2, 1, dev, xs2[0], logits2, routing=True)
+    chain2.set_addends(xs2)
     steps2 = max(20, args.steps // 2)
-    dt, _, graphs = time_graph_steps(torch, chain2, logits2, steps2, 5, n_graphs)
+    dt, _, graphs = time_graph_steps(torch, chain2, steps2, 5, n_graphs)
     del graphs
     hits = tot = 0
     for g in range(n_graphs):
@@ -374,15 +404,14 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
             tot += idx.size
     out["expert_cache"] = {
         "workload": "decode batch 1, 48 stacked layers, 94 of 512 experts + shared resident per layer, "
-                    "Zipf(1.1) routing; GPU computes the resident part and emits the miss list "
-                    "(one moe_decode_layer_acc call per layer)",
+                    "Zipf(1.1) routing; GPU computes the resident part and writes every layer's "
+                    "routing outputs and miss list (one moe_decode_stack call per token)",
         "tok_s": round(steps2 / dt, 2), "ms_per_step": round(dt * 1e3 / steps2, 5),
         "hit_rate": round(hits / tot, 4),
     }
     log(f"expert cache: {steps2 / dt:.1f} tok/s, hit rate {hits / tot:.3f} ({time.perf_counter() - t0:.1f} s)")
     del chain2
     tiers, host_table = build_host_tiers(torch, bf, synth, shape, dev)
-    xs2 = [synth.make_x(2, l, 1, d, device=dev) for l in range(N_LAYERS)]
     out["expert_cache"].update(run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev,
                                              steps2, n_graphs, tot - hits, tiers, host_table,
                                              xs2))
@@ -406,14 +435,13 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
             pool = synth.make_layer_pool(3, l, slot_expert, device=dev, fmt=synth.FMT_Q3G, batch=64)
             pools3.append((pool, torch.tensor(table, dtype=torch.int32, device=dev), shared_slot,
                            synth.FMT_Q3G))
-    # two kernels per layer here: at T = 4 the accumulate mode's four times as
-    # many atomic adds made the step slower (391 against 424 steps/s)
-    chain3 = DecodeChain(torch, bf, shape, pools3, 4, dev,
-                         [synth.make_x(3, l, 4, d, device=dev) for l in range(N_LAYERS)])
     logits3 = [torch.stack([synth.make_logits(3, l, 4, E, 1.5, device=dev, step=g)
                             for l in range(N_LAYERS)]) for g in range(n_graphs)]
+    xs3 = [synth.make_x(3, l, 4, d, device=dev) for l in range(N_LAYERS)]
+    chain3 = StackStep(torch, bf, shape, pools3, 4, dev, xs3[0], logits3)
+    chain3.set_addends(xs3)
     steps3 = max(20, args.steps // 2)
-    dt, _, graphs = time_graph_steps(torch, chain3, logits3, steps3, 5, n_graphs)
+    dt, ev_ms3, graphs = time_graph_steps(torch, chain3, steps3, 5, n_graphs)
     del graphs
     union = []
     for g in range(n_graphs):
@@ -427,12 +455,13 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
     sps = steps3 / dt
     out["verify"] = {
         "workload": "verify step: 1 real + 3 draft tokens routed independently through 48 layers "
-                    "alternating Q2SM / Q3G; each distinct chosen expert read once per step "
-                    "(one moe_decode_layer call per layer)",
+                    "alternating Q2SM / Q3G, chained through their outputs; each distinct chosen "
+                    "expert read once per layer (one moe_decode_stack call per step)",
         "steps_per_s": round(sps, 2), "token_positions_per_s": round(4 * sps, 2),
         "ms_per_step": round(dt * 1e3 / steps3, 5), "mean_union_experts": round(mean_u, 2),
         "hbm_GBps_algorithmic": round(step_bytes * sps / 1e9, 1),
         "frac_of_hbm_peak": round(step_bytes * sps / 1e9 / HBM_PEAK_GBS, 4),
+        "avg_layer_us": round(ev_ms3 * 1e3 / (steps3 * N_LAYERS), 3),
     }
     log(f"verify: {sps:.1f} steps/s, union {mean_u:.2f} ({time.perf_counter() - t0:.1f} s)")
     del pools3, chain3, logits3
@@ -477,9 +506,9 @@ def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_gr
     res = {}
     misses_per_token = n_missed / n_graphs
     for name, r in (("full_layer", None), ("rank_limit_5", 5)):
-        chain = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, tiers=tiers,
+        chain = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, logits2, tiers=tiers,
                             host_table=host_table, max_rank=r)
-        dt, _, graphs = time_graph_steps(torch, chain, logits2, steps, 5, n_graphs)
+        dt, _, graphs = time_graph_steps(torch, chain, steps, 5, n_graphs)
         del graphs
         res[name + "_tok_s"] = round(steps / dt, 2)
         res[name + "_ms_per_step"] = round(dt * 1e3 / steps, 5)
@@ -488,7 +517,7 @@ def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_gr
     res["missed_experts_per_token"] = round(misses_per_token, 2)
     res["host_read_MB_per_token"] = round(misses_per_token * sb / 1e6, 1)
     # effect of the rank limit on each layer's update y - x (graph 0's routing)
-    chain_full = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, tiers=tiers,
+    chain_full = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, logits2, tiers=tiers,
                              host_table=host_table)
     rel = []
     for l in range(N_LAYERS):
@@ -642,8 +671,9 @@ def run_adaptive_cache(torch, np, bf, synth, shape, pools2, tiers, host_table, x
         eos.append(torch.tensor(slot_expert, dtype=torch.int32, device=dev))
         shared.append(shared_slot)
     counts = [torch.zeros(E, dtype=torch.int32, device=dev) for _ in range(N_LAYERS)]
-    chain = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, tiers=tiers, host_table=host_table,
-                        counts=counts)
+    lg_buf = logits_of(0)
+    chain = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, [lg_buf], tiers=tiers,
+                        host_table=host_table, counts=counts)
     swaps = [torch.full((max_swaps, 4), -1, dtype=torch.int32, device=dev) for _ in range(N_LAYERS)]
     n_sw = [torch.zeros(4, dtype=torch.int32, device=dev) for _ in range(N_LAYERS)]
 
@@ -654,16 +684,15 @@ def run_adaptive_cache(torch, np, bf, synth, shape, pools2, tiers, host_table, x
             bf.cache_fill(chain.layers[l], tiers[l], swaps[l], n_sw[l])
             bf.cache_commit(tables[l], swaps[l], n_sw[l])
 
-    lg_buf = logits_of(0)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        chain.step(lg_buf)
+        chain.step(0)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g_step, g_maint = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_step):
-        chain.step(lg_buf)
+        chain.step(0)
     with torch.cuda.graph(g_maint):
         maintain()
     for c in counts:
@@ -797,11 +826,22 @@ def cpu_baseline(np, synth, pools, shape):
     """The oracle on this host's cores: one token through all 48 decode layers
     (route, lookup, unpack of the chosen slots, expert FFNs, combine)."""
     import oracle
+    avail = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
-        cores = 1
+        blas = 1
+    cores = min(blas, avail)        # NumPy's BLAS threads, bounded by the CPUs this process may use
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
     n_tok = 2
     inputs = []
@@ -826,7 +866,7 @@ def cpu_baseline(np, synth, pools, shape):
                       f"decode layers over the same packed pools as the timed workload, logits "
                       f"drawn on the host (route, lookup, unpack of the 11 chosen slots, FFNs, "
                       f"combine)",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "cpus_available": avail, "cpu_model": cpu_model}
 
 
 if __name__ == "__main__":

@@ -67,9 +67,6 @@ SIGNATURES = {
     "moe_decode_stack_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_decode_stack": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _SLP, _vp,
                                   _vp, _c_sz, _vp]),
-    "moe_decode_layer_acc": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                      _vp, _vp, _vp, _vp, _vp, _vp]),
-    "moe_decode_acc_finish": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp]),
     "moe_decode_misses": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, _vp,
                                    _c_sz, _vp]),
     "moe_cache_count": (_c_int, [_vp, _c_int, _c_int, _vp, _vp]),
@@ -316,9 +313,10 @@ def decode_stack(layers, x, logits, tables, addends=None, ys=None, routing=False
     layers: list of MoeLayer (same d_model, d_ff, n_experts, top_k; formats may
     differ); x fp32 [T, d_model]; logits fp32 [L, T, E] (or a list of [T, E]);
     tables: list of int32 [E] slot tables; addends: None or fp32 [L, T, d]
-    (entry 0 unused).  ys: fp32 [L, T, d] outputs (allocated if None).  With
-    routing=True also returns idx, w, slot [L, T, k], miss_expert, miss_pair
-    [L, T*k] and n_miss [L, 4].  Returns a dict."""
+    (entry 0 unused).  ys: fp32 [L, T, d] outputs (allocated if None), or
+    fp32 [T, d] for the last layer's output only.  With routing=True also
+    returns idx, w, slot [L, T, k], miss_expert, miss_pair [L, T*k] and
+    n_miss [L, 4].  Returns a dict."""
     nl = len(layers)
     if nl < 1:
         raise ValueError("decode_stack: at least one layer")
@@ -342,7 +340,8 @@ def decode_stack(layers, x, logits, tables, addends=None, ys=None, routing=False
             _dev(_shape(addends[l], (T, d), f"addends[{l}]"), torch.float32, f"addends[{l}]")
     if ys is None:
         ys = torch.empty((nl, T, d), dtype=torch.float32, device=dev)
-    _dev(_shape(ys, (nl, T, d), "ys"), torch.float32, "ys")
+    last_only = ys.dim() == 2
+    _dev(_shape(ys, (T, d) if last_only else (nl, T, d), "ys"), torch.float32, "ys")
     out = {"y": ys}
     if routing:
         # per-layer rows padded to 16 bytes (every pointer must be 16-byte aligned)
@@ -371,7 +370,10 @@ def decode_stack(layers, x, logits, tables, addends=None, ys=None, routing=False
         c.shared_slot, c.reserved = Lx.shared_slot, 0
         c.slot_of_expert, c.logits = tables[l].data_ptr(), logits[l].data_ptr()
         c.addend = addends[l].data_ptr() if (addends is not None and l > 0) else None
-        c.y = ys[l].data_ptr()
+        if last_only:
+            c.y = ys.data_ptr() if l + 1 == nl else None
+        else:
+            c.y = ys[l].data_ptr()
         if routing:
             c.idx, c.w, c.slot = (out["idx"][l].data_ptr(), out["w"][l].data_ptr(),
                                   out["slot"][l].data_ptr())
@@ -381,72 +383,6 @@ def decode_stack(layers, x, logits, tables, addends=None, ys=None, routing=False
                                   _stream(stream)), "moe_decode_stack")
     out["ws"] = ws
     return out
-
-
-ACC_BUFS = 8   # accumulation buffers of moe_decode_layer_acc
-
-
-def decode_layer_acc(layer: MoeLayer, x, logits, slot_of_expert, acc_out, acc_clear=None,
-                     prev=None, idx=None, w=None, slot=None, miss_expert=None, miss_pair=None,
-                     n_miss=None, want_pairs=True, stream=None):
-    """One decode layer with its weighted terms added into acc_out (fp32
-    [8, T, d_model], zero on entry) instead of forming y
-    (moe_decode_layer_acc).  acc_clear: a buffer of the same shape set to
-    zero.  prev: (prev_x, prev_acc, prev_y) of the previous call, whose y this
-    call forms.  Returns (idx, w, slot, miss_expert, miss_pair, n_miss)."""
-    _dev(_shape(x, (None, layer.d_model), "x"), torch.float32, "x")
-    T = x.shape[0]
-    k = layer.top_k
-    acc_shape = (ACC_BUFS, T, layer.d_model)
-    _dev(_shape(logits, (T, layer.n_experts), "logits"), torch.float32, "logits")
-    _dev(_shape(slot_of_expert, (layer.n_experts,), "slot_of_expert"), torch.int32,
-         "slot_of_expert")
-    _dev(_shape(acc_out, acc_shape, "acc_out"), torch.float32, "acc_out")
-    if acc_clear is not None:
-        _dev(_shape(acc_clear, acc_shape, "acc_clear"), torch.float32, "acc_clear")
-    prev_x = prev_acc = prev_y = None
-    if prev is not None:
-        prev_x, prev_acc, prev_y = prev
-        _dev(_shape(prev_x, tuple(x.shape), "prev_x"), torch.float32, "prev_x")
-        _dev(_shape(prev_acc, acc_shape, "prev_acc"), torch.float32, "prev_acc")
-        _dev(_shape(prev_y, tuple(x.shape), "prev_y"), torch.float32, "prev_y")
-    dev = x.device
-    n = T * k
-    idx = torch.empty((T, k), dtype=torch.int32, device=dev) if idx is None else idx
-    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
-    slot = torch.empty((T, k), dtype=torch.int32, device=dev) if slot is None else slot
-    if miss_expert is None:
-        miss_expert = torch.full((n,), -1, dtype=torch.int32, device=dev)
-    if want_pairs and miss_pair is None:
-        miss_pair = torch.full((n,), -1, dtype=torch.int32, device=dev)
-    n_miss = torch.zeros((4,), dtype=torch.int32, device=dev) if n_miss is None else n_miss
-    for name, t, dt in (("idx", idx, torch.int32), ("w", w, torch.float32),
-                        ("slot", slot, torch.int32)):
-        _dev(_shape(t, (T, k), name), dt, name)
-    _dev(_at_least(miss_expert, n, "miss_expert"), torch.int32, "miss_expert")
-    if miss_pair is not None:
-        _dev(_at_least(miss_pair, n, "miss_pair"), torch.int32, "miss_pair")
-    _dev(_at_least(n_miss, 2, "n_miss"), torch.int32, "n_miss")
-    L = layer.c_struct()
-    _check(lib().moe_decode_layer_acc(ctypes.byref(L), _ptr(x), T, _ptr(logits),
-                                      _ptr(slot_of_expert), _ptr(idx), _ptr(w), _ptr(slot),
-                                      _ptr(miss_expert), _ptr(miss_pair), _ptr(n_miss),
-                                      _ptr(acc_out), _ptr(acc_clear), _ptr(prev_x),
-                                      _ptr(prev_acc), _ptr(prev_y), _stream(stream)),
-           "moe_decode_layer_acc")
-    return idx, w, slot, miss_expert, miss_pair, n_miss
-
-
-def decode_acc_finish(x, acc, y=None, stream=None):
-    """y = x + acc[0] + ... + acc[7] (moe_decode_acc_finish).  Returns y."""
-    _dev(_shape(x, (None, None), "x"), torch.float32, "x")
-    T, d = x.shape
-    _dev(_shape(acc, (ACC_BUFS, T, d), "acc"), torch.float32, "acc")
-    y = torch.empty_like(x) if y is None else y
-    _dev(_shape(y, (T, d), "y"), torch.float32, "y")
-    _check(lib().moe_decode_acc_finish(_ptr(x), _ptr(acc), T, d, _ptr(y), _stream(stream)),
-           "moe_decode_acc_finish")
-    return y
 
 
 @dataclasses.dataclass

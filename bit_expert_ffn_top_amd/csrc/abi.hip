@@ -213,41 +213,6 @@ int moe_decode_stack(int d_model, int d_ff, int n_experts, int top_k, int T, int
   return hip_status(bitffn::launch_decode_stack(D, n_layers, layers, x, ws, stream));
 }
 
-int moe_decode_layer_acc(const moe_layer* L, const float* x, int T, const float* logits,
-                         const int32_t* slot_of_expert, int32_t* idx, float* w, int32_t* slot,
-                         int32_t* miss_expert, int32_t* miss_pair, int32_t* n_miss,
-                         float* acc_out, float* acc_clear, const float* prev_x,
-                         const float* prev_acc, float* prev_y, hipStream_t stream) {
-  const int st = check_layer(L);
-  if (st != MOE_OK) return st;
-  if (T < 1 || T > MOE_MAX_DECODE_T || T * L->top_k > MOE_MAX_DECODE_PAIRS) return MOE_EINVAL;
-  if (!x || !logits || !slot_of_expert || !idx || !w || !slot || !miss_expert || !n_miss ||
-      !acc_out)
-    return MOE_EINVAL;
-  // the previous call's y: all three or none
-  const int prev = (prev_x ? 1 : 0) + (prev_acc ? 1 : 0) + (prev_y ? 1 : 0);
-  if (prev != 0 && prev != 3) return MOE_EINVAL;
-  if (acc_out == acc_clear || acc_out == prev_acc || (prev_acc && prev_acc == acc_clear))
-    return MOE_EINVAL;
-  if (!aligned16(x) || !aligned16(logits) || !aligned16(slot_of_expert) || !aligned16(idx) ||
-      !aligned16(w) || !aligned16(slot) || !aligned16(miss_expert) || !aligned16(n_miss) ||
-      (miss_pair && !aligned16(miss_pair)) || !aligned16(acc_out) ||
-      (acc_clear && !aligned16(acc_clear)) ||
-      (prev && (!aligned16(prev_x) || !aligned16(prev_acc) || !aligned16(prev_y))))
-    return MOE_EALIGN;
-  return hip_status(bitffn::launch_decode_layer_acc(*L, x, T, logits, slot_of_expert, idx, w,
-                                                    slot, miss_expert, miss_pair, n_miss, acc_out,
-                                                    acc_clear, prev_x, prev_acc, prev_y, stream));
-}
-
-int moe_decode_acc_finish(const float* x, const float* acc, int T, int d, float* y,
-                          hipStream_t stream) {
-  if (T < 1 || T > MOE_MAX_DECODE_T || d < 2 || d > 2048 || d % 2 != 0) return MOE_EINVAL;
-  if (!x || !acc || !y) return MOE_EINVAL;
-  if (!aligned16(x) || !aligned16(acc) || !aligned16(y)) return MOE_EALIGN;
-  return hip_status(bitffn::launch_acc_finish(x, acc, T, d, y, stream));
-}
-
 int moe_decode_misses(const moe_layer* H, const float* x, int T, const int32_t* idx,
                       const int32_t* slot, const float* w, const int32_t* host_slot_of_expert,
                       int max_rank, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -25,11 +25,9 @@
 // and scale/min are applied once per block.
 //
 // Modes of the ffn kernel: the pair slots given (moe_expert_ffn_decode), the
-// routing done inside every workgroup (moe_decode_layer), the missed pairs
-// only, with their slots in a second pool such as pinned host memory
-// (moe_decode_misses, whose combine adds into y), or the routing inside with
-// the combine's weighted sum accumulated into buffers by atomic adds
-// (moe_decode_layer_acc, whose y a later call finishes).
+// routing done inside every workgroup (moe_decode_layer, moe_decode_stack), or
+// the missed pairs only, with their slots in a second pool such as pinned host
+// memory (moe_decode_misses, whose combine adds into y).
 #include "moe_internal.h"
 #include "route_device.h"
 
@@ -71,13 +69,7 @@ enum FfnMode {
   kPairs = 0,   // the pair slots given by the caller
   kRoute = 1,   // routing done in the kernel (top-k, slot table)
   kMiss = 2,    // missed pairs only, their slots in a second pool (host tier)
-  kAcc = 3,     // routing in the kernel; weighted terms added into acc buffers
 };
-
-// Accumulation buffers of the kAcc mode: term contributions of slice js go to
-// buffer js % ACC_BUFS, so that an element takes (members x slices / ACC_BUFS)
-// atomic adds instead of one add per slice and member.
-constexpr int ACC_BUFS = 8;
 
 struct FfnArgs {
   const uint8_t* pool;
@@ -102,53 +94,7 @@ struct FfnArgs {
   // a miss of k-slot i runs only if i < max_rank
   const int32_t* idx;           // [T][k]
   int max_rank, n_slots;
-  // kAcc only: acc_out [ACC_BUFS][T][d] (zero on entry) receives the weighted
-  // terms; acc_clear (same shape, optional) is set to zero; if prev_acc is
-  // given, prev_y = prev_x + sum over its buffers (the previous call's y)
-  float* acc_out;
-  float* acc_clear;
-  const float* prev_x;
-  const float* prev_acc;
-  float* prev_y;
 };
-
-// One row job of the kAcc side workgroups (and of the finish kernel): row r
-// < n_zero of `zero` ([n_zero][d]) is set to zero; row n_zero + t is
-// y[t] = x[t] + acc[0][t] + ... + acc[ACC_BUFS-1][t], added in that order.
-// 1024 threads, two values each (d <= 2048, d even).
-__device__ __forceinline__ void acc_row_job(int r, int n_zero, float* __restrict__ zero, int T,
-                                            int d, const float* __restrict__ x,
-                                            const float* __restrict__ acc,
-                                            float* __restrict__ y) {
-  const int c = 2 * static_cast<int>(threadIdx.x);
-  if (c >= d) return;
-  if (r < n_zero) {
-    *reinterpret_cast<float2*>(zero + static_cast<int64_t>(r) * d + c) = make_float2(0.0f, 0.0f);
-    return;
-  }
-  const int t = r - n_zero;
-  const int64_t o = static_cast<int64_t>(t) * d + c;
-  float2 v[ACC_BUFS + 1];
-  v[0] = *reinterpret_cast<const float2*>(x + o);
-#pragma unroll
-  for (int b = 0; b < ACC_BUFS; ++b)
-    v[b + 1] = *reinterpret_cast<const float2*>(acc + static_cast<int64_t>(b) * T * d + o);
-  float2 sum = v[0];
-#pragma unroll
-  for (int b = 1; b <= ACC_BUFS; ++b) {
-    sum.x += v[b].x;
-    sum.y += v[b].y;
-  }
-  *reinterpret_cast<float2*>(y + o) = sum;
-}
-
-// y = x + the ACC_BUFS buffers of acc, token t per workgroup.
-__global__ __launch_bounds__(KA_THREADS) void acc_finish_kernel(const float* __restrict__ x,
-                                                                const float* __restrict__ acc,
-                                                                int T, int d,
-                                                                float* __restrict__ y) {
-  acc_row_job(blockIdx.x, 0, nullptr, T, d, x, acc, y);
-}
 
 // Survivors of the first top-k level in the fused kernel: T * ceil(E/64) * k
 // <= 16 * (T * k) <= 16 * 64.
@@ -221,27 +167,17 @@ __device__ __forceinline__ float wave_total(float v) {
 // slots; workgroups of the shared expert skip routing.  MODE kMiss: a pair's
 // slot is its expert's slot in the host tier if the pair missed the GPU
 // cache and its rank is below the limit, else none; there is no shared
-// member.  MODE kAcc: routing as kRoute; each served token's term, times its
-// routing weight (1 for the shared expert), is added into buffer js % ACC_BUFS
-// of acc_out; the last row of workgroups (u = T*k + 1) only does the row jobs
-// of acc_row_job (clearing acc_clear, finishing prev_y).
+// member.
 template <int FMT, int UPW, int MODE>
 __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
                                                                 const float* __restrict__ x) {
-  constexpr bool ROUTE = MODE == kRoute || MODE == kAcc;
+  constexpr bool ROUTE = MODE == kRoute;
   const int js = blockIdx.x;
   const int u = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int d = a.d;
   const int n = a.T * a.k;
-  if (MODE == kAcc && u == n + 1) {   // side workgroups: row jobs only
-    const int n_zero = a.acc_clear ? ACC_BUFS * a.T : 0;
-    const int jobs = n_zero + (a.prev_acc ? a.T : 0);
-    for (int r = js; r < jobs; r += gridDim.x)
-      acc_row_job(r, n_zero, a.acc_clear, a.T, d, a.prev_x, a.prev_acc, a.prev_y);
-    return;
-  }
   int sp = -1;   // slot of pair `lane`
   if (MODE == kPairs) sp = lane < n ? a.slot[lane] : -1;
   if (MODE == kMiss) {
@@ -265,7 +201,6 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
   }
   __builtin_amdgcn_sched_barrier(0);   // keep the issue order
 
-  __shared__ float s_wt[MOE_MAX_DECODE_PAIRS];   // kAcc: routing weight of pair t*k + i
   if (ROUTE && u < n) {   // uniform per workgroup
     __shared__ uint64_t s_grp[KA_WAVES * 64];
     __shared__ uint64_t s_cand[kFusedCand];
@@ -279,12 +214,6 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
     });
     const int e = lane < n ? key_expert(s_top[lane]) : 0;
     sp = lane < n ? s_table[e] : -1;
-    if (MODE == kAcc && wave < a.T) {   // this workgroup's own routing weights
-      int id;
-      float wt;
-      topk_softmax_lane(s_top + wave * a.k, a.k, lane, id, wt);
-      if (lane < a.k) s_wt[wave * a.k + lane] = wt;
-    }
     if (u == 0 && js == 0) {   // routing outputs
       if (wave < a.T) {
         int id;
@@ -406,9 +335,7 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
     const float HX = hsum[0], HK = hsum[1];
     const int term = member_term(same, t, a.k, u == n);
     float* __restrict__ out =
-        MODE == kAcc ? a.acc_out + (static_cast<int64_t>(js % ACC_BUFS) * a.T + t) * d
-                     : a.part + ((static_cast<int64_t>(t) * (a.k + 1) + term) * nslices + js) * d;
-    const float wterm = MODE == kAcc ? (u == n ? 1.0f : s_wt[t * a.k + term]) : 1.0f;
+        a.part + ((static_cast<int64_t>(t) * (a.k + 1) + term) * nslices + js) * d;
     float a0[MAX_DROWS], a1[MAX_DROWS];
 #pragma unroll
     for (int i = 0; i < MAX_DROWS; ++i) a0[i] = a1[i] = 0.0f;
@@ -442,10 +369,7 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
       if (i < ndr) {
         const float v = block_finish<FMT>(0.0f, a0[i] + a1[i], HK, HX, ds[i],
                                           FMT == MOE_FMT_Q2SM ? dm[i] : 0u);
-        if (MODE == kAcc)
-          unsafeAtomicAdd(out + tid + KA_THREADS * i, wterm * v);
-        else
-          out[tid + KA_THREADS * i] = v;
+        out[tid + KA_THREADS * i] = v;
       }
     }
     __syncthreads();
@@ -556,8 +480,8 @@ size_t part_bytes(int d, int f, int T, int k) {
 
 template <int FMT, int MODE>
 hipError_t launch_ffn(const FfnArgs& a, const float* x, hipStream_t s) {
-  // members (T*k pairs, the shared expert), plus the side row in kAcc mode
-  const dim3 grid(a.f / SLICE, a.T * a.k + (MODE == kMiss ? 0 : MODE == kAcc ? 2 : 1));
+  // members: T*k pairs and the shared expert (none in the miss mode)
+  const dim3 grid(a.f / SLICE, a.T * a.k + (MODE == kMiss ? 0 : 1));
   const int upw = (a.d / 64 + KA_WAVES - 1) / KA_WAVES;
   if (upw <= 1)
     decode_ffn_kernel<FMT, 1, MODE><<<grid, KA_THREADS, 0, s>>>(a, x);
@@ -650,35 +574,6 @@ hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const 
   const hipError_t e = launch_ffn_fmt<kRoute>(L.fmt, a, x, s);
   if (e != hipSuccess) return e;
   return launch_combine_partials(L, x, T, slot, w, a.part, y, s, xnext, addend);
-}
-
-hipError_t launch_decode_layer_acc(const moe_layer& L, const float* x, int T, const float* logits,
-                                   const int32_t* slot_of_expert, int32_t* idx, float* w,
-                                   int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
-                                   int32_t* n_miss, float* acc_out, float* acc_clear,
-                                   const float* prev_x, const float* prev_acc, float* prev_y,
-                                   hipStream_t s) {
-  FfnArgs a = ffn_args(L, T, nullptr, nullptr);
-  a.logits = logits;
-  a.table = slot_of_expert;
-  a.o_idx = idx;
-  a.o_w = w;
-  a.o_slot = slot;
-  a.o_miss_expert = miss_expert;
-  a.o_miss_pair = miss_pair;
-  a.o_n_miss = n_miss;
-  a.acc_out = acc_out;
-  a.acc_clear = acc_clear;
-  a.prev_x = prev_x;
-  a.prev_acc = prev_acc;
-  a.prev_y = prev_y;
-  return launch_ffn_fmt<kAcc>(L.fmt, a, x, s);
-}
-
-hipError_t launch_acc_finish(const float* x, const float* acc, int T, int d, float* y,
-                             hipStream_t s) {
-  acc_finish_kernel<<<T, KA_THREADS, 0, s>>>(x, acc, T, d, y);
-  return hipGetLastError();
 }
 
 hipError_t launch_decode_misses(const moe_layer& H, const void* host_pool_dev, const float* x,

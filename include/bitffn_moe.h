@@ -252,37 +252,6 @@ int moe_decode_stack(int d_model, int d_ff, int n_experts, int top_k, int T, int
                      const moe_stack_layer* layers, const float* x, void* ws, size_t ws_bytes,
                      hipStream_t stream);
 
-/* moe_decode_layer with the combine split in two, so that a step of several
- * layers runs one kernel per layer (same pages and definitions as
- * moe_decode_layer).  The call routes, looks up and runs the chosen experts
- * as moe_decode_layer does, with the same routing outputs bit for bit, but
- * instead of writing y it adds every term w[t*k+i] * FFN_i(x[t]) (and the
- * shared expert's FFN(x[t]), weight 1) into acc_out, fp32 [8][T][d_model],
- * which must be zero on entry: term contributions are spread over the 8
- * buffers and added with atomic operations, so the order of the additions
- * (and the last bits of the sums) varies from call to call.  The layer's
- * output is y = x + acc_out[0] + ... + acc_out[7]; moe_decode_acc_finish
- * forms it, or the next call does, as a side job: if prev_x, prev_acc and
- * prev_y are given (all three, or none), prev_y[t] = prev_x[t] +
- * prev_acc[0][t] + ... + prev_acc[7][t], added in that order.  acc_clear
- * (optional, fp32 [8][T][d_model]) is set to zero, ready to be the next
- * call's acc_out.  acc_out may not be acc_clear or prev_acc; the buffers
- * the call writes (acc_out, acc_clear, prev_y, the routing outputs) must not
- * overlap what it reads.  Limits as moe_decode_layer; no workspace. */
-int moe_decode_layer_acc(const moe_layer* L, const float* x, int T,
-                         const float* logits, const int32_t* slot_of_expert,
-                         int32_t* idx, float* w, int32_t* slot,
-                         int32_t* miss_expert, int32_t* miss_pair,
-                         int32_t* n_miss, float* acc_out, float* acc_clear,
-                         const float* prev_x, const float* prev_acc,
-                         float* prev_y, hipStream_t stream);
-
-/* y[t] = x[t] + acc[0][t] + ... + acc[7][t] (in that order) for the output of
- * a moe_decode_layer_acc call: x, y fp32 [T][d], acc fp32 [8][T][d];
- * 1 <= T <= MOE_MAX_DECODE_T, d even and at most 2048.  y may be x. */
-int moe_decode_acc_finish(const float* x, const float* acc, int T, int d,
-                          float* y, hipStream_t stream);
-
 /* Miss execution and the per-layer join of a decode / verify step.  The
  * chosen experts not resident in the GPU cache are computed from the host
  * tier, a copy of the layer's experts in host memory, and added to the GPU

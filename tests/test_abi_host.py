@@ -242,29 +242,46 @@ def test_stage_layer_host_checks():
     assert call(soe=bad, hs=np.where(np.arange(E) == 300, -1, hs).astype(np.int32)) == -1
 
 
-def test_decode_layer_acc_host_checks():
+def test_decode_stack_host_checks():
     lib = _lib()
     s = ctypes.c_void_p(0)
-    L = _layer()
+    from bit_expert_ffn_top_amd._binding import MoeStackLayerC
+    sb = synth.slot_bytes(2, 2048, 768)
 
-    def call(L=L, T=1, acc=_p(1 << 20), clear=None, px=None, pacc=None, py=None, x=_p()):
-        return lib.moe_decode_layer_acc(ctypes.byref(L), x, T, _p(), _p(), _p(), _p(), _p(), _p(),
-                                        None, _p(), acc, clear, px, pacc, py, s)
+    def layer(**kw):
+        v = dict(pool=FAKE, slot_bytes=sb, n_slots=513, fmt=2, shared_slot=512, reserved=0,
+                 slot_of_expert=_p(1 << 16), logits=_p(1 << 17), addend=None, y=_p(1 << 18),
+                 idx=None, w=None, slot=None, miss_expert=None, miss_pair=None, n_miss=None)
+        v.update(kw)
+        return MoeStackLayerC(**v)
 
-    assert call(T=0) == -1
-    assert call(T=5) == -1
-    assert call(_layer(top_k=20), T=4) == -1                          # T*k > 64
-    assert call(acc=None) == -1                                       # no acc_out
-    assert call(px=_p(1 << 21)) == -1                                 # prev: all or none
-    assert call(px=_p(1 << 21), pacc=_p(1 << 22)) == -1
-    assert call(clear=_p(1 << 20)) == -1                              # acc_out == acc_clear
-    assert call(px=_p(1 << 21), pacc=_p(1 << 20), py=_p(1 << 23)) == -1   # acc_out == prev_acc
-    assert call(acc=_p((1 << 20) + 4)) == -2                          # misaligned
-    assert call(_layer(fmt=7)) == -3
-    fin = lambda T=1, d=2048, acc=_p(1 << 20): lib.moe_decode_acc_finish(_p(), acc, T, d, _p(), s)
-    assert fin(T=0) == -1
-    assert fin(T=5) == -1
-    assert fin(d=2050) == -1
-    assert fin(d=7) == -1
-    assert fin(acc=None) == -1
-    assert fin(acc=_p(4)) == -2
+    need = lib.moe_decode_stack_workspace_bytes(2048, 768, 512, 10, 1)
+    assert need > 0
+    assert lib.moe_decode_stack_workspace_bytes(2048, 768, 512, 10, 5) == 0
+    assert lib.moe_decode_stack_workspace_bytes(2048, 768, 512, 20, 4) == 0   # T*k > 64
+    assert lib.moe_decode_stack_workspace_bytes(2048, 768, 1025, 10, 1) == 0
+
+    def call(layers, n=None, T=1, k=10, E=512, d=2048, f=768, x=_p(1 << 21), ws=_p(1 << 22),
+             nb=need):
+        arr = (MoeStackLayerC * len(layers))(*layers)
+        return lib.moe_decode_stack(d, f, E, k, T, len(layers) if n is None else n, arr, x, ws,
+                                    nb, s)
+
+    ok = [layer(y=None), layer()]
+    assert call(ok, n=0) == -1
+    assert call(ok, T=5) == -1
+    assert call(ok, T=4, k=20) == -1
+    assert call(ok, nb=need - 1) == -4
+    assert call(ok, ws=_p((1 << 22) + 16)) == -2                      # workspace 256-aligned
+    assert call(ok, x=None) == -1
+    assert call([layer(), layer(y=None)]) == -1                        # last y required
+    assert call([layer(y=None), layer(fmt=7)]) == -3
+    assert call([layer(y=None), layer(slot_bytes=sb + 256)]) == -3
+    assert call([layer(y=None), layer(reserved=1)]) == -1
+    assert call([layer(y=None), layer(shared_slot=513)]) == -1
+    assert call([layer(y=None), layer(logits=None)]) == -1
+    assert call([layer(y=None), layer(idx=_p(1 << 19))]) == -1         # routing: all or none
+    assert call([layer(y=None), layer(n_miss=_p(1 << 19))]) == -1      # with miss_expert only
+    assert call([layer(y=None), layer(pool=FAKE + 16)]) == -2
+    assert call([layer(y=None), layer(addend=_p((1 << 19) + 4))]) == -2
+    assert call([layer(y=None), layer(y=_p(1 << 21))]) == -1           # y aliases x
