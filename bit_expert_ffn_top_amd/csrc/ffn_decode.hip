@@ -54,10 +54,6 @@ __device__ __forceinline__ uint32_t stream_u16(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
 }
 
-// x is read-only for the whole kernel: reading it through the constant address
-// space lets its wavefront-uniform loads become scalar loads.
-typedef const __attribute__((address_space(4))) float cfloat;
-
 constexpr int KA_THREADS = 1024;
 constexpr int KA_WAVES = KA_THREADS / 64;
 constexpr int SLICE = 32;          // h indices per workgroup
@@ -71,10 +67,16 @@ enum FfnMode {
   kMiss = 2,    // missed pairs only, their slots in a second pool (host tier)
 };
 
+// Plane offsets within a slot (a slot is far below 4 GiB), 32-bit so that a
+// load address is the slot base (scalar) plus a 32-bit offset.
+struct Planes32 {
+  uint32_t codes, hi, scale, min;
+};
+
 struct FfnArgs {
   const uint8_t* pool;
   int64_t slot_bytes;
-  Planes G, D;
+  Planes32 G, D;
   int d, f, T, k, shared_slot;
   const int32_t* slot;
   float* part;  // [T][k+1][f/32][d]: term i of token t, the shared expert at i = k
@@ -96,12 +98,21 @@ struct FfnArgs {
   int max_rank, n_slots;
 };
 
-// Survivors of the first top-k level in the fused kernel: T * ceil(E/64) * k
-// <= 16 * (T * k) <= 16 * 64.
-constexpr int kFusedCand = (MOE_MAX_EXPERTS / 64) * MOE_MAX_DECODE_PAIRS;
+// Routing inside the kernel: experts are taken in chunks of 512, one
+// wavefront per (token, chunk) holding 8 keys per lane; each chunk's top k is
+// found by wave_topk_keys, and with two chunks a second pass ranks the 2k
+// survivors of each token.
+constexpr int kRouteChunk = 512;
+constexpr int kRouteChunks = (MOE_MAX_EXPERTS + kRouteChunk - 1) / kRouteChunk;
 static_assert(MOE_MAX_EXPERTS <= KA_THREADS, "one slot-table entry per thread");
-static_assert(MOE_MAX_DECODE_T * (MOE_MAX_EXPERTS / 64) <= 4 * KA_WAVES,
-              "logit groups per wavefront above 4");
+static_assert(MOE_MAX_DECODE_T * kRouteChunks <= KA_WAVES, "one wavefront per token and chunk");
+static_assert(kRouteChunks <= 2, "at most two chunks (the merge holds 2 keys per lane)");
+
+// Jobs of the shared expert per slice: one (it serves every token), none
+// without a shared expert or in the miss mode.
+__host__ __device__ inline int shared_jobs_per_slice(int shared_slot, bool miss) {
+  return (miss || shared_slot < 0) ? 0 : 1;
+}
 
 // Union member u: its slot, the mask of tokens it serves, and `same`, the
 // mask of pairs naming that slot (all of them for the shared expert, whose
@@ -168,12 +179,10 @@ __device__ __forceinline__ float wave_total(float v) {
 // slot is its expert's slot in the host tier if the pair missed the GPU
 // cache and its rank is below the limit, else none; there is no shared
 // member.
-template <int FMT, int UPW, int MODE>
-__global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
+template <int FMT, int UPW, int MODE, bool LOOP>
+__global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amdgpu_waves_per_eu(8, 8))) void decode_ffn_kernel(FfnArgs a,
                                                                 const float* __restrict__ x) {
   constexpr bool ROUTE = MODE == kRoute;
-  const int js = blockIdx.x;
-  const int u = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int d = a.d;
@@ -190,8 +199,7 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
 
   // Every load below is unconditional, with indices clamped into range (the
   // surplus values are never used), so the compiler can count outstanding
-  // loads and wait for each group alone.  Order: the pair slots, x (needed
-  // first, by the block sums), G units in the order they are used, then D.
+  // loads and wait for each group alone.  First x and the routing inputs.
   float2 xv[MOE_MAX_DECODE_T];
   const int ex = min(2 * tid, d - 2);
 #pragma unroll
@@ -199,22 +207,77 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
     const int tt = min(t, a.T - 1);
     xv[t] = *reinterpret_cast<const float2*>(x + static_cast<int64_t>(tt) * d + ex);
   }
+  const int nslices = a.f / SLICE;
+  // Jobs: first the shared expert's, one per slice js at j = js, then one
+  // per (pair u, slice js) at j = n_shared + u * nslices + js.  A workgroup
+  // of a shared job does only that job (it serves every token, the longest
+  // job) and skips routing; the others take the pair jobs in turn.
+  const int n_shared = shared_jobs_per_slice(a.shared_slot, MODE == kMiss) * nslices;
+  const int n_jobs = n_shared + n * nslices;
+  const bool routing = ROUTE && static_cast<int>(blockIdx.x) >= n_shared;   // uniform
+  const int nchunk = (a.E + kRouteChunk - 1) / kRouteChunk;
+  const int rt = wave / kRouteChunks, rc = wave % kRouteChunks;   // token and chunk of a routing wave
+  const bool route_wave = routing && rt < a.T && rc < nchunk;
+  float lg[8];
+  int tv = 0;
+  if (ROUTE) {
+    const int tt = min(rt, a.T - 1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      lg[j] = a.logits[static_cast<int64_t>(tt) * a.E + min(rc * kRouteChunk + 64 * j + lane, a.E - 1)];
+    tv = a.table[min(tid, a.E - 1)];
+  }
   __builtin_amdgcn_sched_barrier(0);   // keep the issue order
 
-  if (ROUTE && u < n) {   // uniform per workgroup
-    __shared__ uint64_t s_grp[KA_WAVES * 64];
-    __shared__ uint64_t s_cand[kFusedCand];
-    __shared__ uint64_t s_top[MOE_MAX_DECODE_PAIRS];
-    __shared__ int32_t s_table[MOE_MAX_EXPERTS];
-    float lg[4];
-    topk_load<4>(a.logits, a.T, a.E, lg);
-    const int tv = a.table[min(tid, a.E - 1)];
-    topk_select<4>(lg, a.T, a.E, a.k, TopkLds{s_grp, s_cand, s_top}, [&] {
-      if (tid < a.E) s_table[tid] = tv;
-    });
+  __shared__ __attribute__((aligned(16))) float s_x[MOE_MAX_DECODE_T][2048];
+  __shared__ float2 bsum[MOE_MAX_DECODE_T][2048 / 32];   // per block of x: (sum, offset constant)
+  __shared__ uint64_t s_cand[MOE_MAX_DECODE_T * kRouteChunks * MOE_MAX_TOPK];
+  __shared__ uint64_t s_top[MOE_MAX_DECODE_PAIRS];
+  __shared__ uint64_t s_scr[MOE_MAX_DECODE_T * kRouteChunks][64];
+  __shared__ int32_t s_table[MOE_MAX_EXPERTS];
+
+  // x into LDS (the gate/up products read it from there), and per-block sums
+  // of x (sum, offset constant) for every token: each thread adds two
+  // neighbouring values, the 16 threads of a block reduce by DPP rotations
+  // within their row of 16 lanes; lane 0 of the row stores
+  const float cw0 = block_offset_weight<FMT>(ex & 31), cw1 = block_offset_weight<FMT>((ex & 31) + 1);
+#pragma unroll
+  for (int t = 0; t < MOE_MAX_DECODE_T; ++t) {
+    if (t < a.T && 2 * tid < d) *reinterpret_cast<float2*>(&s_x[t][2 * tid]) = xv[t];
+    const float sx = row16_sum(xv[t].x + xv[t].y);
+    const float sc = row16_sum(fmaf(cw1, xv[t].y, cw0 * xv[t].x));
+    if (t < a.T && (tid & 15) == 0 && 2 * tid < d)
+      bsum[t][tid >> 4] = make_float2(sx, block_const<FMT>(sx, sc));
+  }
+
+  if (ROUTE) {
+    if (route_wave) {   // top k of chunk rc of token rt
+      uint64_t key[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = rc * kRouteChunk + 64 * j + lane;
+        key[j] = route_key(lg[j], e, e < a.E);
+      }
+      uint64_t* out = nchunk == 1 ? s_top + rt * a.k : s_cand + (rt * kRouteChunks + rc) * a.k;
+      wave_topk_keys<8>(key, a.k, out, s_scr[wave]);
+    }
+    if (tid < a.E) s_table[tid] = tv;
+  }
+  __syncthreads();
+  if (ROUTE && nchunk > 1) {   // uniform: rank the 2k survivors of each token
+    if (routing && wave < a.T) {
+      uint64_t key[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        key[h] = lane < a.k ? s_cand[(wave * kRouteChunks + h) * a.k + lane] : 0ull;
+      wave_topk_keys<2>(key, a.k, s_top + wave * a.k, s_scr[wave]);
+    }
+    __syncthreads();
+  }
+  if (routing) {
     const int e = lane < n ? key_expert(s_top[lane]) : 0;
     sp = lane < n ? s_table[e] : -1;
-    if (u == 0 && js == 0) {   // routing outputs
+    if (static_cast<int>(blockIdx.x) == n_shared) {   // routing outputs: the first routing workgroup
       if (wave < a.T) {
         int id;
         float wt;
@@ -230,13 +293,27 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
     }
   }
 
+  __shared__ float red[KA_WAVES][64];
+  __shared__ __attribute__((aligned(16))) float hsh[SLICE];
+  __shared__ float hsum[2];
+
+  // one job; LOOP: the workgroup takes jobs blockIdx.x, + gridDim.x, ...,
+  // else exactly one (grid = jobs), with no loop around the job's code
+  auto run_job = [&](int job) {
+  const bool shared_job = job < n_shared;
+  const int u = shared_job ? n : (job - n_shared) / nslices;
+  const int js = shared_job ? job : (job - n_shared) % nslices;
   int s;
   uint32_t mask;
   uint64_t same;
   if (!union_member(sp, a.T, a.k, a.shared_slot, u, s, mask, same)) return;
   const uint8_t* __restrict__ base = a.pool + static_cast<int64_t>(s) * a.slot_bytes;
-  const int64_t R = 2 * static_cast<int64_t>(a.f);   // G rows
-  const int64_t grow = 2 * SLICE * js + lane;        // this lane's G row
+  // the thread index, opaque here so that the per-thread offsets below are
+  // formed in each job instead of being kept (and spilled) across jobs
+  int tj = tid;
+  opaque(tj);
+  const uint32_t R = 2u * static_cast<uint32_t>(a.f);                   // G rows
+  const uint32_t grow = 2u * SLICE * js + static_cast<uint32_t>(tj & 63);   // this lane's G row
   const int nu = d / 64;
 
   // ---- loads: G units of this wavefront, then D block column js ----
@@ -245,58 +322,35 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
   uint2 gh[UPW];
 #pragma unroll
   for (int i = 0; i < UPW; ++i) {
-    const int64_t unit = static_cast<int64_t>(min(wave + KA_WAVES * i, nu - 1)) * R + grow;
-    gc[i] = stream_u4(base + a.G.codes + unit * 16);
-    gs[i] = stream_u32(base + a.G.scale + unit * 4);
-    if (FMT == MOE_FMT_Q2SM) gm[i] = stream_u32(base + a.G.min + unit * 4);
-    if (FMT == MOE_FMT_Q3G) gh[i] = stream_u2(base + a.G.hi + unit * 8);
+    const uint32_t unit = static_cast<uint32_t>(min(wave + KA_WAVES * i, nu - 1)) * R + grow;
+    gc[i] = stream_u4(base + (a.G.codes + unit * 16u));
+    gs[i] = stream_u32(base + (a.G.scale + unit * 4u));
+    if (FMT == MOE_FMT_Q2SM) gm[i] = stream_u32(base + (a.G.min + unit * 4u));
+    if (FMT == MOE_FMT_Q3G) gh[i] = stream_u2(base + (a.G.hi + unit * 8u));
   }
   __builtin_amdgcn_sched_barrier(0);
-  const int ndr = (d - tid + KA_THREADS - 1) / KA_THREADS;   // D rows of this thread
+  const int ndr = (d - tj + KA_THREADS - 1) / KA_THREADS;   // D rows of this thread
   uint2 dc[MAX_DROWS];
   uint32_t ds[MAX_DROWS], dm[MAX_DROWS], dh[MAX_DROWS];
 #pragma unroll
   for (int i = 0; i < MAX_DROWS; ++i) {
-    const int64_t unit = static_cast<int64_t>(js) * d + min(tid + KA_THREADS * i, d - 1);
-    dc[i] = stream_u2(base + a.D.codes + unit * 8);
-    ds[i] = stream_u16(base + a.D.scale + unit * 2);
-    if (FMT == MOE_FMT_Q2SM) dm[i] = stream_u16(base + a.D.min + unit * 2);
-    if (FMT == MOE_FMT_Q3G) dh[i] = stream_u32(base + a.D.hi + unit * 4);
+    const uint32_t unit = static_cast<uint32_t>(js * d + min(tj + KA_THREADS * i, d - 1));
+    dc[i] = stream_u2(base + (a.D.codes + unit * 8u));
+    ds[i] = stream_u16(base + (a.D.scale + unit * 2u));
+    if (FMT == MOE_FMT_Q2SM) dm[i] = stream_u16(base + (a.D.min + unit * 2u));
+    if (FMT == MOE_FMT_Q3G) dh[i] = stream_u32(base + (a.D.hi + unit * 4u));
   }
 
-  __shared__ float red[KA_WAVES][64];
-  __shared__ float2 bsum[MOE_MAX_DECODE_T][2048 / 32];   // per block of x: (sum, offset constant)
-  __shared__ __attribute__((aligned(16))) float hsh[SLICE];
-  __shared__ float hsum[2];
-
-  // per-block sums of x (sum, offset constant) for every served token: each
-  // thread adds two neighbouring values, the 16 threads of a block reduce by
-  // DPP rotations within their row of 16 lanes; lane 0 of the row stores
-  // (computed for all token slots, stored for served ones: no branch for
-  // the compiler to sink the x loads into)
-  const float cw0 = block_offset_weight<FMT>(ex & 31), cw1 = block_offset_weight<FMT>((ex & 31) + 1);
-#pragma unroll
-  for (int t = 0; t < MOE_MAX_DECODE_T; ++t) {
-    const float sx = row16_sum(xv[t].x + xv[t].y);
-    const float sc = row16_sum(fmaf(cw1, xv[t].y, cw0 * xv[t].x));
-    if (((mask >> t) & 1u) && (tid & 15) == 0 && 2 * tid < d)
-      bsum[t][tid >> 4] = make_float2(sx, block_const<FMT>(sx, sc));
-  }
-  __syncthreads();
-
-  const int nslices = a.f / SLICE;
   // one served token: gate/up, SiLU gating, partial down product
   auto token_pass = [&](int t) {
-    const float* __restrict__ xt = x + static_cast<int64_t>(t) * d;
-
-    // gate/up rows: partial sums over this wavefront's units (x as scalar
-    // operands)
+    // gate/up rows: partial sums over this wavefront's units (x read from
+    // LDS, the same address in every lane)
     float row = 0.0f;
 #pragma unroll
     for (int i = 0; i < UPW; ++i) {
       const int c = wave + KA_WAVES * i;
       if (c < nu) {
-        const cfloat* xw = (const cfloat*)(xt + 64 * c);
+        const float* xw = &s_x[t][64 * c];
         const float2 s0 = bsum[t][2 * c], s1 = bsum[t][2 * c + 1];
         const uint32_t hw0 = FMT == MOE_FMT_Q3G ? gh[i].x : 0u;
         const uint32_t hw1 = FMT == MOE_FMT_Q3G ? gh[i].y : 0u;
@@ -398,6 +452,13 @@ __global__ __launch_bounds__(KA_THREADS) void decode_ffn_kernel(FfnArgs a,
     }
     token_pass(__builtin_ctz(rest));
   }
+  };   // run_job
+  if (LOOP && static_cast<int>(blockIdx.x) >= n_shared) {
+    const int stride = static_cast<int>(gridDim.x) - n_shared;
+    for (int job = blockIdx.x; job < n_jobs; job += stride) run_job(job);
+  } else if (static_cast<int>(blockIdx.x) < n_jobs) {
+    run_job(blockIdx.x);
+  }
 }
 
 // y = x + sum_{i: slot >= 0} w_i * P(t, i) + P(t, k), P(t, i) = sum over
@@ -478,15 +539,44 @@ size_t part_bytes(int d, int f, int T, int k) {
   return static_cast<size_t>(static_cast<int64_t>(T) * (k + 1) * (f / SLICE) * d * 4);
 }
 
+// Workgroups of the ffn kernel: one per job if all fit at two workgroups per
+// CU (two fit together), else one per shared job plus the fewest rounds of
+// the pair jobs over the other places, spread evenly.
+struct FfnGrid {
+  int jobs, grid;
+};
+FfnGrid ffn_grid(int T, int k, int f, int shared_slot, bool miss) {
+  const int nslices = f / SLICE;
+  const int n_shared = shared_jobs_per_slice(shared_slot, miss) * nslices;
+  const int n_pair = T * k * nslices;
+  const int slots = 2 * device_cus();
+  if (n_shared + n_pair <= slots || slots <= n_shared) return {n_shared + n_pair, n_shared + n_pair};
+  const int rounds = (n_pair + (slots - n_shared) - 1) / (slots - n_shared);
+  return {n_shared + n_pair, n_shared + (n_pair + rounds - 1) / rounds};
+}
+
 template <int FMT, int MODE>
 hipError_t launch_ffn(const FfnArgs& a, const float* x, hipStream_t s) {
-  // members: T*k pairs and the shared expert (none in the miss mode)
-  const dim3 grid(a.f / SLICE, a.T * a.k + (MODE == kMiss ? 0 : 1));
+  const FfnGrid g = ffn_grid(a.T, a.k, a.f, a.shared_slot, MODE == kMiss);
+  const int jobs = g.jobs, grid = g.grid;
   const int upw = (a.d / 64 + KA_WAVES - 1) / KA_WAVES;
-  if (upw <= 1)
-    decode_ffn_kernel<FMT, 1, MODE><<<grid, KA_THREADS, 0, s>>>(a, x);
-  else
-    decode_ffn_kernel<FMT, 2, MODE><<<grid, KA_THREADS, 0, s>>>(a, x);
+  // the job loop only where a workgroup takes more than one job (routing
+  // mode: one routing per workgroup for all its jobs)
+  if constexpr (MODE == kRoute) {
+    if (grid < jobs) {
+      if (upw <= 1)
+        decode_ffn_kernel<FMT, 1, MODE, true><<<grid, KA_THREADS, 0, s>>>(a, x);
+      else
+        decode_ffn_kernel<FMT, 2, MODE, true><<<grid, KA_THREADS, 0, s>>>(a, x);
+      return hipGetLastError();
+    }
+  }
+  {
+    if (upw <= 1)
+      decode_ffn_kernel<FMT, 1, MODE, false><<<jobs, KA_THREADS, 0, s>>>(a, x);
+    else
+      decode_ffn_kernel<FMT, 2, MODE, false><<<jobs, KA_THREADS, 0, s>>>(a, x);
+  }
   return hipGetLastError();
 }
 
@@ -495,8 +585,12 @@ FfnArgs ffn_args(const moe_layer& L, int T, const int32_t* slot, void* ws) {
   FfnArgs a = {};
   a.pool = static_cast<const uint8_t*>(L.pool);
   a.slot_bytes = L.slot_bytes;
-  a.G = lay.G;
-  a.D = lay.D;
+  auto p32 = [](const Planes& P) {
+    return Planes32{static_cast<uint32_t>(P.codes), static_cast<uint32_t>(P.hi),
+                    static_cast<uint32_t>(P.scale), static_cast<uint32_t>(P.min)};
+  };
+  a.G = p32(lay.G);
+  a.D = p32(lay.D);
   a.d = L.d_model;
   a.f = L.d_ff;
   a.T = T;

@@ -637,24 +637,6 @@ PrefillWs prefill_ws(void* ws, int d, int f, int T, int k, int E) {
   return w;
 }
 
-// Compute units of the current device, looked up once per device (devices
-// beyond the table are asked every time).
-constexpr int kMaxDevices = 64;
-
-int device_cus() {
-  static std::atomic<int> cus[kMaxDevices] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (dev >= 0 && dev < kMaxDevices) {
-    const int c = cus[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  hipDeviceProp_t prop;
-  const int c = hipGetDeviceProperties(&prop, dev) == hipSuccess ? prop.multiProcessorCount : 256;
-  if (dev >= 0 && dev < kMaxDevices) cus[dev].store(c, std::memory_order_relaxed);
-  return c;
-}
-
 // Persistent grid: one workgroup per CU, a multiple of 8 so that job j and
 // workgroup j mod grid share an XCD.
 int prefill_grid(int64_t max_jobs) {

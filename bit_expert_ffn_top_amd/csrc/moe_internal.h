@@ -48,6 +48,10 @@ hipError_t launch_group_pairs(const int32_t* idx, const int32_t* slot_of_pair,
                               int32_t* tile_base, int tile_m, int32_t* tile_group,
                               int32_t* group_slot, hipStream_t s);
 
+// Compute units of the current device (looked up once per device).
+constexpr int kMaxDevices = 64;
+int device_cus();
+
 size_t decode_workspace_bytes(int d, int f, int T, int k);
 hipError_t launch_decode(const moe_layer& L, const float* x, int T, const int32_t* idx,
                          const int32_t* slot, const float* w, float* y, void* ws,

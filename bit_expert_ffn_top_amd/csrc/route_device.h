@@ -133,12 +133,14 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ logits, int
   topk_select<MAXIT>(lg, T, E, k, s, [] {});
 }
 
-// k-th largest of one 32-bit value per lane (k <= 64): the largest tau with
-// at least k values >= tau, found bit by bit with ballot counts.
+// A lower bound of the k-th largest of one 32-bit value per lane (k <= 64):
+// the largest tau whose low LOW bits are zero with at least k values >= tau,
+// found bit by bit with ballot counts (the k-th largest itself for LOW = 0).
+template <int LOW = 0>
 __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k) {
   uint32_t tau = 0;
 #pragma unroll
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 31; b >= LOW; --b) {
     const uint32_t cand = tau | (1u << b);
     if (__popcll(__ballot(v >= cand)) >= k) tau = cand;
   }
@@ -174,8 +176,9 @@ __device__ __forceinline__ void wave_topk_rounds(uint64_t (&key)[NJ], int k, uin
 // Top-k keys of one token in one whole wavefront: lane l holds the keys of
 // experts 64j + l (j < NJ; key = orderable value << 32 | ~id, 0 for experts
 // >= E, below every real key).  A bound first: tau0, the k-th largest of the
-// 64 lane maxima (by value), has at least k keys whose value is >= tau0, so
-// the top k are among them.  Those candidates (usually a little over k) are
+// 64 lane maxima (by value) with its low 16 bits cleared, has at least k keys
+// whose value is >= tau0, and the k-th largest key is at least the k-th
+// largest lane maximum, so the top k are among them.  Those candidates (usually a little over k) are
 // gathered one per lane and ranked among themselves by (value desc, id asc);
 // the first k, in rank order, go to top[0..k).  When more than 64 keys pass
 // the bound (many equal values), k rounds of the largest remaining key are
@@ -188,7 +191,7 @@ __device__ __forceinline__ void wave_topk_keys(uint64_t (&key)[NJ], int k, uint6
   uint64_t m = key[0];
 #pragma unroll
   for (int j = 1; j < NJ; ++j) m = key[j] > m ? key[j] : m;
-  const uint32_t tau0 = wave_kth_largest(static_cast<uint32_t>(m >> 32), k);
+  const uint32_t tau0 = wave_kth_largest<16>(static_cast<uint32_t>(m >> 32), k);
   const uint64_t below = (1ull << lane) - 1ull;
   int n_c = 0;
 #pragma unroll
