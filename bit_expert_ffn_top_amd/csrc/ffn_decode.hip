@@ -203,10 +203,9 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
   float2 xv[MOE_MAX_DECODE_T];
   const int ex = min(2 * tid, d - 2);
 #pragma unroll
-  for (int t = 0; t < MOE_MAX_DECODE_T; ++t) {
-    const int tt = min(t, a.T - 1);
-    xv[t] = *reinterpret_cast<const float2*>(x + static_cast<int64_t>(tt) * d + ex);
-  }
+  for (int t = 0; t < MOE_MAX_DECODE_T; ++t)   // uniform: only the T tokens' rows
+    xv[t] = t < a.T ? *reinterpret_cast<const float2*>(x + static_cast<int64_t>(t) * d + ex)
+                    : make_float2(0.0f, 0.0f);
   const int nslices = a.f / SLICE;
   // Jobs: first the shared expert's, one per slice js at j = js, then one
   // per (pair u, slice js) at j = n_shared + u * nslices + js.  A workgroup
@@ -218,10 +217,11 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
   const int nchunk = (a.E + kRouteChunk - 1) / kRouteChunk;
   const int rt = wave / kRouteChunks, rc = wave % kRouteChunks;   // token and chunk of a routing wave
   const bool route_wave = routing && rt < a.T && rc < nchunk;
-  float lg[8];
+  float lg[8] = {};
   int tv = 0;
   if (ROUTE) {
     const int tt = min(rt, a.T - 1);
+    if (route_wave)   // uniform: the logits only in the wavefronts that rank them
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       lg[j] = a.logits[static_cast<int64_t>(tt) * a.E + min(rc * kRouteChunk + 64 * j + lane, a.E - 1)];
