@@ -146,36 +146,67 @@ def test_prefill_with_misses():
 
 def test_prefill_full_chunk_sampled():
     """The prefill chunk at full size: T=8192, E=512, top-10 + shared,
-    d=2048, d_ff=768, Q2SM.  Grouping is checked in full; outputs on a sample
-    of tokens the oracle evaluates one by one."""
+    d=2048, d_ff=768, Q2SM.  Grouping is checked in full; against the oracle
+    (one expert unpacked at a time, in worker processes): all 8,192 shared
+    rows, every pair row of 32 whole expert groups (the largest, the
+    smallest and 30 seeded others), and y on 256 seeded tokens; y of every
+    token equals the oracle's combine of the kernel's own rows."""
+    import oracle_pool
     dev = need_gpu()
     shape = synth.config_shape(4)
-    T = 8192
+    T, k, E, d, f = 8192, shape.top_k, shape.n_experts, shape.d_model, shape.d_ff
     L = GpuLayer(4, 0, shape, synth.FMT_Q2SM, dev)
-    x = synth.make_x(4, 0, T, shape.d_model, dtype=torch.bfloat16)
-    logits = synth.make_logits(4, 0, T, shape.n_experts, 1.5)
-    out_pairs, pair_pos, offs, out_sh, y, idx, slot, w = _prefill(L, x, logits, 10, dev)
-    ref_idx = np.argsort(-logits.numpy(), axis=1, kind="stable")[:, :10]
+    x = synth.make_x(4, 0, T, d, dtype=torch.bfloat16)
+    logits = synth.make_logits(4, 0, T, E, 1.5)
+    out_pairs, pair_pos, offs, out_sh, y, idx, slot, w = _prefill(L, x, logits, k, dev)
+    ref_idx = np.argsort(-logits.numpy(), axis=1, kind="stable")[:, :k]
     np.testing.assert_array_equal(idx, ref_idx)
-    roffs, rpos, order = _oracle_groups(idx, slot, shape.n_experts)
+    roffs, rpos, order = _oracle_groups(idx, slot, E)
     np.testing.assert_array_equal(offs, roffs)
     np.testing.assert_array_equal(pair_pos, rpos)
-    sample = np.random.default_rng(1).choice(T, 6, replace=False)
     xd = x.double().numpy()
-    rows_got, rows_ref = [], []
-    for t in sample:
-        ridx, rw = oracle.route_topk(logits.numpy()[t:t + 1], 10)
-        ref = xd[t].copy()
-        for i in range(10):
-            o = oracle.expert_ffn_bf16(xd[t:t + 1], *L.weights_of_expert(int(ridx[0, i])))[0]
-            rows_ref.append(o)
-            rows_got.append(out_pairs.numpy()[pair_pos[t, i]])
-            ref += rw[0, i] * o
-        osh = oracle.expert_ffn_bf16(xd[t:t + 1], *L.weights_of_slot(L.shared_slot))[0]
-        check_close(out_sh.numpy()[t], osh, what="out_shared")
-        ref += osh
-        check_close(y.numpy()[t], ref, xd[t])
-    check_close(np.array(rows_got), np.array(rows_ref), what="out_pairs")
+    op = out_pairs.numpy()
+    yg = y.numpy()
+    osh_ref = oracle.expert_ffn_bf16(xd, *L.weights_of_slot(L.shared_slot))
+    check_close(out_sh.numpy(), osh_ref, what="out_shared (all 8192 rows)")
+    # the combine step on every token, over the kernel's own rows
+    _, rw = oracle.route_topk(logits.numpy(), k)
+    ycomb = oracle.combine(xd, op.astype(np.float64), pair_pos, rw, out_sh.numpy().astype(np.float64))
+    check_close(yg, ycomb, xd, what="y vs combine of the kernel's rows")
+
+    sizes = np.diff(offs)
+    nonempty = np.flatnonzero(sizes > 0)
+    big, small = int(nonempty[np.argmax(sizes[nonempty])]), int(nonempty[np.argmin(sizes[nonempty])])
+    rng = np.random.default_rng(11)
+    others = [int(e) for e in rng.permutation(nonempty) if e not in (big, small)][:30]
+    groups = [big, small] + others
+    flat = idx.reshape(-1)
+    tokens_of = {e: np.array([p // k for p in order[offs[e]:offs[e + 1]]]) for e in groups}
+    sample = np.sort(rng.choice(T, 256, replace=False))
+    need = sorted(set(groups) | set(int(e) for e in idx[sample].reshape(-1)))
+    tasks, keys = [], []
+    for e in need:
+        rows_t = tokens_of[e] if e in tokens_of else np.array([], dtype=np.int64)
+        samp_t = sample[(idx[sample] == e).any(axis=1)]
+        toks = np.unique(np.concatenate([rows_t, samp_t])).astype(np.int64)
+        tasks.append((L._bytes[int(L.table[e])], xd[toks]))
+        keys.append((e, toks))
+    outs = oracle_pool.ffn_rows_many(tasks, L.fmt, d, f)
+    ref_of = {}
+    for (e, toks), o in zip(keys, outs):
+        for t, row in zip(toks, o):
+            ref_of[(e, int(t))] = row
+    for e in groups:
+        got = op[offs[e]:offs[e + 1]]
+        ref = np.stack([ref_of[(e, int(t))] for t in tokens_of[e]])
+        check_close(got, ref, what=f"out_pairs of group {e} ({len(ref)} rows)")
+    yref = np.empty((len(sample), d))
+    for j, t in enumerate(sample):
+        acc = xd[t].copy()
+        for i in range(k):
+            acc += rw[t, i] * ref_of[(int(idx[t, i]), int(t))]
+        yref[j] = acc + osh_ref[t]
+    check_close(yg[sample], yref, xd[sample], what="y on 256 tokens")
 
 
 def test_combine_parity():

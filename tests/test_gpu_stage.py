@@ -4,7 +4,8 @@ tier (moe_stage_layer).
 The staging pool must hold exactly every expert's bytes in expert order, and
 a prefill chunk run on it must give the same bits as on a pool that holds
 every expert resident (at other slots), also when the staging of the next
-layer runs on a second stream during the current layer's prefill.
+layer runs on a second stream during the current layer's prefill; at full
+size its y is also checked against the oracle on sampled tokens.
 """
 import numpy as np
 import pytest
@@ -181,3 +182,22 @@ def test_stage_full_size_bitwise():
     torch.cuda.synchronize()
     for g, r in zip(got, ref):
         assert torch.equal(g, r)
+    # y of the staged prefill against the oracle on 16 seeded tokens (each
+    # chosen expert unpacked once from its packed bytes, in worker processes)
+    import oracle
+    import oracle_pool
+    from parity import check_close
+    sample = np.sort(np.random.default_rng(5).choice(T, 16, replace=False))
+    lg = logits.cpu().numpy()[sample]
+    ridx, rw = oracle.route_topk(lg, k)
+    xd = x.cpu().double().numpy()[sample]
+    host = Lr.packed.cpu().numpy()
+    experts = sorted(set(int(e) for e in ridx.reshape(-1))) + [E]
+    tasks = [(host[e], xd) for e in experts]
+    outs = dict(zip(experts, oracle_pool.ffn_rows_many(tasks, synth.FMT_Q2SM, shape.d_model,
+                                                        shape.d_ff)))
+    yref = xd + outs[E]
+    for j in range(len(sample)):
+        for i in range(k):
+            yref[j] += rw[j, i] * outs[int(ridx[j, i])][j]
+    check_close(got[4].cpu().numpy()[sample], yref, xd, what="staged prefill y")
