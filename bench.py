@@ -142,10 +142,12 @@ class DecodeChain:
     scratch buffer."""
 
     def __init__(self, torch, bf, shape, pools, T, dev, xs, logit_sets, tiers=None,
-                 host_table=None, max_rank=None, counts=None):
+                 host_table=None, max_rank=None, counts=None, overlap=False, misses_only=False):
         self.torch, self.bf = torch, bf
         self.T = T
         self.tiers, self.host_table, self.max_rank = tiers, host_table, max_rank
+        self.overlap = overlap
+        self.misses_only = misses_only   # overlapped step without the GPU part (timing)
         self.counts = counts
         self.logit_sets = logit_sets
         self.layers = [bf.MoeLayer(shape.d_model, shape.d_ff, shape.n_experts, shape.top_k, fmt,
@@ -160,6 +162,9 @@ class DecodeChain:
         self.n_miss = torch.empty((4,), dtype=torch.int32, device=dev)
         ws = max(bf.decode_workspace_bytes(L, T) for L in self.layers)
         self.ws = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        if overlap:   # the host-tier read runs on its own stream, with its own workspace
+            self.ws_miss = torch.empty((ws,), dtype=torch.uint8, device=dev)
+            self.side = torch.cuda.Stream()
         self.xs = xs
         self.y = torch.empty((T, d), dtype=torch.float32, device=dev)
 
@@ -169,6 +174,8 @@ class DecodeChain:
         call that adds the missed experts."""
         bf = self.bf
         logits = self.logit_sets[g]
+        if self.overlap:
+            return self._step_overlapped(logits)
         for l, L in enumerate(self.layers):
             bf.decode_layer(L, self.xs[l], logits[l], self.tables[l], idx=self.idx, w=self.w,
                             slot=self.slot, miss_expert=self.miss_e, miss_pair=self.miss_p,
@@ -178,6 +185,32 @@ class DecodeChain:
                                  self.host_table, self.y, max_rank=self.max_rank, ws=self.ws)
             if self.counts is not None:
                 bf.cache_count(self.idx, self.counts[l])
+        return self.y
+
+    def _step_overlapped(self, logits):
+        """Per layer: routing and lookup; then the missed experts' host-tier
+        read (moe_decode_misses_phases, READ) on the side stream while the GPU
+        part (moe_expert_ffn_decode) runs; then the join (JOIN) once both
+        are done, before the next layer."""
+        torch, bf = self.torch, self.bf
+        main = torch.cuda.current_stream()
+        k = self.layers[0].top_k
+        for l, L in enumerate(self.layers):
+            bf.route_topk(logits[l], k, idx=self.idx, w=self.w)
+            bf.cache_lookup(self.idx, self.tables[l], slot=self.slot, miss_expert=self.miss_e,
+                            miss_pair=self.miss_p, n_miss=self.n_miss)
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                bf.decode_misses(self.tiers[l], self.xs[l], self.idx, self.slot, None,
+                                 self.host_table, None, max_rank=self.max_rank, ws=self.ws_miss,
+                                 phases=bf.MISSES_READ)
+            if not self.misses_only:
+                bf.expert_ffn_decode(L, self.xs[l], self.idx, self.slot, self.w, y=self.y,
+                                     ws=self.ws)
+            main.wait_stream(self.side)
+            bf.decode_misses(self.tiers[l], None, self.idx, self.slot, self.w, self.host_table,
+                             self.y, max_rank=self.max_rank, ws=self.ws_miss,
+                             phases=bf.MISSES_JOIN)
         return self.y
 
 
@@ -505,9 +538,11 @@ def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_gr
     sb = synth.slot_bytes(synth.FMT_Q2SM, d, f)
     res = {}
     misses_per_token = n_missed / n_graphs
-    for name, r in (("full_layer", None), ("rank_limit_5", 5)):
+    for name, r, ov, mo in (("full_layer", None, False, False), ("rank_limit_5", 5, False, False),
+                            ("full_layer_two_streams", None, True, False),
+                            ("host_part_only", None, True, True)):
         chain = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, logits2, tiers=tiers,
-                            host_table=host_table, max_rank=r)
+                            host_table=host_table, max_rank=r, overlap=ov, misses_only=mo)
         dt, _, graphs = time_graph_steps(torch, chain, steps, 5, n_graphs)
         del graphs
         res[name + "_tok_s"] = round(steps / dt, 2)
@@ -535,8 +570,12 @@ def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_gr
         rel.append((y_full - y_lim).norm().item() / upd if upd > 0 else 0.0)
     res["rank_limit_5_rel_change_of_update"] = round(float(np.mean(rel)), 4)
     res["host_tier"] = ("all 512 experts of each layer in pinned host memory, read by the decode "
-                        "kernel over the host link (no copy engine); one moe_decode_misses call "
-                        "per layer after the GPU part, in the same graph")
+                        "kernel over the host link (no copy engine); full_layer, rank_limit_5: "
+                        "moe_decode_layer then moe_decode_misses on one stream, in one graph; "
+                        "full_layer_two_streams: per layer routing and lookup, then the host-tier "
+                        "read (moe_decode_misses_phases READ) on a second stream while the GPU "
+                        "part runs, the join (JOIN) after both; host_part_only: that step "
+                        "without the GPU part")
     log(f"host tier: {res} ({time.perf_counter() - t0:.1f} s)")
     del chain, chain_full
     return res

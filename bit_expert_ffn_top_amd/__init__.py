@@ -4,7 +4,7 @@ The computation lives in libbitffn_moe.so (HIP kernels behind the C ABI of
 include/bitffn_moe.h); this package is its thin Python binding.
 """
 from ._binding import (  # noqa: F401
-    DTYPE_BF16, DTYPE_F32, FMT_Q2S, FMT_Q2SM, FMT_Q3G, HostTier, MoeError, MoeLayer,
+    DTYPE_BF16, MISSES_JOIN, MISSES_READ, DTYPE_F32, FMT_Q2S, FMT_Q2SM, FMT_Q3G, HostTier, MoeError, MoeLayer,
     abi_version,
     cache_commit, cache_count, cache_fill, cache_lookup, cache_plan, combine,
     decode_layer, decode_misses, decode_stack, decode_stack_workspace_bytes,

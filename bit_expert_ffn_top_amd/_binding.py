@@ -69,6 +69,8 @@ SIGNATURES = {
                                   _vp, _c_sz, _vp]),
     "moe_decode_misses": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp, _vp,
                                    _c_sz, _vp]),
+    "moe_decode_misses_phases": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp,
+                                          _vp, _c_sz, _c_int, _vp]),
     "moe_cache_count": (_c_int, [_vp, _c_int, _c_int, _vp, _vp]),
     "moe_cache_plan": (_c_int, [_vp, _c_int, _vp, _vp, _c_int, _c_int, _vp, _c_int, _c_int,
                                 _c_int, _vp, _vp, _vp]),
@@ -408,30 +410,36 @@ class HostTier:
                          n_slots, -1, 0, sb, self.pool.data_ptr())
 
 
+MISSES_READ, MISSES_JOIN = 1, 2   # phases of moe_decode_misses_phases
+
+
 def decode_misses(tier: HostTier, x, idx, slot, w, host_slot_of_expert, y, max_rank=None,
-                  ws=None, stream=None):
+                  ws=None, stream=None, phases=MISSES_READ | MISSES_JOIN):
     """Add the missed pairs of a decode step, computed from the host tier,
-    into y (moe_decode_misses).  y holds the GPU part on entry.  Returns y."""
-    _shape(x, (None, tier.d_model), "x")
-    T = x.shape[0]
+    into y (moe_decode_misses).  y holds the GPU part on entry.  Returns y.
+    phases: MISSES_READ (the products into ws; y, w unused and may be None),
+    MISSES_JOIN (y += the products in ws; x may be None), or both
+    (moe_decode_misses_phases)."""
+    T = (x if x is not None else y).shape[0]
     k = tier.top_k
-    for t, shp, name in ((idx, (T, k), "idx"), (slot, (T, k), "slot"), (w, (T, k), "w"),
-                         (host_slot_of_expert, (tier.n_experts,), "host_slot_of_expert"),
-                         (y, (T, tier.d_model), "y")):
-        _shape(t, shp, name)
-    for t, dt, name in ((x, torch.float32, "x"), (idx, torch.int32, "idx"),
-                        (slot, torch.int32, "slot"), (w, torch.float32, "w"),
-                        (host_slot_of_expert, torch.int32, "host_slot_of_expert"),
-                        (y, torch.float32, "y")):
-        _dev(t, dt, name)
+    read, join = bool(phases & MISSES_READ), bool(phases & MISSES_JOIN)
+    checks = [(idx, (T, k), torch.int32, "idx"), (slot, (T, k), torch.int32, "slot"),
+              (host_slot_of_expert, (tier.n_experts,), torch.int32, "host_slot_of_expert")]
+    if read or x is not None:
+        checks.append((x, (T, tier.d_model), torch.float32, "x"))
+    if join:
+        checks += [(w, (T, k), torch.float32, "w"), (y, (T, tier.d_model), torch.float32, "y")]
+    for t, shp, dt, name in checks:
+        _dev(_shape(t, shp, name), dt, name)
     r = k if max_rank is None else int(max_rank)
     L = tier.c_struct()
     if ws is None:
         ws = torch.empty((int(lib().moe_decode_workspace_bytes(ctypes.byref(L), T)),),
-                         dtype=torch.uint8, device=x.device)
-    _check(lib().moe_decode_misses(ctypes.byref(L), _ptr(x), T, _ptr(idx), _ptr(slot), _ptr(w),
-                                   _ptr(host_slot_of_expert), r, _ptr(y), _ptr(ws), ws.numel(),
-                                   _stream(stream)), "moe_decode_misses")
+                         dtype=torch.uint8, device=idx.device)
+    _check(lib().moe_decode_misses_phases(ctypes.byref(L), _ptr(x), T, _ptr(idx), _ptr(slot),
+                                          _ptr(w), _ptr(host_slot_of_expert), r, _ptr(y),
+                                          _ptr(ws), ws.numel(), int(phases), _stream(stream)),
+           "moe_decode_misses_phases")
     return y
 
 

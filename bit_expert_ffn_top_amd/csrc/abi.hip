@@ -216,15 +216,26 @@ int moe_decode_stack(int d_model, int d_ff, int n_experts, int top_k, int T, int
 int moe_decode_misses(const moe_layer* H, const float* x, int T, const int32_t* idx,
                       const int32_t* slot, const float* w, const int32_t* host_slot_of_expert,
                       int max_rank, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return moe_decode_misses_phases(H, x, T, idx, slot, w, host_slot_of_expert, max_rank, y, ws,
+                                  ws_bytes, MOE_MISSES_READ | MOE_MISSES_JOIN, stream);
+}
+
+int moe_decode_misses_phases(const moe_layer* H, const float* x, int T, const int32_t* idx,
+                             const int32_t* slot, const float* w,
+                             const int32_t* host_slot_of_expert, int max_rank, float* y, void* ws,
+                             size_t ws_bytes, int phases, hipStream_t stream) {
   const int st = check_layer(H);
   if (st != MOE_OK) return st;
   if (H->shared_slot != -1) return MOE_EINVAL;
   if (T < 1 || T > MOE_MAX_DECODE_T || T * H->top_k > MOE_MAX_DECODE_PAIRS) return MOE_EINVAL;
   if (max_rank < 0 || max_rank > H->top_k) return MOE_EINVAL;
-  if (!x || !idx || !slot || !w || !host_slot_of_expert || !y || !ws) return MOE_EINVAL;
-  if (static_cast<const void*>(x) == static_cast<const void*>(y)) return MOE_EINVAL;
-  if (!aligned16(x) || !aligned16(idx) || !aligned16(slot) || !aligned16(w) ||
-      !aligned16(host_slot_of_expert) || !aligned16(y))
+  if (phases < 1 || phases > (MOE_MISSES_READ | MOE_MISSES_JOIN)) return MOE_EINVAL;
+  const bool read = (phases & MOE_MISSES_READ) != 0, join = (phases & MOE_MISSES_JOIN) != 0;
+  if (!idx || !slot || !host_slot_of_expert || !ws || (read && !x) || (join && (!w || !y)))
+    return MOE_EINVAL;
+  if (x && y && static_cast<const void*>(x) == static_cast<const void*>(y)) return MOE_EINVAL;
+  if ((x && !aligned16(x)) || !aligned16(idx) || !aligned16(slot) || (w && !aligned16(w)) ||
+      !aligned16(host_slot_of_expert) || (y && !aligned16(y)))
     return MOE_EALIGN;
   if (!aligned256(ws)) return MOE_EALIGN;
   if (ws_bytes < bitffn::decode_workspace_bytes(H->d_model, H->d_ff, T, H->top_k))
@@ -235,7 +246,8 @@ int moe_decode_misses(const moe_layer* H, const float* x, int T, const int32_t* 
   if (!device_address(H->pool, &pool_dev)) return MOE_EINVAL;
   if (max_rank == 0) return MOE_OK;   // no miss can run
   return hip_status(bitffn::launch_decode_misses(*H, pool_dev, x, T, idx, slot, w,
-                                                 host_slot_of_expert, max_rank, y, ws, stream));
+                                                 host_slot_of_expert, max_rank, y, ws, stream,
+                                                 phases));
 }
 
 int moe_cache_count(const int32_t* idx, int n_pairs, int E, uint32_t* counts,

@@ -673,7 +673,7 @@ hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const 
 hipError_t launch_decode_misses(const moe_layer& H, const void* host_pool_dev, const float* x,
                                 int T, const int32_t* idx, const int32_t* slot, const float* w,
                                 const int32_t* host_slot_of_expert, int max_rank, float* y,
-                                void* ws, hipStream_t s) {
+                                void* ws, hipStream_t s, int phases) {
   FfnArgs a = ffn_args(H, T, slot, ws);
   a.pool = static_cast<const uint8_t*>(host_pool_dev);
   a.shared_slot = -1;
@@ -681,9 +681,13 @@ hipError_t launch_decode_misses(const moe_layer& H, const void* host_pool_dev, c
   a.idx = idx;
   a.max_rank = max_rank;
   a.n_slots = H.n_slots;
-  const hipError_t e = launch_ffn_fmt<kMiss>(H.fmt, a, x, s);
-  if (e != hipSuccess) return e;
-  return launch_combine_misses(H, T, idx, slot, w, host_slot_of_expert, max_rank, a.part, y, s);
+  if (phases & MOE_MISSES_READ) {
+    const hipError_t e = launch_ffn_fmt<kMiss>(H.fmt, a, x, s);
+    if (e != hipSuccess) return e;
+  }
+  if (phases & MOE_MISSES_JOIN)
+    return launch_combine_misses(H, T, idx, slot, w, host_slot_of_expert, max_rank, a.part, y, s);
+  return hipSuccess;
 }
 
 }  // namespace bitffn

@@ -71,7 +71,7 @@ hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const 
 hipError_t launch_decode_misses(const moe_layer& H, const void* host_pool_dev, const float* x,
                                 int T, const int32_t* idx, const int32_t* slot, const float* w,
                                 const int32_t* host_slot_of_expert, int max_rank, float* y,
-                                void* ws, hipStream_t s);
+                                void* ws, hipStream_t s, int phases = MOE_MISSES_READ | MOE_MISSES_JOIN);
 
 // Expert-cache admission and eviction (cache_policy.hip).
 hipError_t launch_cache_count(const int32_t* idx, int n, int E, uint32_t* counts,

@@ -292,6 +292,30 @@ int moe_decode_misses(const moe_layer* H, const float* x, int T,
                       const int32_t* host_slot_of_expert, int max_rank,
                       float* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_decode_misses in two phases that the caller may put on different
+ * streams, so that the host-tier reads overlap the GPU part ("Strataとは？
+ * VRAM 12GBのGPUで…" (vramglass.com), section "その2": the missed experts
+ * are computed at the same time as the resident ones; "FreeToken vs
+ * Strata", "共通の仕組み": the parts meet before the next layer).
+ *   MOE_MISSES_READ  the missed experts' products into ws (reads x, idx,
+ *                    slot, host_slot_of_expert and the host tier; w and y
+ *                    are not used and may be NULL);
+ *   MOE_MISSES_JOIN  y += those products, as moe_decode_misses adds them
+ *                    (reads ws, idx, slot, w, host_slot_of_expert; x may be
+ *                    NULL).
+ * phases = READ | JOIN is moe_decode_misses.  The JOIN of a step must run
+ * after its READ has completed and after y holds the GPU part (the caller
+ * orders the streams, e.g. with events); between the two, ws belongs to the
+ * call.  The result is the same, bit for bit, as moe_decode_misses.  Other
+ * arguments and limits as moe_decode_misses. */
+#define MOE_MISSES_READ 1
+#define MOE_MISSES_JOIN 2
+int moe_decode_misses_phases(const moe_layer* H, const float* x, int T,
+                             const int32_t* idx, const int32_t* slot, const float* w,
+                             const int32_t* host_slot_of_expert, int max_rank,
+                             float* y, void* ws, size_t ws_bytes, int phases,
+                             hipStream_t stream);
+
 /* Expert-cache admission and eviction.  The cache starts from a table of
  * usage frequencies and is updated as the conversation moves on ("FreeToken
  * vs Strata", comparison table, row "VRAMのエキスパートの入れ替え";

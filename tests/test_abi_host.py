@@ -175,6 +175,17 @@ def test_decode_misses_host_checks():
     assert call(H, y=_p()) == -1                                            # y aliases x
     assert call(_layer(shared_slot=-1, fmt=9)) == -3
 
+    def phases(ph, x=_p(), y=_p(1 << 20), w=_p(1 << 21)):
+        return lib.moe_decode_misses_phases(ctypes.byref(H), x, 1, _p(), _p(), w, _p(), 10, y,
+                                            _p(), need, ph, s)
+    assert phases(0) == -1
+    assert phases(4) == -1
+    assert phases(1, x=None) == -1                                           # the read needs x
+    assert phases(2, y=None) == -1                                           # the join needs y ...
+    assert phases(2, w=None) == -1                                           # ... and w
+    assert phases(3, y=_p()) == -1                                           # y aliases x
+    assert phases(2, x=None, y=_p(8)) == -2
+
 
 def test_cache_policy_host_checks():
     lib = _lib()

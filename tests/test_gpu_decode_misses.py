@@ -4,8 +4,10 @@ The GPU part (moe_decode_layer over the resident experts) followed by
 moe_decode_misses (the missed experts read from a pinned host copy of the
 layer) must equal the oracle's two-tier layer within the fp32 bounds, for
 every rank limit; a step without misses must leave y bit for bit as it was;
-graph replays must equal the eager call bit for bit; the host-side argument
-checks must refuse what the header rules out.
+graph replays must equal the eager call bit for bit; the two phases on two
+streams (host-tier read overlapping the GPU part, join after both) must give
+the serial call's bits; the host-side argument checks must refuse what the
+header rules out.
 """
 import ctypes
 
@@ -232,6 +234,75 @@ def test_misses_graph_replay_matches_eager():
     ref = _oracle(L, H, x, bufs["idx"].cpu().numpy(), bufs["w"].cpu().numpy(),
                   bufs["slot"].cpu().numpy(), None)
     check_close(eager.cpu().numpy(), ref, x.cpu().numpy())
+
+
+def _overlapped_step(bf, L, H, x, logits, tab, htab, bufs, ws_gpu, ws_miss, side, max_rank=None):
+    """Routing and lookup, then the host-tier read on stream `side` while the
+    GPU part runs on the current stream; the join after both."""
+    main = torch.cuda.current_stream()
+    k = L.shape.top_k
+    bf.route_topk(logits, k, idx=bufs["idx"], w=bufs["w"])
+    bf.cache_lookup(bufs["idx"], tab, slot=bufs["slot"], miss_expert=bufs["miss_expert"],
+                    n_miss=bufs["n_miss"])
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        bf.decode_misses(H.tier, x, bufs["idx"], bufs["slot"], None, htab, None,
+                         max_rank=max_rank, ws=ws_miss, phases=bf.MISSES_READ)
+    bf.expert_ffn_decode(L.layer_obj, x, bufs["idx"], bufs["slot"], bufs["w"], y=bufs["y"],
+                         ws=ws_gpu)
+    main.wait_stream(side)
+    bf.decode_misses(H.tier, None, bufs["idx"], bufs["slot"], bufs["w"], htab, bufs["y"],
+                     max_rank=max_rank, ws=ws_miss, phases=bf.MISSES_JOIN)
+
+
+@pytest.mark.parametrize("max_rank", [None, 4])
+def test_misses_two_phases_on_two_streams(max_rank):
+    """The host-tier read on a second stream, overlapping the GPU part, and
+    the join after both: the same bits as the GPU part followed by
+    moe_decode_misses, eager and in every replay of a captured graph."""
+    import bit_expert_ffn_top_amd as bf
+    dev = need_gpu()
+    shape = synth.LayerShape(200, 10, 512, 256, True)
+    T = 3
+    rng = np.random.default_rng(8)
+    resident = sorted(rng.choice(200, 70, replace=False).tolist())
+    L = GpuLayer(0, 11, shape, synth.FMT_Q2SM, dev, resident=resident)
+    x = synth.make_x(0, 11, T, shape.d_model).to(dev)
+    logits = synth.make_logits(0, 11, T, 200, 1.0)
+    H = HostTier(0, 11, shape, synth.FMT_Q2SM, _chosen(logits, 10), seed=8)
+    logits = logits.to(dev)
+    tab, htab = L.table_dev(dev), H.table_dev()
+    k = shape.top_k
+    y_ser, *_ = _run(L, H, x, logits, max_rank)
+    bufs = dict(idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+                w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                slot=torch.empty((T, k), dtype=torch.int32, device=dev),
+                miss_expert=torch.empty((T * k,), dtype=torch.int32, device=dev),
+                n_miss=torch.empty((4,), dtype=torch.int32, device=dev),
+                y=torch.empty((T, shape.d_model), dtype=torch.float32, device=dev))
+    nb = bf.decode_workspace_bytes(L.layer_obj, T)
+    ws_gpu = torch.empty((nb,), dtype=torch.uint8, device=dev)
+    ws_miss = torch.empty((nb,), dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream()
+    step = lambda: _overlapped_step(bf, L, H, x, logits, tab, htab, bufs, ws_gpu, ws_miss, side,
+                                    max_rank)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(bufs["y"].cpu(), y_ser)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        bufs["y"].fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["y"].cpu(), y_ser)
+        step()                                    # eager work between replays
+        torch.cuda.synchronize()
 
 
 def test_misses_argument_checks():
