@@ -64,6 +64,8 @@ SIGNATURES = {
     "moe_expert_ffn_decode": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
     "moe_decode_layer": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _c_sz, _vp]),
+    "moe_decode_layer_noalloc": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp, _vp]),
     "moe_decode_stack_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "moe_decode_stack": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _SLP, _vp,
                                   _vp, _c_sz, _vp]),
@@ -285,14 +287,35 @@ def decode_layer(layer: MoeLayer, x, logits, slot_of_expert, idx=None, w=None, s
         _dev(_at_least(miss_pair, n, "miss_pair"), torch.int32, "miss_pair")
     _dev(_at_least(n_miss, 2, "n_miss"), torch.int32, "n_miss")
     _dev(_shape(y, tuple(x.shape), "y"), torch.float32, "y")
+    L = layer.c_struct()
+    if ws is _NO_WS:   # moe_decode_layer_noalloc: the library's own scratch
+        _check(lib().moe_decode_layer_noalloc(ctypes.byref(L), _ptr(x), T, _ptr(logits),
+                                              _ptr(slot_of_expert), _ptr(idx), _ptr(w),
+                                              _ptr(slot), _ptr(miss_expert), _ptr(miss_pair),
+                                              _ptr(n_miss), _ptr(y), _stream(stream)),
+               "moe_decode_layer_noalloc")
+        return y, idx, w, slot, miss_expert, miss_pair, n_miss
     if ws is None:
         ws = torch.empty((decode_workspace_bytes(layer, T),), dtype=torch.uint8, device=dev)
-    L = layer.c_struct()
     _check(lib().moe_decode_layer(ctypes.byref(L), _ptr(x), T, _ptr(logits),
                                   _ptr(slot_of_expert), _ptr(idx), _ptr(w), _ptr(slot),
                                   _ptr(miss_expert), _ptr(miss_pair), _ptr(n_miss), _ptr(y),
                                   _ptr(ws), ws.numel(), _stream(stream)), "moe_decode_layer")
     return y, idx, w, slot, miss_expert, miss_pair, n_miss
+
+
+_NO_WS = object()
+
+
+def decode_layer_noalloc(layer: MoeLayer, x, logits, slot_of_expert, idx=None, w=None, slot=None,
+                         miss_expert=None, miss_pair=None, n_miss=None, y=None, want_pairs=True,
+                         stream=None):
+    """decode_layer through moe_decode_layer_noalloc (no workspace: the
+    library's own scratch array).  Outputs not given are allocated here, by
+    torch; pass every output to allocate nothing."""
+    return decode_layer(layer, x, logits, slot_of_expert, idx=idx, w=w, slot=slot,
+                        miss_expert=miss_expert, miss_pair=miss_pair, n_miss=n_miss, y=y,
+                        ws=_NO_WS, want_pairs=want_pairs, stream=stream)
 
 
 def decode_stack_workspace_bytes(d_model, d_ff, n_experts, top_k, T) -> int:

@@ -3,6 +3,8 @@
 #include <stdint.h>
 
 #include "bitffn_moe.h"
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace {
@@ -23,6 +25,33 @@ bool valid_dims(int fmt, int d, int f) {
   if (d < 64 || d > 2048 || d % 64 != 0) return false;
   if (f < 32 || f > 4096 || f % 32 != 0) return false;
   return true;
+}
+
+// Scratch of moe_decode_layer_noalloc: a file-scope device array, one copy
+// per GPU, kept until the process ends.  Host code never passes the array's
+// name to a kernel (that is a host-side stand-in); it asks the runtime for
+// each device's address once, with that device current, and uses that.
+constexpr size_t kNoAllocScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kScratchDevices] = {};
+
+// This device's address of `scratch` (looked up on the first call per
+// device); nullptr with *err set when the lookup fails.
+void* scratch_address(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kScratchDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 bool valid_fmt(int fmt) {
@@ -167,6 +196,22 @@ int moe_decode_layer(const moe_layer* L, const float* x, int T, const float* log
     return MOE_ENOSPC;
   return hip_status(bitffn::launch_decode_layer(*L, x, T, logits, slot_of_expert, idx, w, slot,
                                                 miss_expert, miss_pair, n_miss, y, ws, stream));
+}
+
+int moe_decode_layer_noalloc(const moe_layer* L, const float* x, int T, const float* logits,
+                             const int32_t* slot_of_expert, int32_t* idx, float* w,
+                             int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
+                             int32_t* n_miss, float* y, hipStream_t stream) {
+  const int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 1 || T > MOE_MAX_DECODE_T || T * L->top_k > MOE_MAX_DECODE_PAIRS) return MOE_EINVAL;
+  if (bitffn::decode_workspace_bytes(L->d_model, L->d_ff, T, L->top_k) > kNoAllocScratchBytes)
+    return MOE_ENOSPC;
+  hipError_t e = hipSuccess;
+  void* ws = scratch_address(&e);
+  if (!ws) return hip_status(e);
+  return moe_decode_layer(L, x, T, logits, slot_of_expert, idx, w, slot, miss_expert, miss_pair,
+                          n_miss, y, ws, kNoAllocScratchBytes, stream);
 }
 
 size_t moe_decode_stack_workspace_bytes(int d_model, int d_ff, int n_experts, int top_k, int T) {

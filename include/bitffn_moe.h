@@ -194,6 +194,22 @@ int moe_decode_layer(const moe_layer* L, const float* x, int T,
                      int32_t* miss_expert, int32_t* miss_pair, int32_t* n_miss,
                      float* y, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_decode_layer with no workspace argument and no allocation, for
+ * callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace is a 16 MiB array
+ * in device memory that the library holds on every GPU it runs on until the
+ * process ends; its address is looked up once per device.  Sizes whose
+ * moe_decode_workspace_bytes(L, T) exceeds 16 MiB give MOE_ENOSPC (the
+ * model's layer, d_model 2048, d_ff 768, top-10, needs 8.7 MB at T = 4).
+ * Every call on one GPU uses the same array: calls that overlap on a GPU
+ * (on different streams, without ordering between them) race and give
+ * undefined results.  Arguments, outputs and limits as moe_decode_layer. */
+int moe_decode_layer_noalloc(const moe_layer* L, const float* x, int T,
+                             const float* logits, const int32_t* slot_of_expert,
+                             int32_t* idx, float* w, int32_t* slot,
+                             int32_t* miss_expert, int32_t* miss_pair,
+                             int32_t* n_miss, float* y, hipStream_t stream);
+
 /* Decode / verify through a stack of layers ("Strata" page, "Strataとは":
  * 48 MoE layers, each choosing 10 of 512 experts plus a shared one per
  * token; "FreeToken vs Strata", "共通の仕組み": a layer's output is complete
