@@ -48,6 +48,10 @@ PREFILL_SOURCES = ["bit_expert_ffn_top_amd/csrc/ffn_prefill.hip",
                    "bit_expert_ffn_top_amd/csrc/cache_lookup.hip",
                    "bit_expert_ffn_top_amd/csrc/moe_common.h",
                    "bit_expert_ffn_top_amd/csrc/route_device.h"]
+VERIFY_TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                                   "verify_t4_e512_k10_d2048_f768_q2sm_q3g_kernel_stats_and_traffic.txt")
+PREFILL_MFMA_FILE = os.path.join(ROOT, "profiles",
+                                 "prefill_e512_k10_d2048_f768_q2sm_t8192_mfma_counters.txt")
 
 
 def log(*a):
@@ -69,9 +73,12 @@ def parse():
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill workload (for profiling); prints its object")
     ap.add_argument("--counters", action="store_true",
-                    help="counter pass for rocprofv3 --pmc: eager decode layer calls plus one "
+                    help="counter pass for rocprofv3 --pmc: two eager decode steps plus one "
                          "device copy of COPY_BYTES for calibration; prints no result line "
                          "(with --prefill-only: the prefill workload, then the copy)")
+    ap.add_argument("--counters-verify", action="store_true",
+                    help="counter pass of the verify step (T = 4): two eager steps, then the "
+                         "calibration copy; prints no result line")
     return ap.parse_args()
 
 
@@ -257,6 +264,23 @@ def sources_digest(paths):
     return h.hexdigest()[:16]
 
 
+def summary_keys(path, sources):
+    """The key: value lines of a committed counter summary, or None when the
+    file is missing or the kernels' sources changed since it was taken."""
+    try:
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    kv[key.strip()] = val.strip()
+        if kv.get("sources_sha256_16") != sources_digest(sources):
+            return None
+        return kv
+    except OSError:
+        return None
+
+
 def measured_traffic(path=TRAFFIC_FILE, sources=DECODE_SOURCES):
     """HBM bytes per unit from a committed counter summary (FETCH_SIZE +
     WRITE_SIZE per dispatch, scaled by what the counters read for a plain
@@ -336,6 +360,11 @@ def main():
         print(json.dumps({"prefill": run_prefill(torch, np, bf, synth, pools, dev, args)}), flush=True)
         if args.counters:
             calibration_copy(torch, dev)
+        return
+
+    if args.counters_verify:
+        chain3, _, _ = verify_chain(torch, bf, synth, shape, pools, dev, 2)
+        counter_pass(torch, bf, synth, chain3, dev)
         return
 
     # ---------------- decode (headline) ----------------
@@ -459,20 +488,7 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
 
     # ---------------- verify step ----------------
     t0 = time.perf_counter()
-    pools3 = []
-    for l in range(N_LAYERS):
-        if l % 2 == 0:
-            pools3.append(pools[l])       # Q2SM layers shared with the decode workload
-        else:
-            table, shared_slot, slot_expert = synth.make_slot_table(3, l)
-            pool = synth.make_layer_pool(3, l, slot_expert, device=dev, fmt=synth.FMT_Q3G, batch=64)
-            pools3.append((pool, torch.tensor(table, dtype=torch.int32, device=dev), shared_slot,
-                           synth.FMT_Q3G))
-    logits3 = [torch.stack([synth.make_logits(3, l, 4, E, 1.5, device=dev, step=g)
-                            for l in range(N_LAYERS)]) for g in range(n_graphs)]
-    xs3 = [synth.make_x(3, l, 4, d, device=dev) for l in range(N_LAYERS)]
-    chain3 = StackStep(torch, bf, shape, pools3, 4, dev, xs3[0], logits3)
-    chain3.set_addends(xs3)
+    chain3, pools3, logits3 = verify_chain(torch, bf, synth, shape, pools, dev, n_graphs)
     steps3 = max(20, args.steps // 2)
     dt, ev_ms3, graphs = time_graph_steps(torch, chain3, steps3, 5, n_graphs)
     del graphs
@@ -495,6 +511,8 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
         "hbm_GBps_algorithmic": round(step_bytes * sps / 1e9, 1),
         "frac_of_hbm_peak": round(step_bytes * sps / 1e9 / HBM_PEAK_GBS, 4),
         "avg_layer_us": round(ev_ms3 * 1e3 / (steps3 * N_LAYERS), 3),
+        "bytes_per_layer_algorithmic": round(step_bytes / N_LAYERS),
+        "traffic": measured_traffic(VERIFY_TRAFFIC_FILE, DECODE_SOURCES),
     }
     log(f"verify: {sps:.1f} steps/s, union {mean_u:.2f} ({time.perf_counter() - t0:.1f} s)")
     del pools3, chain3, logits3
@@ -503,6 +521,28 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
     # ---------------- prefill chunk ----------------
     out["prefill"] = run_prefill(torch, np, bf, synth, pools, dev, args)
     return out
+
+
+def verify_chain(torch, bf, synth, shape, pools, dev, n_graphs):
+    """The verify workload: 1 + 3 tokens through 48 layers alternating Q2SM
+    (the decode workload's pools) and Q3G; a StackStep over n_graphs logit
+    sets, its addends set."""
+    E, d = shape.n_experts, shape.d_model
+    pools3 = []
+    for l in range(N_LAYERS):
+        if l % 2 == 0:
+            pools3.append(pools[l])       # Q2SM layers shared with the decode workload
+        else:
+            table, shared_slot, slot_expert = synth.make_slot_table(3, l)
+            pool = synth.make_layer_pool(3, l, slot_expert, device=dev, fmt=synth.FMT_Q3G, batch=64)
+            pools3.append((pool, torch.tensor(table, dtype=torch.int32, device=dev), shared_slot,
+                           synth.FMT_Q3G))
+    logits3 = [torch.stack([synth.make_logits(3, l, 4, E, 1.5, device=dev, step=g)
+                            for l in range(N_LAYERS)]) for g in range(n_graphs)]
+    xs3 = [synth.make_x(3, l, 4, d, device=dev) for l in range(N_LAYERS)]
+    chain3 = StackStep(torch, bf, shape, pools3, 4, dev, xs3[0], logits3)
+    chain3.set_addends(xs3)
+    return chain3, pools3, logits3
 
 
 def build_host_tiers(torch, bf, synth, shape, dev):
@@ -858,7 +898,22 @@ def run_prefill(torch, np, bf, synth, pools, dev, args):
             "traffic": measured_traffic(PREFILL_TRAFFIC_FILE, PREFILL_SOURCES),
             "avg_call_ms": round(call_ms, 4), "flops_per_call": flops,
         },
+        "mfma_busy_counters": mfma_busy_counters(),
     }
+
+
+def mfma_busy_counters():
+    """MFMA utilisation of the two prefill GEMMs from the committed rocprofv3
+    counter summary (SQ_VALU_MFMA_BUSY_CYCLES over the active cycles of all
+    SIMDs), or None when the prefill sources changed since it was taken."""
+    kv = summary_keys(PREFILL_MFMA_FILE, PREFILL_SOURCES)
+    if kv is None:
+        return None
+    try:
+        return {"gate_up": float(kv["mfma_busy_gate_up"]), "down": float(kv["mfma_busy_down"]),
+                "source": os.path.basename(PREFILL_MFMA_FILE)}
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(np, synth, pools, shape):

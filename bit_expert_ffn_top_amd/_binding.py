@@ -452,8 +452,10 @@ def decode_misses(tier: HostTier, x, idx, slot, w, host_slot_of_expert, y, max_r
         checks.append((x, (T, tier.d_model), torch.float32, "x"))
     if join:
         checks += [(w, (T, k), torch.float32, "w"), (y, (T, tier.d_model), torch.float32, "y")]
+    for t, shp, dt, name in checks:   # every shape first, then the devices and types
+        _shape(t, shp, name)
     for t, shp, dt, name in checks:
-        _dev(_shape(t, shp, name), dt, name)
+        _dev(t, dt, name)
     r = k if max_rank is None else int(max_rank)
     L = tier.c_struct()
     if ws is None:

@@ -8,9 +8,12 @@ import bench
 
 
 def test_committed_traffic_summaries_match_sources():
-    # both summaries in profiles/ were taken on the kernels as committed
+    # the summaries in profiles/ were taken on the kernels as committed
     assert bench.measured_traffic() is not None
+    assert bench.measured_traffic(bench.VERIFY_TRAFFIC_FILE, bench.DECODE_SOURCES) is not None
     assert bench.measured_traffic(bench.PREFILL_TRAFFIC_FILE, bench.PREFILL_SOURCES) is not None
+    m = bench.mfma_busy_counters()
+    assert m is not None and 0 < m["gate_up"] < 1 and 0 < m["down"] < 1
 
 
 def test_traffic_is_dropped_when_sources_change(tmp_path):
