@@ -150,7 +150,7 @@ int moe_cache_lookup(const int32_t* idx, int T, int k, const int32_t* slot_of_ex
   hipError_t e = bitffn::launch_lookup_slots(idx, T, k, slot_of_expert, slot, stream);
   if (e != hipSuccess) return hip_status(e);
   const bitffn::GroupWorkspace gws = bitffn::group_workspace(ws, T, E);
-  return hip_status(bitffn::launch_group_pairs(idx, slot, nullptr, T, k, E, false, gws, nullptr,
+  return hip_status(bitffn::launch_group_pairs(idx, slot, nullptr, T, k, E, false, 0, gws, nullptr,
                                                miss_pair, nullptr, miss_expert, n_miss, nullptr,
                                                0, nullptr, nullptr, stream));
 }

@@ -88,14 +88,14 @@ __global__ __launch_bounds__(64) void lookup_wave_kernel(
   wave_miss_lists(p, n, e, s, miss_expert, miss_pair, n_miss);
 }
 
-__device__ __forceinline__ bool selected(int s, bool select_hits) {
-  return select_hits ? (s >= 0) : (s < 0);
+__device__ __forceinline__ bool selected(int s, bool select_hits, int n_slots) {
+  return select_hits ? (s >= 0 && s < n_slots) : (s < 0);
 }
 
 // pass 1: per-chunk histograms
 __global__ __launch_bounds__(256) void group_count_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ slot_of_pair,
-    const int32_t* __restrict__ table, int T, int k, int E, bool select_hits,
+    const int32_t* __restrict__ table, int T, int k, int E, bool select_hits, int n_slots,
     int32_t* __restrict__ chunk_counts) {
   __shared__ int32_t hist[kMaxE];
   const int chunk = blockIdx.x;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void group_count_kernel(
   for (int p = t0 * k + threadIdx.x; p < t1 * k; p += blockDim.x) {
     const int e = idx[p];
     const int s = slot_of_pair ? slot_of_pair[p] : table[e];
-    if (selected(s, select_hits)) atomicAdd(&hist[e], 1);
+    if (selected(s, select_hits, n_slots)) atomicAdd(&hist[e], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x)
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(1024) void group_scan_kernel(
 // pass 3: stable scatter, one wavefront per chunk of tokens
 __global__ __launch_bounds__(64) void group_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ slot_of_pair,
-    const int32_t* __restrict__ table, int T, int k, int E, bool select_hits,
+    const int32_t* __restrict__ table, int T, int k, int E, bool select_hits, int n_slots,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ starts,
     int32_t* __restrict__ perm, int32_t* __restrict__ pos, int32_t* __restrict__ group_slot) {
   __shared__ int32_t cursor[kMaxE];
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(64) void group_scatter_kernel(
         const int e = idx[p];
         const int s = slot_of_pair ? slot_of_pair[p] : table[e];
         int at = -1;
-        if (selected(s, select_hits)) {
+        if (selected(s, select_hits, n_slots)) {
           at = atomicAdd(&cursor[e], 1);
           if (perm) perm[at] = p;
           if (group_slot && at == starts[e]) group_slot[e] = s;   // the group's first pair
@@ -289,20 +289,20 @@ GroupWorkspace group_workspace(void* ws, int T, int E) {
 
 hipError_t launch_group_pairs(const int32_t* idx, const int32_t* slot_of_pair,
                               const int32_t* table, int T, int k, int E, bool select_hits,
-                              GroupWorkspace gws, int32_t* offsets, int32_t* perm,
+                              int n_slots, GroupWorkspace gws, int32_t* offsets, int32_t* perm,
                               int32_t* pos, int32_t* distinct, int32_t* counts_out,
                               int32_t* tile_base, int tile_m, int32_t* tile_group,
                               int32_t* group_slot, hipStream_t s) {
   const int n_chunks = (T + kGroupChunkTokens - 1) / kGroupChunkTokens;
   group_count_kernel<<<n_chunks, 256, 0, s>>>(idx, slot_of_pair, table, T, k, E, select_hits,
-                                              gws.chunk_counts);
+                                              n_slots, gws.chunk_counts);
   group_scan_chunks_kernel<<<E, kScanThreads, 0, s>>>(n_chunks, E, gws.chunk_counts,
                                                       gws.totals);
   group_scan_kernel<<<1, 1024, 0, s>>>(E, T, gws.totals, gws.totals + kMaxE, offsets, distinct,
                                        counts_out, tile_base, tile_m > 0 ? tile_m : 1,
                                        tile_group);
   group_scatter_kernel<<<n_chunks, 64, 0, s>>>(idx, slot_of_pair, table, T, k, E, select_hits,
-                                               gws.chunk_counts, gws.totals + kMaxE, perm, pos,
+                                               n_slots, gws.chunk_counts, gws.totals + kMaxE, perm, pos,
                                                group_slot);
   return hipGetLastError();
 }

@@ -92,10 +92,12 @@ struct FfnArgs {
   int32_t* o_miss_pair;         // [T*k] or null
   int32_t* o_n_miss;            // [2]
   // miss mode only: the pairs' experts; `table` is then the host tier's
-  // slot of each expert (entries outside [0, n_slots) count as absent), and
-  // a miss of k-slot i runs only if i < max_rank
+  // slot of each expert, and a miss of k-slot i runs only if i < max_rank
   const int32_t* idx;           // [T][k]
-  int max_rank, n_slots;
+  int max_rank;
+  // slots of the pool read here (the host tier's in the miss mode): a slot
+  // outside [0, n_slots), whether given or looked up, counts as a miss
+  int n_slots;
 };
 
 // Routing inside the kernel: experts are taken in chunks of 512, one
@@ -188,7 +190,10 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
   const int d = a.d;
   const int n = a.T * a.k;
   int sp = -1;   // slot of pair `lane`
-  if (MODE == kPairs) sp = lane < n ? a.slot[lane] : -1;
+  if (MODE == kPairs) {
+    const int gs = a.slot[min(lane, n - 1)];
+    sp = lane < n && gs < a.n_slots ? gs : -1;
+  }
   if (MODE == kMiss) {
     const int p = min(lane, n - 1);
     const int gpu_slot = a.slot[p];
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
       uint64_t* out = nchunk == 1 ? s_top + rt * a.k : s_cand + (rt * kRouteChunks + rc) * a.k;
       wave_topk_keys<8>(key, a.k, out, s_scr[wave]);
     }
-    if (tid < a.E) s_table[tid] = tv;
+    if (tid < a.E) s_table[tid] = tv < a.n_slots ? tv : -1;   // out of the pool: a miss
   }
   __syncthreads();
   if (ROUTE && nchunk > 1) {   // uniform: rank the 2k survivors of each token
@@ -498,6 +503,8 @@ __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
   if (MISS) {
     const int hs = host_slot[min(max(idx[t * k + ti], 0), n_experts - 1)];
     sp = sp < 0 && ti < max_rank && hs < n_slots ? hs : -1;
+  } else {
+    sp = sp < n_slots ? sp : -1;   // a slot outside the pool is a miss, as in the ffn kernel
   }
   const float xr = MISS ? y[static_cast<int64_t>(t) * d + r] : x[static_cast<int64_t>(t) * d + r];
   // sp and wv are read across lanes inside branches only some lanes take:
@@ -599,6 +606,7 @@ FfnArgs ffn_args(const moe_layer& L, int T, const int32_t* slot, void* ws) {
   a.slot = slot;
   a.part = static_cast<float*>(ws);
   a.E = L.n_experts;
+  a.n_slots = L.n_slots;
   return a;
 }
 
@@ -620,7 +628,7 @@ hipError_t launch_combine_partials(const moe_layer& L, const float* x, int T,
   const size_t lds = static_cast<size_t>(L.top_k + 1) * KB_ROWS * 4;
   decode_combine_kernel<false><<<grid, KB_WAVES * 64, lds, s>>>(
       x, slot, w, T, L.top_k, L.d_model, L.d_ff / SLICE, L.shared_slot >= 0 ? 1 : 0, part,
-      nullptr, nullptr, 1, 0, 0, y, xnext, addend);
+      nullptr, nullptr, 1, 0, L.n_slots, y, xnext, addend);
   return hipGetLastError();
 }
 

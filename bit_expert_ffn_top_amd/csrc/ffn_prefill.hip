@@ -710,13 +710,12 @@ hipError_t launch_prefill(const moe_layer& L, const uint16_t* x_bf16, int T, con
                           const int32_t* slot, float* out_pairs, int32_t* pair_pos,
                           int32_t* expert_offsets, float* out_shared, void* ws, hipStream_t s) {
   const PrefillWs w = prefill_ws(ws, L.d_model, L.d_ff, T, L.top_k, L.n_experts);
-  // a shared group with zero rows when no shared output is wanted
-  const int T_shared = out_shared ? T : 0;
-  hipError_t e = launch_group_pairs(idx, slot, nullptr, T, L.top_k, L.n_experts, true, w.gws,
+  // the pairs whose slot lies in the pool; the others are misses
+  hipError_t e = launch_group_pairs(idx, slot, nullptr, T, L.top_k, L.n_experts, true,
+                                    L.n_slots, w.gws,
                                     expert_offsets, w.perm, pair_pos, nullptr, nullptr,
                                     w.tile_base, PM, w.tile_group, w.group_slot, s);
   if (e != hipSuccess) return e;
-  (void)T_shared;
   switch (L.fmt) {
     case MOE_FMT_Q2S:
       return launch_prefill_fmt<MOE_FMT_Q2S>(L, x_bf16, T, slot, out_pairs, expert_offsets,

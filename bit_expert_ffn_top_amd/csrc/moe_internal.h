@@ -24,7 +24,8 @@ hipError_t launch_lookup_small(const int32_t* idx, int T, int k, const int32_t* 
                                int32_t* n_miss, hipStream_t s);
 
 // Grouping of (t, i) pairs by expert id, stable in (t, i) order, for the pairs
-// whose slot satisfies the predicate (hits: slot >= 0, misses: slot < 0).
+// whose slot satisfies the predicate (hits: 0 <= slot < n_slots, misses:
+// slot < 0; n_slots is read only for hits).
 // Outputs: offsets[E+1] (may be null), perm (pair ids in group order),
 // pos[T*k] (position of each pair, -1 if not selected; may be null),
 // distinct[E] (ascending ids of non-empty groups; may be null),
@@ -43,7 +44,7 @@ size_t group_workspace_bytes(int T, int E);
 GroupWorkspace group_workspace(void* ws, int T, int E);
 hipError_t launch_group_pairs(const int32_t* idx, const int32_t* slot_of_pair,
                               const int32_t* table, int T, int k, int E, bool select_hits,
-                              GroupWorkspace gws, int32_t* offsets, int32_t* perm,
+                              int n_slots, GroupWorkspace gws, int32_t* offsets, int32_t* perm,
                               int32_t* pos, int32_t* distinct, int32_t* counts_out,
                               int32_t* tile_base, int tile_m, int32_t* tile_group,
                               int32_t* group_slot, hipStream_t s);

@@ -163,7 +163,8 @@ size_t moe_decode_workspace_bytes(const moe_layer* L, int T);
  *               + FFN_{shared_slot}(x[t])          (if shared_slot >= 0)
  * with FFN(x) = D (silu(G_gate x) * (G_up x)), silu(z) = z / (1 + e^-z),
  * summed for each token in k-slot order, shared expert last.  Misses
- * (slot < 0) are skipped: the caller adds them (moe_combine can).
+ * (slot < 0) are skipped: the caller adds them (moe_combine can).  A slot
+ * at or past L->n_slots is a miss as well: no byte outside the pool is read.
  * Each distinct resident expert chosen by any of the T tokens is streamed
  * from memory once for all tokens that chose it.  x, y fp32 [T][d_model]
  * (y may not alias x); idx, slot int32 [T][k]; w fp32 [T][k].
@@ -180,7 +181,9 @@ int moe_expert_ffn_decode(const moe_layer* L, const float* x, int T,
  * output ("Strata" page, "Strataとは" and "投機的デコード": the router picks
  * 10 of 512 experts plus the shared one, the cached ones run on the GPU,
  * the misses are handed on).  logits fp32 [T][n_experts]; slot_of_expert
- * int32 [n_experts]; outputs as those three calls define them: idx, slot
+ * int32 [n_experts], an entry outside [0, L->n_slots) meaning not resident
+ * (such an expert's slot output is -1 and it is in the miss list); outputs
+ * as those three calls define them: idx, slot
  * int32 [T][k], w fp32 [T][k], miss_expert int32 [T*k], miss_pair int32
  * [T*k] (may be NULL), n_miss int32 [2], y fp32 [T][d_model] (may not alias
  * x).  Limits: as moe_expert_ffn_decode (T * top_k <= 64); n_experts <= 1024.
@@ -285,7 +288,9 @@ int moe_decode_stack(int d_model, int d_ff, int n_experts, int top_k, int T, int
  *   x          fp32 [T][d_model], the layer input.
  *   idx, w     int32 / fp32 [T][k], the routing of this step (rank order;
  *              ids distinct within a token, as moe_route_topk gives them).
- *   slot       int32 [T][k], the GPU slots of this step (-1 = miss).
+ *   slot       int32 [T][k], the GPU slots of this step as the GPU part
+ *              wrote them (-1 = miss; any value >= 0 counts as computed
+ *              there).
  *   host_slot_of_expert  int32 [n_experts], slot of each expert in H; a
  *              value outside [0, H->n_slots) means not there, and such a
  *              miss adds nothing.
@@ -426,9 +431,10 @@ size_t moe_prefill_workspace_bytes(const moe_layer* L, int T);
 
 /* Prefill chunk ("Strata" page, "GPU・CPU・RAM・SSDの分担": up to 8,192
  * tokens at a time).  x_bf16 [T][d_model] bfloat16 bits.  Pairs (t,i) with
- * slot[t*k+i] >= 0 are grouped by expert id (groups ascending, inside a
- * group by t then i); expert_offsets int32 [E+1] receives the group bounds,
- * pair_pos int32 [T*k] each pair's row in out_pairs (-1 for a miss).  For
+ * 0 <= slot[t*k+i] < L->n_slots are grouped by expert id (groups ascending,
+ * inside a group by t then i); expert_offsets int32 [E+1] receives the group
+ * bounds, pair_pos int32 [T*k] each pair's row in out_pairs (-1 for a miss,
+ * which is any other slot value).  For
  * every pair the expert FFN runs with bf16 inputs and weights (weights
  * dequantized to bf16 round-to-nearest-even), fp32 accumulation, and
  * h = silu(g) * u rounded to bf16 before the down product:

@@ -173,3 +173,69 @@ def test_decode_layer_workspace_reuse():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out["y"], eager)
+
+
+def test_slots_outside_the_pool_are_misses():
+    """Slot values at or past the pool's n_slots count as misses everywhere a
+    pool is read: moe_decode_layer writes -1 for them and lists them as
+    misses, moe_expert_ffn_decode skips them, moe_expert_ffn_prefill gives
+    them pair_pos -1.  Every output equals, bit for bit, the same call with
+    those entries set to -1."""
+    import bit_expert_ffn_top_amd as bf
+    dev = need_gpu()
+    shape = synth.LayerShape(200, 8, 512, 256, True)
+    L = GpuLayer(0, 13, shape, synth.FMT_Q2SM, dev)
+    n_slots = L.pool.shape[0]
+    k, T = shape.top_k, 4
+    x = synth.make_x(0, 13, T, shape.d_model).to(dev)
+    logits = synth.make_logits(0, 13, T, shape.n_experts, 1.0).to(dev)
+    oidx, _ = oracle.route_topk(logits.cpu().numpy(), k)
+    chosen = sorted(set(oidx.reshape(-1).tolist()))
+    bad = chosen[::3]
+    table_bad = L.table.copy()
+    table_neg = L.table.copy()
+    for j, e in enumerate(bad):
+        table_bad[e] = (n_slots, n_slots + 7, 1 << 30, 2 ** 31 - 1)[j % 4]
+        table_neg[e] = -1
+    tb = torch.tensor(table_bad, dtype=torch.int32, device=dev)
+    tn = torch.tensor(table_neg, dtype=torch.int32, device=dev)
+
+    got = [t.cpu() for t in bf.decode_layer(L.layer_obj, x, logits, tb)]
+    ref = [t.cpu() for t in bf.decode_layer(L.layer_obj, x, logits, tn)]
+    y, idx, w, slot, me, mp, nm = got
+    ry, ridx, rw, rslot, rme, rmp, rnm = ref
+    assert torch.equal(idx, ridx) and torch.equal(w, rw)
+    assert torch.equal(slot, rslot)
+    assert all(int(s) == -1 for e, s in zip(idx.reshape(-1).tolist(), slot.reshape(-1).tolist())
+               if e in bad)
+    assert torch.equal(nm[:2], rnm[:2])
+    assert set(bad) <= set(me[:int(nm[0])].tolist())
+    assert torch.equal(me[:int(nm[0])], rme[:int(rnm[0])])
+    assert torch.equal(mp[:int(nm[1])], rmp[:int(rnm[1])])
+    assert torch.equal(y, ry)
+
+    # given slots: the out-of-range values straight from the table
+    idx_d = idx.to(dev)
+    w_d = w.to(dev)
+    slot_bad = tb[idx_d.long()]
+    slot_neg = tn[idx_d.long()]
+    yb = bf.expert_ffn_decode(L.layer_obj, x, idx_d, slot_bad, w_d)
+    yn = bf.expert_ffn_decode(L.layer_obj, x, idx_d, slot_neg, w_d)
+    torch.cuda.synchronize()
+    assert torch.equal(yb.cpu(), yn.cpu())
+    assert torch.equal(yb.cpu(), y)
+
+    # prefill: the same pairs are misses
+    xb = x.to(torch.bfloat16)
+    pb = bf.expert_ffn_prefill(L.layer_obj, xb, idx_d, slot_bad)
+    pn = bf.expert_ffn_prefill(L.layer_obj, xb, idx_d, slot_neg)
+    torch.cuda.synchronize()
+    out_b, pos_b, off_b = (t.cpu() for t in pb[:3])
+    out_n, pos_n, off_n = (t.cpu() for t in pn[:3])
+    assert torch.equal(pos_b, pos_n) and torch.equal(off_b, off_n)
+    bad_pairs = np.isin(idx.numpy(), bad)
+    assert (pos_b.numpy()[bad_pairs] == -1).all()
+    n_rows = int(off_n[-1])
+    assert torch.equal(out_b[:n_rows], out_n[:n_rows])
+    if pb[3] is not None:
+        assert torch.equal(pb[3].cpu(), pn[3].cpu())
