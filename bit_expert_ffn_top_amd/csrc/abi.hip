@@ -88,6 +88,23 @@ bool device_address(const void* p, const void** out) {
   return true;
 }
 
+// The checks of moe_decode_layer's arguments other than the workspace.
+int check_decode_layer(const moe_layer* L, const float* x, int T, const float* logits,
+                       const int32_t* slot_of_expert, const int32_t* idx, const float* w,
+                       const int32_t* slot, const int32_t* miss_expert, const int32_t* miss_pair,
+                       const int32_t* n_miss, const float* y) {
+  const int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (T < 1 || T > MOE_MAX_DECODE_T || T * L->top_k > MOE_MAX_DECODE_PAIRS) return MOE_EINVAL;
+  if (!x || !logits || !slot_of_expert || !idx || !w || !slot || !miss_expert || !n_miss || !y)
+    return MOE_EINVAL;
+  if (static_cast<const void*>(x) == static_cast<const void*>(y)) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(logits) || !aligned16(slot_of_expert) || !aligned16(idx) ||
+      !aligned16(w) || !aligned16(slot) || !aligned16(miss_expert) || !aligned16(n_miss) ||
+      (miss_pair && !aligned16(miss_pair)) || !aligned16(y))
+    return MOE_EALIGN;
+  return MOE_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -180,17 +197,10 @@ int moe_decode_layer(const moe_layer* L, const float* x, int T, const float* log
                      const int32_t* slot_of_expert, int32_t* idx, float* w, int32_t* slot,
                      int32_t* miss_expert, int32_t* miss_pair, int32_t* n_miss, float* y,
                      void* ws, size_t ws_bytes, hipStream_t stream) {
-  const int st = check_layer(L);
+  const int st = check_decode_layer(L, x, T, logits, slot_of_expert, idx, w, slot, miss_expert,
+                                    miss_pair, n_miss, y);
   if (st != MOE_OK) return st;
-  if (T < 1 || T > MOE_MAX_DECODE_T || T * L->top_k > MOE_MAX_DECODE_PAIRS) return MOE_EINVAL;
-  if (!x || !logits || !slot_of_expert || !idx || !w || !slot || !miss_expert || !n_miss || !y ||
-      !ws)
-    return MOE_EINVAL;
-  if (static_cast<const void*>(x) == static_cast<const void*>(y)) return MOE_EINVAL;
-  if (!aligned16(x) || !aligned16(logits) || !aligned16(slot_of_expert) || !aligned16(idx) ||
-      !aligned16(w) || !aligned16(slot) || !aligned16(miss_expert) || !aligned16(n_miss) ||
-      (miss_pair && !aligned16(miss_pair)) || !aligned16(y))
-    return MOE_EALIGN;
+  if (!ws) return MOE_EINVAL;
   if (!aligned256(ws)) return MOE_EALIGN;
   if (ws_bytes < bitffn::decode_workspace_bytes(L->d_model, L->d_ff, T, L->top_k))
     return MOE_ENOSPC;
@@ -202,9 +212,10 @@ int moe_decode_layer_noalloc(const moe_layer* L, const float* x, int T, const fl
                              const int32_t* slot_of_expert, int32_t* idx, float* w,
                              int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
                              int32_t* n_miss, float* y, hipStream_t stream) {
-  const int st = check_layer(L);
+  // every argument is checked before the first HIP call (the address lookup)
+  const int st = check_decode_layer(L, x, T, logits, slot_of_expert, idx, w, slot, miss_expert,
+                                    miss_pair, n_miss, y);
   if (st != MOE_OK) return st;
-  if (T < 1 || T > MOE_MAX_DECODE_T || T * L->top_k > MOE_MAX_DECODE_PAIRS) return MOE_EINVAL;
   if (bitffn::decode_workspace_bytes(L->d_model, L->d_ff, T, L->top_k) > kNoAllocScratchBytes)
     return MOE_ENOSPC;
   hipError_t e = hipSuccess;
@@ -234,7 +245,6 @@ int moe_decode_stack(int d_model, int d_ff, int n_experts, int top_k, int T, int
   if (n_layers < 1) return MOE_EINVAL;
   if (!layers || !x || !ws) return MOE_EINVAL;
   if (!aligned16(x) || !aligned256(ws)) return MOE_EALIGN;
-  if (ws_bytes < bitffn::decode_stack_workspace_bytes(d_model, d_ff, T, top_k)) return MOE_ENOSPC;
   for (int l = 0; l < n_layers; ++l) {
     const moe_stack_layer& S = layers[l];
     if (!valid_fmt(S.fmt)) return MOE_EFORMAT;
@@ -254,6 +264,7 @@ int moe_decode_stack(int d_model, int d_ff, int n_experts, int top_k, int T, int
       if (q && !aligned16(q)) return MOE_EALIGN;
     if (S.y && static_cast<const void*>(S.y) == static_cast<const void*>(x)) return MOE_EINVAL;
   }
+  if (ws_bytes < bitffn::decode_stack_workspace_bytes(d_model, d_ff, T, top_k)) return MOE_ENOSPC;
   const bitffn::StackDims D{d_model, d_ff, n_experts, top_k, T};
   return hip_status(bitffn::launch_decode_stack(D, n_layers, layers, x, ws, stream));
 }
@@ -362,14 +373,14 @@ int moe_stage_layer(const moe_layer* C, const int32_t* slot_of_expert, const moe
   if (!slot_of_expert || !host_slot_of_expert || !staging) return MOE_EINVAL;
   if (!aligned256(staging)) return MOE_EALIGN;
   const int E = C->n_experts;
-  if (staging_bytes < static_cast<size_t>(E + 1) * static_cast<size_t>(C->slot_bytes))
-    return MOE_ENOSPC;
   for (int e = 0; e < E; ++e) {   // every expert needs a source
     const int cs = slot_of_expert[e], hs = host_slot_of_expert[e];
     const bool in_cache = cs >= 0 && cs < C->n_slots && cs != C->shared_slot;
     const bool in_host = hs >= 0 && hs < H->n_slots;
     if (!in_cache && (cs >= 0 || !in_host)) return MOE_EINVAL;
   }
+  if (staging_bytes < static_cast<size_t>(E + 1) * static_cast<size_t>(C->slot_bytes))
+    return MOE_ENOSPC;
   const void* host_dev = nullptr;
   if (!device_address(H->pool, &host_dev)) return MOE_EINVAL;
   return hip_status(bitffn::launch_stage_layer(*C, slot_of_expert, H->pool, host_slot_of_expert,
