@@ -80,6 +80,7 @@ struct FfnArgs {
   int d, f, T, k, shared_slot;
   const int32_t* slot;
   float* part;  // [T][k+1][f/32][d]: term i of token t, the shared expert at i = k
+  uint32_t part_bytes;
   // fused routing only: inputs, and the routing outputs written by
   // workgroup (0, 0)
   const float* logits;          // [T][E]
@@ -301,6 +302,11 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
   __shared__ float red[KA_WAVES][64];
   __shared__ __attribute__((aligned(16))) float hsh[SLICE];
   __shared__ float hsum[2];
+  // the pair slots, kept in LDS for the jobs: every wavefront holds the same
+  // values and writes them to the same place, then reads back its own lane,
+  // so no barrier is needed, and no register holds them across a job loop
+  __shared__ int32_t s_sp[64];
+  s_sp[lane] = sp;
 
   // one job; LOOP: the workgroup takes jobs blockIdx.x, + gridDim.x, ...,
   // else exactly one (grid = jobs), with no loop around the job's code
@@ -308,15 +314,15 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
   const bool shared_job = job < n_shared;
   const int u = shared_job ? n : (job - n_shared) / nslices;
   const int js = shared_job ? job : (job - n_shared) % nslices;
-  int s;
-  uint32_t mask;
-  uint64_t same;
-  if (!union_member(sp, a.T, a.k, a.shared_slot, u, s, mask, same)) return;
-  const uint8_t* __restrict__ base = a.pool + static_cast<int64_t>(s) * a.slot_bytes;
   // the thread index, opaque here so that the per-thread offsets below are
   // formed in each job instead of being kept (and spilled) across jobs
   int tj = tid;
   opaque(tj);
+  int s;
+  uint32_t mask;
+  uint64_t same;
+  if (!union_member(s_sp[tj & 63], a.T, a.k, a.shared_slot, u, s, mask, same)) return;
+  const uint8_t* __restrict__ base = a.pool + static_cast<int64_t>(s) * a.slot_bytes;
   const uint32_t R = 2u * static_cast<uint32_t>(a.f);                   // G rows
   const uint32_t grow = 2u * SLICE * js + static_cast<uint32_t>(tj & 63);   // this lane's G row
   const int nu = d / 64;
@@ -393,8 +399,11 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
     // every row of the thread before the next half is read.
     const float HX = hsum[0], HK = hsum[1];
     const int term = member_term(same, t, a.k, u == n);
-    float* __restrict__ out =
-        a.part + ((static_cast<int64_t>(t) * (a.k + 1) + term) * nslices + js) * d;
+    // this row of partials, addressed through a buffer resource over the
+    // partials (32-bit offsets, so the stores need one VGPR each)
+    const uint32_t obase = static_cast<uint32_t>(((t * (a.k + 1) + term) * nslices + js) * d) * 4u;
+    const __amdgpu_buffer_rsrc_t prs =
+        __builtin_amdgcn_make_buffer_rsrc(a.part, 0, static_cast<int>(a.part_bytes), 0x00020000);
     float a0[MAX_DROWS], a1[MAX_DROWS];
 #pragma unroll
     for (int i = 0; i < MAX_DROWS; ++i) a0[i] = a1[i] = 0.0f;
@@ -428,7 +437,13 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
       if (i < ndr) {
         const float v = block_finish<FMT>(0.0f, a0[i] + a1[i], HK, HX, ds[i],
                                           FMT == MOE_FMT_Q2SM ? dm[i] : 0u);
-        out[tid + KA_THREADS * i] = v;
+        // written through to memory (cache policy SC1, device scope: bit 4
+        // of the policy operand on gfx950): the combine reads the partials
+        // on other XCDs, and lines left dirty in this XCD's L2 would have to
+        // be written back when the kernel ends, before the combine starts
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __builtin_bit_cast(uint32_t, v), prs,
+            static_cast<int>(obase + 4u * static_cast<uint32_t>(tid + KA_THREADS * i)), 0, 16);
       }
     }
     __syncthreads();
@@ -605,6 +620,7 @@ FfnArgs ffn_args(const moe_layer& L, int T, const int32_t* slot, void* ws) {
   a.shared_slot = L.shared_slot;
   a.slot = slot;
   a.part = static_cast<float*>(ws);
+  a.part_bytes = static_cast<uint32_t>(part_bytes(L.d_model, L.d_ff, T, L.top_k));
   a.E = L.n_experts;
   a.n_slots = L.n_slots;
   return a;
