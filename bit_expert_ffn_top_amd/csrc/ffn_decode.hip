@@ -239,7 +239,7 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
   __shared__ float2 bsum[MOE_MAX_DECODE_T][2048 / 32];   // per block of x: (sum, offset constant)
   __shared__ uint64_t s_cand[MOE_MAX_DECODE_T * kRouteChunks * MOE_MAX_TOPK];
   __shared__ uint64_t s_top[MOE_MAX_DECODE_PAIRS];
-  __shared__ uint64_t s_scr[MOE_MAX_DECODE_T * kRouteChunks][64];
+  __shared__ uint64_t s_scr[MOE_MAX_DECODE_T * kRouteChunks][128];
   __shared__ int32_t s_table[MOE_MAX_EXPERTS];
 
   // x into LDS (the gate/up products read it from there), and per-block sums

@@ -178,34 +178,47 @@ __device__ __forceinline__ void wave_topk_rounds(uint64_t (&key)[NJ], int k, uin
 // >= E, below every real key).  A bound first: tau0, the k-th largest of the
 // 64 lane maxima (by value) with its low 16 bits cleared, has at least k keys
 // whose value is >= tau0, and the k-th largest key is at least the k-th
-// largest lane maximum, so the top k are among them.  Those candidates (usually a little over k) are
-// gathered one per lane and ranked among themselves by (value desc, id asc);
-// the first k, in rank order, go to top[0..k).  When more than 64 keys pass
-// the bound (many equal values), k rounds of the largest remaining key are
-// taken instead.  scratch: 64 uint64 of LDS for this wavefront.  Same keys,
-// same order as ranking every key.
+// largest lane maximum, so the top k are among them.  Those candidates
+// (usually a little over k) are gathered into scratch in (j, lane) order and
+// ranked among themselves by (value desc, id asc); the first k, in rank
+// order, go to top[0..k).  Up to 16 candidates, every lane reads all 16
+// slots at once and counts the larger keys (no serial chain of lane reads);
+// up to 64, one lane read per candidate; past 64 (many equal values), k
+// rounds of the largest remaining key.  scratch: 128 uint64 of LDS for this
+// wavefront (slots 64 + lane take the writes of lanes without a candidate,
+// so the gather needs no branch).  Same keys, same order as ranking every key.
 template <int NJ>
 __device__ __forceinline__ void wave_topk_keys(uint64_t (&key)[NJ], int k, uint64_t* top,
                                                uint64_t* scratch) {
+  constexpr int kDirect = 16;
   const int lane = threadIdx.x & 63;
-  uint64_t m = key[0];
+  uint32_t m = static_cast<uint32_t>(key[0] >> 32);   // lane maximum of the values
 #pragma unroll
-  for (int j = 1; j < NJ; ++j) m = key[j] > m ? key[j] : m;
-  const uint32_t tau0 = wave_kth_largest<16>(static_cast<uint32_t>(m >> 32), k);
+  for (int j = 1; j < NJ; ++j) m = max(m, static_cast<uint32_t>(key[j] >> 32));
+  const uint32_t tau0 = wave_kth_largest<16>(m, k);
   const uint64_t below = (1ull << lane) - 1ull;
+  // gather and count in one pass; candidates past the 64th are not stored
   int n_c = 0;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) n_c += __popcll(__ballot(static_cast<uint32_t>(key[j] >> 32) >= tau0));
-  if (n_c <= 64) {
-    int pos = 0;
+  for (int j = 0; j < NJ; ++j) {
+    const bool c = static_cast<uint32_t>(key[j] >> 32) >= tau0;
+    const uint64_t sel = __ballot(c);
+    const int at = n_c + __popcll(sel & below);
+    scratch[c && at < 64 ? at : 64 + lane] = key[j];
+    n_c += __popcll(sel);
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (n_c <= kDirect) {
+    const uint64_t mine = lane < n_c ? scratch[lane] : 0ull;
+    uint64_t other[kDirect];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const bool c = static_cast<uint32_t>(key[j] >> 32) >= tau0;
-      const uint64_t sel = __ballot(c);
-      if (c) scratch[pos + __popcll(sel & below)] = key[j];
-      pos += __popcll(sel);
-    }
+    for (int q = 0; q < kDirect; ++q) other[q] = scratch[q];   // same address in every lane
+    int rank = 0;
+#pragma unroll
+    for (int q = 0; q < kDirect; ++q) rank += q < n_c && other[q] > mine ? 1 : 0;
     __builtin_amdgcn_wave_barrier();
+    if (lane < n_c && rank < k) top[rank] = mine;
+  } else if (n_c <= 64) {
     const uint64_t mine = lane < n_c ? scratch[lane] : 0ull;
     int rank = 0;
     for (int q = 0; q < n_c; ++q) rank += readlane_u64(mine, q) > mine ? 1 : 0;
