@@ -144,32 +144,6 @@ __device__ __forceinline__ BlockRaw load_block(const uint8_t* base, int64_t oc, 
   return r;
 }
 
-// 16 codes of one 32-bit word (2-bit formats) as weights m + s*q: each code is
-// read as an fp16 value c_j + q in place (the extraction of the decode path,
-// c_j = q2_offset(j)), two codes per register; one packed fp16 subtraction
-// leaves q exactly, and w = fma(s, q, m) is the correctly rounded value the
-// plain formula gives (about 2.6 vector instructions per weight instead of 3.5).
-__device__ __forceinline__ void weights16_q2(uint32_t w, float s, float m, float (&out)[16]) {
-  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-  const uint32_t b = w >> 6, c = w << 6;
-  const uint32_t rr[8] = {
-      and_or(c, 0x00C000C0u, 0x4C004C00u),   // 16+q0  | 16+q8
-      and_or(c, 0x03000300u, 0x44004400u),   // 4+q1   | 4+q9
-      and_or(w, 0x00300030u, 0x54005400u),   // 64+q2  | 64+q10
-      and_or(w, 0x00C000C0u, 0x4C004C00u),   // 16+q3  | 16+q11
-      and_or(w, 0x03000300u, 0x44004400u),   // 4+q4   | 4+q12
-      and_or(b, 0x00300030u, 0x54005400u),   // 64+q5  | 64+q13
-      and_or(b, 0x00C000C0u, 0x4C004C00u),   // 16+q6  | 16+q14
-      and_or(b, 0x03000300u, 0x44004400u)};  // 4+q7   | 4+q15
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const _Float16 cj = static_cast<_Float16>(q2_offset(j));
-    const half2_t q = __builtin_bit_cast(half2_t, rr[j]) - half2_t{cj, cj};
-    out[j] = fmaf(s, static_cast<float>(q.x), m);
-    out[j + 8] = fmaf(s, static_cast<float>(q.y), m);
-  }
-}
-
 // The block's 32 weights (dequant_one, rounded to bf16 nearest even) as four
 // 16-byte pieces piece0 .. piece0+3 of a 128-byte LDS row, piece c stored at
 // position c ^ key.
@@ -182,12 +156,29 @@ __device__ __forceinline__ void store_block_bf16(const BlockRaw& r, __bf16* row,
   // Q2S: s*(q - 1.5) = s*q + (-1.5 s), -1.5 s exact
   const float m0 = FMT == MOE_FMT_Q2SM ? m : -1.5f * s;
   if (FMT != MOE_FMT_Q3G) {
+    // A 2-bit code takes one of four values, w_q = fma(s, q, m0) rounded to
+    // bf16 once: they form an 8-byte table (w_0 w_1 | w_2 w_3), and each pair
+    // of weights is picked from it by one byte permute whose selector holds
+    // bytes 2q, 2q+1 of each code (about 2 vector instructions per weight
+    // instead of 2.6; the same bits as dequantizing every weight).
+    const uint32_t t01 = pack_bf16x2(fmaf(s, 0.0f, m0), fmaf(s, 1.0f, m0));
+    const uint32_t t23 = pack_bf16x2(fmaf(s, 2.0f, m0), fmaf(s, 3.0f, m0));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      float wv[16];
-      weights16_q2(h == 0 ? r.codes.x : r.codes.y, s, m0, wv);
+      const uint32_t w = h == 0 ? r.codes.x : r.codes.y;
+      // 2q of codes 4i, 4i+1, 4i+2, 4i+3 in byte i of d0, d1, d2, d3
+      const uint32_t d0 = (w << 1) & 0x06060606u, d1 = (w >> 1) & 0x06060606u;
+      const uint32_t d2 = (w >> 3) & 0x06060606u, d3 = (w >> 5) & 0x06060606u;
 #pragma unroll
-      for (int j = 0; j < 16; j += 2) packed[8 * h + j / 2] = pack_bf16x2(wv[j], wv[j + 1]);
+      for (int j = 0; j < 8; ++j) {   // weights 2j, 2j+1 of this word
+        const uint32_t lo = (j & 1) ? d2 : d0, hi = (j & 1) ? d3 : d1;
+        const uint32_t b = static_cast<uint32_t>(j >> 1);
+        // (2q_a, 2q_a, 2q_b, 2q_b), then + 1 in the high byte of each weight
+        const uint32_t sel =
+            __builtin_amdgcn_perm(hi, lo, b | (b << 8) | ((4u + b) << 16) | ((4u + b) << 24)) |
+            0x01000100u;
+        packed[8 * h + j] = __builtin_amdgcn_perm(t23, t01, sel);
+      }
     }
     u32x4* d4 = reinterpret_cast<u32x4*>(row);
 #pragma unroll
