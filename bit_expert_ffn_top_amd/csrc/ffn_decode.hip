@@ -10,13 +10,16 @@
 //    h indices).  Gate/up: the slice owns G rows 64js..64js+63 (gate and up
 //    rows of h indices 32js..32js+31); lane l streams row 64js+l, so every
 //    load of a wavefront reads one 1 KiB unit of 64 consecutive rows, and the
-//    activation x is the same for all lanes (scalar operands).  The 16
-//    wavefronts split the d_model columns in interleaved 64-column units;
-//    their row sums meet in LDS in a fixed order, and h = silu(g) * u is
-//    formed for the 32 h indices.
+//    activation x is the same for all lanes (read from LDS, one address per
+//    wavefront).  The 16 wavefronts split the d_model columns in interleaved
+//    64-column units; their row sums meet in LDS in a fixed order, and
+//    h = silu(g) * u is formed for the 32 h indices.
 //    Down, split over d_ff: the same workgroup multiplies its 32 h values into
-//    block column js of D (all d_model rows) and stores that partial product.
-//    Weight bytes of both parts are loaded before any arithmetic.
+//    block column js of D (all d_model rows) and stores that partial product,
+//    written through the L2 to memory.
+//    Weight bytes of both parts are loaded before any arithmetic.  When there
+//    are more jobs than two per CU (T >= 3 at top-10), each routing workgroup
+//    takes its pair jobs in turn after routing once.
 // 2. combine kernel: y[t] = x[t] + sum_i w[t,i] * (sum over slices of the
 //    partials of member u(t,i)) + (same for the shared member), slices summed
 //    in a fixed tree, terms in k-slot order, shared last.
