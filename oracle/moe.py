@@ -136,6 +136,30 @@ def unpack_expert(slot, fmt, d_model, d_ff):
 
 
 # ---------------------------------------------------------------------------
+# router projection (adjacent to the path)
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits):
+    """Value of each bfloat16 bit pattern (uint16): the upper half of the
+    IEEE single with the same sign, exponent and top 7 mantissa bits."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def router_logits(x, w_bits):
+    """Router projection ([P2] "なぜVRAM 12GBで足りるのか" and [P4]
+    "GPU・CPU・RAM・SSDの分担": the router is part of the common part that
+    stays on the GPU; it turns a token's hidden state into one logit per
+    routed expert).  The pages give no precision; the reading here: router
+    weights stored as bfloat16, [E][d] row-major (w_bits, uint16), the hidden
+    state and the logits in fp32, the sums exact (float64 here).
+    x [T][d] -> logits [T][E] = x . W^T."""
+    x = np.asarray(x, dtype=np.float64)
+    W = bf16_bits_to_f64(w_bits)
+    return x @ W.T
+
+
+# ---------------------------------------------------------------------------
 # router top-k
 # ---------------------------------------------------------------------------
 
