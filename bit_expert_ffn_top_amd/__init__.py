@@ -10,5 +10,5 @@ from ._binding import (  # noqa: F401
     decode_layer, decode_layer_noalloc, decode_misses, decode_stack, decode_stack_workspace_bytes,
     decode_workspace_bytes, expert_ffn_decode, new_stack_workspace,
     expert_ffn_prefill, lib, lib_path, lookup_workspace_bytes, prefill_workspace_bytes,
-    route_topk, slot_bytes, stage_layer,
+    route_topk, router_logits, slot_bytes, stage_layer,
 )

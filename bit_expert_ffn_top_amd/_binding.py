@@ -56,6 +56,7 @@ SIGNATURES = {
     "moe_status_str": (ctypes.c_char_p, [_c_int]),
     "moe_last_hip_error": (_c_int, []),
     "moe_slot_bytes": (_c_i64, [_c_int, _c_int, _c_int]),
+    "moe_router_logits": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _vp, _vp]),
     "moe_route_topk": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp, _vp]),
     "moe_lookup_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int]),
     "moe_cache_lookup": (_c_int, [_vp, _c_int, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _vp,
@@ -183,6 +184,20 @@ def slot_bytes(fmt: int, d_model: int, d_ff: int) -> int:
     v = lib().moe_slot_bytes(fmt, d_model, d_ff)
     _check(int(v) if v < 0 else 0, "moe_slot_bytes")
     return int(v)
+
+
+def router_logits(x: torch.Tensor, w: torch.Tensor, logits=None, stream=None):
+    """logits [T, E] = x [T, d] (fp32) times the bf16 router weights w [E, d]."""
+    _dev(_shape(x, (None, None), "x"), torch.float32, "x")
+    T, d = x.shape
+    _dev(_shape(w, (None, d), "w"), torch.bfloat16, "w")
+    E = w.shape[0]
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _dev(_shape(logits, (T, E), "logits"), torch.float32, "logits")
+    _check(lib().moe_router_logits(_ptr(x), T, d, _ptr(w), E, _ptr(logits), _stream(stream)),
+           "moe_router_logits")
+    return logits
 
 
 def route_topk(logits: torch.Tensor, k: int, idx=None, w=None, stream=None):

@@ -131,6 +131,19 @@ int64_t moe_slot_bytes(int fmt, int d_model, int d_ff) {
   return bitffn::slot_layout(fmt, d_model, d_ff).total;
 }
 
+int moe_router_logits(const float* x, int T, int d_model, const uint16_t* w, int n_experts,
+                      float* logits, hipStream_t stream) {
+  if (T < 1 || T > MOE_MAX_DECODE_T) return MOE_EINVAL;
+  if (d_model < 64 || d_model > 2048 || d_model % 64 != 0) return MOE_EINVAL;
+  if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return MOE_EINVAL;
+  if (!x || !w || !logits) return MOE_EINVAL;
+  if (static_cast<const void*>(logits) == static_cast<const void*>(x) ||
+      static_cast<const void*>(logits) == static_cast<const void*>(w))
+    return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(logits)) return MOE_EALIGN;
+  return hip_status(bitffn::launch_router_logits(x, T, d_model, w, n_experts, logits, stream));
+}
+
 int moe_route_topk(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                    hipStream_t stream) {
   if (E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E) return MOE_EINVAL;

@@ -11,6 +11,10 @@
 
 namespace bitffn {
 
+// Router projection, T <= MOE_MAX_DECODE_T tokens (router.hip).
+hipError_t launch_router_logits(const float* x, int T, int d, const uint16_t* w, int E,
+                                float* logits, hipStream_t s);
+
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* idx,
                              float* w, hipStream_t s);
 

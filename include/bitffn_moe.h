@@ -123,6 +123,22 @@ int moe_last_hip_error(void);
  * negative value) for an unknown format or unsupported sizes. */
 int64_t moe_slot_bytes(int fmt, int d_model, int d_ff);
 
+/* Router projection (vramglass.com page, "なぜVRAM 12GBで足りるのか", and
+ * "Strata" page, "GPU・CPU・RAM・SSDの分担": the router belongs to the
+ * common part that stays on the GPU; it gives each routed expert a logit
+ * from the token's hidden state).  For a decode or verify step of
+ * 1 <= T <= MOE_MAX_DECODE_T tokens:
+ *   logits[t][e] = sum_j x[t][j] * w[e][j]
+ * x fp32 [T][d_model], w bfloat16 bits [n_experts][d_model] row-major (the
+ * pages give no precision; bf16 router weights are this library's reading),
+ * logits fp32 [T][n_experts] (may not alias x or w); all device memory,
+ * 16-byte aligned.  Products and sums in fp32 in a fixed order (bitwise
+ * reproducible).  Limits: d_model a multiple of 64 in 64..2048,
+ * 1 <= n_experts <= MOE_MAX_EXPERTS.  The logits then feed moe_route_topk,
+ * moe_decode_layer or moe_decode_stack. */
+int moe_router_logits(const float* x, int T, int d_model, const uint16_t* w,
+                      int n_experts, float* logits, hipStream_t stream);
+
 /* Router top-k ("Strata" page, "Strataとは": 10 of 512 per token).
  * logits fp32 [T][E] row-major.  Per token the experts are ranked by
  * (logit descending, expert id ascending); NaN ranks as -inf and -0.0 as

@@ -49,6 +49,7 @@ ALIGN = 256
 
 # tags that separate the seeded streams
 TAG_W, TAG_X, TAG_LOGITS, TAG_SLOTS, TAG_ZIPF, TAG_RESIDENT = 1, 2, 3, 4, 5, 6
+TAG_ROUTER = 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -278,6 +279,14 @@ def make_logits(cfg: int, layer: int, T: int, E: int, sigma: float,
     """Router logits ~ N(0, sigma), fp32 [T, E]."""
     g = torch_gen(seed_of(cfg, layer, -1, TAG_LOGITS, step), device)
     return torch.randn((T, E), generator=g, dtype=torch.float32, device=device) * sigma
+
+
+def make_router_weights(cfg: int, layer: int, E: int, d: int, sigma: float = 0.02,
+                        device="cpu") -> torch.Tensor:
+    """Router projection weights ~ N(0, sigma), bfloat16 [E, d]."""
+    g = torch_gen(seed_of(cfg, layer, -1, TAG_ROUTER), device)
+    w = torch.randn((E, d), generator=g, dtype=torch.float32, device=device) * sigma
+    return w.to(torch.bfloat16)
 
 
 def _zipf_perm(cfg: int, layer: int, E: int) -> np.ndarray:

@@ -77,6 +77,29 @@ void version_and_sizes() {
   EXPECT(moe_lookup_workspace_bytes(-1, 10, 512), 0);
 }
 
+void router() {
+  auto call = [&](int T, int d, int E, float* x, uint16_t* w, float* out) {
+    return moe_router_logits(x, T, d, w, E, out, s0);
+  };
+  float* x = fp<float>();
+  uint16_t* w = fp<uint16_t>(1 << 20);
+  float* out = fp<float>(1 << 24);
+  EXPECT(call(0, 2048, 512, x, w, out), MOE_EINVAL);
+  EXPECT(call(5, 2048, 512, x, w, out), MOE_EINVAL);
+  EXPECT(call(1, 96, 512, x, w, out), MOE_EINVAL);
+  EXPECT(call(1, 4096, 512, x, w, out), MOE_EINVAL);
+  EXPECT(call(1, 1 << 30, 512, x, w, out), MOE_EINVAL);
+  EXPECT(call(1, 2048, 0, x, w, out), MOE_EINVAL);
+  EXPECT(call(1, 2048, 2000, x, w, out), MOE_EINVAL);
+  EXPECT(call(1, 2048, 512, nullptr, w, out), MOE_EINVAL);
+  EXPECT(call(1, 2048, 512, x, nullptr, out), MOE_EINVAL);
+  EXPECT(call(1, 2048, 512, x, w, nullptr), MOE_EINVAL);
+  EXPECT(call(1, 2048, 512, x, w, x), MOE_EINVAL);
+  EXPECT(call(1, 2048, 512, fp<float>(4), w, out), MOE_EALIGN);
+  EXPECT(call(1, 2048, 512, x, fp<uint16_t>((1 << 20) + 8), out), MOE_EALIGN);
+  EXPECT(call(1, 2048, 512, x, w, fp<float>((1 << 24) + 4)), MOE_EALIGN);
+}
+
 void route_and_lookup() {
   EXPECT(moe_route_topk(fp<float>(), 1, 0, 1, fp<int32_t>(), fp<float>(), s0), MOE_EINVAL);
   EXPECT(moe_route_topk(fp<float>(), 1, 2000, 4, fp<int32_t>(), fp<float>(), s0), MOE_EINVAL);
@@ -349,6 +372,7 @@ void stack() {
 
 int main() {
   version_and_sizes();
+  router();
   route_and_lookup();
   decode();
   prefill_and_combine();

@@ -86,6 +86,27 @@ def test_route_topk_host_checks():
     assert lib.moe_route_topk(None, 0, 64, 4, None, None, s) == 0          # T = 0: no-op
 
 
+def test_router_logits_host_checks():
+    lib = _lib()
+    s = ctypes.c_void_p(0)
+    call = lambda T=1, d=2048, E=512, x=_p(), w=_p(1 << 20), out=_p(1 << 24): \
+        lib.moe_router_logits(x, T, d, w, E, out, s)
+    assert call(T=0) == -1
+    assert call(T=5) == -1                                      # decode / verify only
+    assert call(d=96) == -1                                     # not a multiple of 64
+    assert call(d=4096) == -1
+    assert call(E=0) == -1
+    assert call(E=2000) == -1
+    assert call(x=None) == -1
+    assert call(w=None) == -1
+    assert call(out=None) == -1
+    assert call(out=_p()) == -1                                 # logits alias x
+    assert call(out=_p(1 << 20)) == -1                          # logits alias w
+    assert call(x=_p(4)) == -2
+    assert call(w=_p((1 << 20) + 8)) == -2
+    assert call(out=_p((1 << 24) + 4)) == -2
+
+
 def test_lookup_host_checks():
     lib = _lib()
     s = ctypes.c_void_p(0)
