@@ -518,9 +518,55 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
     del pools3, chain3, logits3
     torch.cuda.empty_cache()
 
+    # ---------------- router projection ----------------
+    out["router"] = run_router(torch, bf, synth, dev)
+
     # ---------------- prefill chunk ----------------
     out["prefill"] = run_prefill(torch, np, bf, synth, pools, dev, args)
     return out
+
+
+class RouterChain:
+    """48 router projections (one per layer) of one token step; step g takes
+    the weights of matrices 48g .. 48g+47 (mod the count), so that a replay
+    reads weights no recent replay has left in the caches."""
+
+    def __init__(self, torch, bf, ws, x, out):
+        self.bf, self.ws, self.x, self.out = bf, ws, x, out
+
+    def step(self, g):
+        n = len(self.ws)
+        for l in range(N_LAYERS):
+            self.bf.router_logits(self.x, self.ws[(N_LAYERS * g + l) % n], logits=self.out[l])
+
+
+def run_router(torch, bf, synth, dev):
+    """The router projection at the model's size (E = 512, d_model = 2048, bf16
+    weights: 2 MiB per layer), T = 1 and the verify step's T = 4, timed as 48
+    launches per graph.  160 distinct weight matrices (320 MiB, more than the
+    last-level cache) are cycled through."""
+    shape = synth.config_shape(1)
+    E, d = shape.n_experts, shape.d_model
+    n_w = 160
+    ws = [synth.make_router_weights(1, l, E, d, device=dev) for l in range(n_w)]
+    res = {"workload": "router projection: logits [T, 512] = x [T, 2048] (fp32) times bf16 weights "
+                       "[512, 2048] (2 MiB), 48 layers per step, weights cycled over 320 MiB",
+           "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    for T in (1, 4):
+        x = synth.make_x(1, 0, T, d, device=dev)
+        out = torch.empty((N_LAYERS, T, E), dtype=torch.float32, device=dev)
+        chain = RouterChain(torch, bf, ws, x, out)
+        steps = 60
+        _, ev_ms, graphs = time_graph_steps(torch, chain, steps, 5, 6)
+        del graphs
+        us = ev_ms * 1e3 / (steps * N_LAYERS)
+        nbytes = E * d * 2 + T * d * 4 + T * E * 4
+        res[f"T{T}"] = {"us_per_call": round(us, 3), "achieved": round(nbytes / us / 1e3, 1),
+                        "frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes}
+        log(f"router T={T}: {us:.2f} us per call, {nbytes / us / 1e3:.0f} GB/s")
+    del ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def verify_chain(torch, bf, synth, shape, pools, dev, n_graphs):
