@@ -72,6 +72,8 @@ def parse():
                          "adaptive cache; for profiling); prints their object")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill workload (for profiling); prints its object")
+    ap.add_argument("--router-only", action="store_true",
+                    help="run only the router projection (for profiling); prints its object")
     ap.add_argument("--counters", action="store_true",
                     help="counter pass for rocprofv3 --pmc: two eager decode steps plus one "
                          "device copy of COPY_BYTES for calibration; prints no result line "
@@ -349,6 +351,10 @@ def main():
     if args.cache_only:
         print(json.dumps(run_extras(torch, np, bf, synth, None, dev, args, cache_only=True)),
               flush=True)
+        return
+
+    if args.router_only:
+        print(json.dumps({"router": run_router(torch, bf, synth, dev)}), flush=True)
         return
 
     t_gen = time.perf_counter()
