@@ -7,14 +7,10 @@
 // Distinct experts have distinct keys, so every rank is a count of larger
 // keys, and one unsigned compare decides each pair.
 //
-// Top-k, two levels, all in LDS:
-//   1. groups of 64 experts: each key's rank within its group (64 compares
-//      against the group's keys); keys ranked below k survive, at position
-//      group*k + rank;
-//   2. each survivor's rank among the G*k survivors of its token; a survivor
-//      with rank r < k is the token's r-th choice.
-// The k-th largest key of a token is among the k largest of its own group,
-// so nothing that belongs to the top k is dropped in step 1.
+// Top-k of one token in one wavefront (wave_topk_keys): a lower bound from the
+// lane maxima, the candidates at or above it gathered and ranked among
+// themselves; every rank is a count of larger keys, so any correct selection
+// gives the same keys in the same order.
 #pragma once
 
 #include "moe_common.h"
@@ -52,85 +48,6 @@ __device__ __forceinline__ float route_wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
-}
-
-// LDS scratch of block_topk for T tokens of E experts, top k:
-//   grp  [nwaves * 64]   per-wavefront group keys
-//   cand [T * G * k]     survivors of step 1, G = ceil(E / 64)
-//   top  [T * k]         result keys in rank order
-struct TopkLds {
-  uint64_t* grp;
-  uint64_t* cand;
-  uint64_t* top;
-};
-
-// Top-k keys of T tokens, called by every thread of the workgroup (blockDim.x
-// a multiple of 64).  Wavefront w handles groups w, w + nwaves, ...; MAXIT
-// bounds the groups per wavefront: T * G <= MAXIT * nwaves.
-//
-// topk_load requests the logits of the wavefront's groups (clamped indices:
-// every load is in range and unconditional); topk_select ranks them.  `hook`
-// runs in every thread just before the first barrier (callers use it to
-// store data that must be visible after the selection).  Ends with a
-// barrier; the result is in s.top.
-template <int MAXIT>
-__device__ __forceinline__ void topk_load(const float* __restrict__ logits, int T, int E,
-                                          float (&lg)[MAXIT]) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
-  const int G = (E + 63) >> 6;
-#pragma unroll
-  for (int it = 0; it < MAXIT; ++it) {
-    const int q = min(wave + it * nwaves, T * G - 1);
-    const int t = q / G, e = (q - t * G) * 64 + lane;
-    lg[it] = logits[static_cast<int64_t>(t) * E + min(e, E - 1)];
-  }
-}
-
-template <int MAXIT, typename Hook>
-__device__ __forceinline__ void topk_select(const float (&lg)[MAXIT], int T, int E, int k,
-                                            const TopkLds& s, Hook&& hook) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nwaves = blockDim.x >> 6;
-  const int G = (E + 63) >> 6;
-  uint64_t* grp = s.grp + wave * 64;
-#pragma unroll
-  for (int it = 0; it < MAXIT; ++it) {
-    const int q = wave + it * nwaves;
-    if (q < T * G) {   // uniform
-      const int t = q / G, g = q - t * G, e = g * 64 + lane;
-      const uint64_t key = route_key(lg[it], e, e < E);
-      grp[lane] = key;
-      __builtin_amdgcn_wave_barrier();
-      int rank = 0;
-#pragma unroll 8
-      for (int j = 0; j < 64; ++j) rank += grp[j] > key ? 1 : 0;
-      if (rank < k) s.cand[(t * G + g) * k + rank] = key;
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
-  hook();
-  __syncthreads();
-
-  const int C = G * k;
-  for (int c = tid; c < T * C; c += blockDim.x) {
-    const uint64_t* cand = s.cand + (c / C) * C;
-    const uint64_t key = s.cand[c];
-    int rank = 0;
-    for (int j = 0; j < C; ++j) rank += cand[j] > key ? 1 : 0;
-    if (rank < k) s.top[(c / C) * k + rank] = key;
-  }
-  __syncthreads();
-}
-
-template <int MAXIT>
-__device__ __forceinline__ void block_topk(const float* __restrict__ logits, int T, int E, int k,
-                                           const TopkLds& s) {
-  float lg[MAXIT];
-  topk_load<MAXIT>(logits, T, E, lg);
-  topk_select<MAXIT>(lg, T, E, k, s, [] {});
 }
 
 // A lower bound of the k-th largest of one 32-bit value per lane (k <= 64):

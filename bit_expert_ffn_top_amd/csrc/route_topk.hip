@@ -2,8 +2,9 @@
 // 64j + l (the 64-bit keys of the shared routing building blocks: value desc,
 // index asc, -0 as +0, NaN as -inf; all distinct), and k rounds each take the
 // wavefront's largest remaining key, so choice r is the key of rank r, as the
-// two-level rank selection of the fused decode layer finds it.  The softmax
-// over the k chosen logits is the shared one, so both give identical bits.
+// fused decode layer's selection (bound, candidates, their ranks) finds it.
+// The softmax over the k chosen logits is the shared one, so both give
+// identical bits.
 #include "moe_internal.h"
 #include "route_device.h"
 
