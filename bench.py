@@ -145,14 +145,17 @@ class StackStep:
 
 class DecodeChain:
     """48 layers of decode for T tokens, one moe_decode_layer call per layer
-    (plus moe_decode_misses from a host tier and cache counting when given),
+    (plus moe_decode_misses from a host tier and cache counting when given;
+    with one_launch, one moe_decode_layer_tiers call instead of the two),
     with preallocated buffers, so that a whole step can be captured in a
     graph.  Each layer reads its own seeded input x_l and writes its y to a
     scratch buffer."""
 
     def __init__(self, torch, bf, shape, pools, T, dev, xs, logit_sets, tiers=None,
-                 host_table=None, max_rank=None, counts=None, overlap=False, misses_only=False):
+                 host_table=None, max_rank=None, counts=None, overlap=False, misses_only=False,
+                 one_launch=False):
         self.torch, self.bf = torch, bf
+        self.one_launch = one_launch   # hits and misses in one moe_decode_layer_tiers call
         self.T = T
         self.tiers, self.host_table, self.max_rank = tiers, host_table, max_rank
         self.overlap = overlap
@@ -186,10 +189,17 @@ class DecodeChain:
         if self.overlap:
             return self._step_overlapped(logits)
         for l, L in enumerate(self.layers):
-            bf.decode_layer(L, self.xs[l], logits[l], self.tables[l], idx=self.idx, w=self.w,
-                            slot=self.slot, miss_expert=self.miss_e, miss_pair=self.miss_p,
-                            n_miss=self.n_miss, y=self.y, ws=self.ws)
-            if self.tiers is not None:
+            if self.one_launch:
+                bf.decode_layer_tiers(L, self.tiers[l], self.xs[l], logits[l], self.tables[l],
+                                      self.host_table, max_rank=self.max_rank, idx=self.idx,
+                                      w=self.w, slot=self.slot, miss_expert=self.miss_e,
+                                      miss_pair=self.miss_p, n_miss=self.n_miss, y=self.y,
+                                      ws=self.ws)
+            else:
+                bf.decode_layer(L, self.xs[l], logits[l], self.tables[l], idx=self.idx, w=self.w,
+                                slot=self.slot, miss_expert=self.miss_e, miss_pair=self.miss_p,
+                                n_miss=self.n_miss, y=self.y, ws=self.ws)
+            if self.tiers is not None and not self.one_launch:
                 bf.decode_misses(self.tiers[l], self.xs[l], self.idx, self.slot, self.w,
                                  self.host_table, self.y, max_rank=self.max_rank, ws=self.ws)
             if self.counts is not None:
@@ -630,11 +640,15 @@ def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_gr
     sb = synth.slot_bytes(synth.FMT_Q2SM, d, f)
     res = {}
     misses_per_token = n_missed / n_graphs
-    for name, r, ov, mo in (("full_layer", None, False, False), ("rank_limit_5", 5, False, False),
-                            ("full_layer_two_streams", None, True, False),
-                            ("host_part_only", None, True, True)):
+    for name, r, ov, mo, one in (("full_layer", None, False, False, False),
+                                 ("rank_limit_5", 5, False, False, False),
+                                 ("full_layer_two_streams", None, True, False, False),
+                                 ("host_part_only", None, True, True, False),
+                                 ("full_layer_one_launch", None, False, False, True),
+                                 ("rank_limit_5_one_launch", 5, False, False, True)):
         chain = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, logits2, tiers=tiers,
-                            host_table=host_table, max_rank=r, overlap=ov, misses_only=mo)
+                            host_table=host_table, max_rank=r, overlap=ov, misses_only=mo,
+                            one_launch=one)
         dt, _, graphs = time_graph_steps(torch, chain, steps, 5, n_graphs)
         del graphs
         res[name + "_tok_s"] = round(steps / dt, 2)
@@ -667,7 +681,8 @@ def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_gr
                         "full_layer_two_streams: per layer routing and lookup, then the host-tier "
                         "read (moe_decode_misses_phases READ) on a second stream while the GPU "
                         "part runs, the join (JOIN) after both; host_part_only: that step "
-                        "without the GPU part")
+                        "without the GPU part; *_one_launch: moe_decode_layer_tiers, the hits "
+                        "and the misses in the same two kernels per layer")
     log(f"host tier: {res} ({time.perf_counter() - t0:.1f} s)")
     del chain, chain_full
     return res
@@ -767,8 +782,9 @@ def run_adaptive_cache(torch, np, bf, synth, shape, pools2, tiers, host_table, x
     """Routing drifts to another conversation (a new popularity order per
     layer), and the cache follows it: every token counts its experts, every
     `period` tokens each layer plans up to `max_swaps` swaps (counts halve),
-    copies the newcomers from the host tier and commits them.  Whole layers
-    (GPU part + misses from the host tier).  Reported: the hit rate of the
+    copies the newcomers from the host tier and commits them.  Whole layers:
+    the resident experts and the misses from the host tier in one
+    moe_decode_layer_tiers call per layer.  Reported: the hit rate of the
     original cache on the new routing, the hit rate after adapting (on
     held-out tokens of the new routing), and tok/s of the timed steps with
     the maintenance included."""
@@ -804,7 +820,7 @@ def run_adaptive_cache(torch, np, bf, synth, shape, pools2, tiers, host_table, x
     counts = [torch.zeros(E, dtype=torch.int32, device=dev) for _ in range(N_LAYERS)]
     lg_buf = logits_of(0)
     chain = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, [lg_buf], tiers=tiers,
-                        host_table=host_table, counts=counts)
+                        host_table=host_table, counts=counts, one_launch=True)
     swaps = [torch.full((max_swaps, 4), -1, dtype=torch.int32, device=dev) for _ in range(N_LAYERS)]
     n_sw = [torch.zeros(4, dtype=torch.int32, device=dev) for _ in range(N_LAYERS)]
 
@@ -873,7 +889,8 @@ def run_adaptive_cache(torch, np, bf, synth, shape, pools2, tiers, host_table, x
         "workload": f"routing moves to another popularity order; count every token, every "
                     f"{period} tokens up to {max_swaps} swaps per layer (counts halve), newcomers "
                     f"copied from the host tier by a kernel; whole layers with misses from the "
-                    f"host tier; timed after {warm_steps} adapting tokens",
+                    f"host tier (moe_decode_layer_tiers); timed after {warm_steps} adapting "
+                    f"tokens",
         "hit_rate_before": round(static_hit, 4),
         "hit_rate_after": round(adapted_hit, 4),
         "hit_rate_of_the_new_top_94": round(top_hit, 4),

@@ -74,6 +74,8 @@ SIGNATURES = {
                                    _c_sz, _vp]),
     "moe_decode_misses_phases": (_c_int, [_LP, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _vp,
                                           _vp, _c_sz, _c_int, _vp]),
+    "moe_decode_layer_tiers": (_c_int, [_LP, _LP, _vp, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp]),
     "moe_cache_count": (_c_int, [_vp, _c_int, _c_int, _vp, _vp]),
     "moe_cache_plan": (_c_int, [_vp, _c_int, _vp, _vp, _c_int, _c_int, _vp, _c_int, _c_int,
                                 _c_int, _vp, _vp, _vp]),
@@ -481,6 +483,53 @@ def decode_misses(tier: HostTier, x, idx, slot, w, host_slot_of_expert, y, max_r
                                           _ptr(ws), ws.numel(), int(phases), _stream(stream)),
            "moe_decode_misses_phases")
     return y
+
+
+def decode_layer_tiers(layer: MoeLayer, tier: HostTier, x, logits, slot_of_expert,
+                       host_slot_of_expert, max_rank=None, idx=None, w=None, slot=None,
+                       miss_expert=None, miss_pair=None, n_miss=None, y=None, ws=None,
+                       want_pairs=True, stream=None):
+    """Route, look up and run one decode layer with the misses read from the
+    host tier in the same launch (moe_decode_layer_tiers).
+    Returns (y, idx, w, slot, miss_expert, miss_pair, n_miss)."""
+    _dev(_shape(x, (None, layer.d_model), "x"), torch.float32, "x")
+    T = x.shape[0]
+    k = layer.top_k
+    _dev(_shape(logits, (T, layer.n_experts), "logits"), torch.float32, "logits")
+    _dev(_shape(slot_of_expert, (layer.n_experts,), "slot_of_expert"), torch.int32,
+         "slot_of_expert")
+    _dev(_shape(host_slot_of_expert, (tier.n_experts,), "host_slot_of_expert"), torch.int32,
+         "host_slot_of_expert")
+    dev = x.device
+    n = T * k
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev) if idx is None else idx
+    w = torch.empty((T, k), dtype=torch.float32, device=dev) if w is None else w
+    slot = torch.empty((T, k), dtype=torch.int32, device=dev) if slot is None else slot
+    if miss_expert is None:
+        miss_expert = torch.full((n,), -1, dtype=torch.int32, device=dev)
+    if want_pairs and miss_pair is None:
+        miss_pair = torch.full((n,), -1, dtype=torch.int32, device=dev)
+    n_miss = torch.zeros((4,), dtype=torch.int32, device=dev) if n_miss is None else n_miss
+    y = torch.empty_like(x) if y is None else y
+    for name, t, dt in (("idx", idx, torch.int32), ("w", w, torch.float32),
+                        ("slot", slot, torch.int32)):
+        _dev(_shape(t, (T, k), name), dt, name)
+    _dev(_at_least(miss_expert, n, "miss_expert"), torch.int32, "miss_expert")
+    if miss_pair is not None:
+        _dev(_at_least(miss_pair, n, "miss_pair"), torch.int32, "miss_pair")
+    _dev(_at_least(n_miss, 2, "n_miss"), torch.int32, "n_miss")
+    _dev(_shape(y, tuple(x.shape), "y"), torch.float32, "y")
+    if ws is None:
+        ws = torch.empty((decode_workspace_bytes(layer, T),), dtype=torch.uint8, device=dev)
+    r = k if max_rank is None else int(max_rank)
+    L, H = layer.c_struct(), tier.c_struct()
+    _check(lib().moe_decode_layer_tiers(ctypes.byref(L), ctypes.byref(H),
+                                        _ptr(host_slot_of_expert), r, _ptr(x), T, _ptr(logits),
+                                        _ptr(slot_of_expert), _ptr(idx), _ptr(w), _ptr(slot),
+                                        _ptr(miss_expert), _ptr(miss_pair), _ptr(n_miss),
+                                        _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_decode_layer_tiers")
+    return y, idx, w, slot, miss_expert, miss_pair, n_miss
 
 
 def cache_count(idx, counts, stream=None):

@@ -238,6 +238,34 @@ int moe_decode_layer_noalloc(const moe_layer* L, const float* x, int T, const fl
                           n_miss, y, ws, kNoAllocScratchBytes, stream);
 }
 
+int moe_decode_layer_tiers(const moe_layer* L, const moe_layer* H,
+                           const int32_t* host_slot_of_expert, int max_rank, const float* x,
+                           int T, const float* logits, const int32_t* slot_of_expert,
+                           int32_t* idx, float* w, int32_t* slot, int32_t* miss_expert,
+                           int32_t* miss_pair, int32_t* n_miss, float* y, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  int st = check_decode_layer(L, x, T, logits, slot_of_expert, idx, w, slot, miss_expert,
+                              miss_pair, n_miss, y);
+  if (st != MOE_OK) return st;
+  st = check_layer(H);
+  if (st != MOE_OK) return st;
+  // the host tier holds slots of the same experts in the same format
+  if (H->fmt != L->fmt || H->d_model != L->d_model || H->d_ff != L->d_ff ||
+      H->n_experts != L->n_experts || H->top_k != L->top_k || H->shared_slot != -1)
+    return MOE_EINVAL;
+  if (max_rank < 0 || max_rank > L->top_k) return MOE_EINVAL;
+  if (!host_slot_of_expert || !ws) return MOE_EINVAL;
+  if (!aligned16(host_slot_of_expert) || !aligned256(ws)) return MOE_EALIGN;
+  if (ws_bytes < bitffn::decode_workspace_bytes(L->d_model, L->d_ff, T, L->top_k))
+    return MOE_ENOSPC;
+  const void* host_dev = nullptr;
+  if (!device_address(H->pool, &host_dev)) return MOE_EINVAL;
+  return hip_status(bitffn::launch_decode_layer_tiers(*L, *H, host_dev, host_slot_of_expert,
+                                                      max_rank, x, T, logits, slot_of_expert,
+                                                      idx, w, slot, miss_expert, miss_pair,
+                                                      n_miss, y, ws, stream));
+}
+
 size_t moe_decode_stack_workspace_bytes(int d_model, int d_ff, int n_experts, int top_k, int T) {
   if (!valid_dims(MOE_FMT_Q2SM, d_model, d_ff)) return 0;
   if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS || top_k < 1 || top_k > MOE_MAX_TOPK ||

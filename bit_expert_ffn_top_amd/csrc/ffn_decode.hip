@@ -28,9 +28,13 @@
 // and scale/min are applied once per block.
 //
 // Modes of the ffn kernel: the pair slots given (moe_expert_ffn_decode), the
-// routing done inside every workgroup (moe_decode_layer, moe_decode_stack), or
+// routing done inside every workgroup (moe_decode_layer, moe_decode_stack),
 // the missed pairs only, with their slots in a second pool such as pinned host
-// memory (moe_decode_misses, whose combine adds into y).
+// memory (moe_decode_misses, whose combine adds into y), or routing with both
+// pools at once (moe_decode_layer_tiers): a chosen expert missing from the
+// first pool is a union member read from the second, its slot h carried as
+// -2 - h, so the two kinds of member never share a slot value and the layer
+// costs the slower of the two reads, not their sum.
 #include "moe_internal.h"
 #include "route_device.h"
 
@@ -68,6 +72,7 @@ enum FfnMode {
   kPairs = 0,   // the pair slots given by the caller
   kRoute = 1,   // routing done in the kernel (top-k, slot table)
   kMiss = 2,    // missed pairs only, their slots in a second pool (host tier)
+  kRouteTiers = 3,   // routing in the kernel; hits from the pool, misses from the host tier
 };
 
 // Plane offsets within a slot (a slot is far below 4 GiB), 32-bit so that a
@@ -102,6 +107,11 @@ struct FfnArgs {
   // slots of the pool read here (the host tier's in the miss mode): a slot
   // outside [0, n_slots), whether given or looked up, counts as a miss
   int n_slots;
+  // two-tier routing mode only: the host tier (same layout and slot size),
+  // the host slot of each expert, and the tier's slot count
+  const uint8_t* host_pool;
+  const int32_t* host_table;    // [E]
+  int host_n_slots;
 };
 
 // Routing inside the kernel: experts are taken in chunks of 512, one
@@ -126,7 +136,8 @@ __host__ __device__ inline int shared_jobs_per_slice(int shared_slot, bool miss)
 // T*k <= 64), so the test is a lane read and a ballot; the result is uniform
 // across the wavefront.
 __device__ __forceinline__ bool union_member(int sp, int T, int k, int shared_slot, int u,
-                                             int& s, uint32_t& mask, uint64_t& same) {
+                                             int& s, uint32_t& mask, uint64_t& same,
+                                             bool host_members = false) {
   const int n = T * k;
   if (u == n) {
     if (shared_slot < 0) return false;
@@ -136,7 +147,7 @@ __device__ __forceinline__ bool union_member(int sp, int T, int k, int shared_sl
     return true;
   }
   s = __builtin_amdgcn_readlane(sp, u);
-  if (s < 0) return false;
+  if (host_members ? s == -1 : s < 0) return false;
   same = __ballot(sp == s);
   if (same & ((1ull << u) - 1ull)) return false;   // an earlier pair names this slot
   const uint64_t kmask = k >= 64 ? ~0ull : (1ull << k) - 1ull;
@@ -188,7 +199,8 @@ __device__ __forceinline__ float wave_total(float v) {
 template <int FMT, int UPW, int MODE, bool LOOP>
 __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amdgpu_waves_per_eu(8, 8))) void decode_ffn_kernel(FfnArgs a,
                                                                 const float* __restrict__ x) {
-  constexpr bool ROUTE = MODE == kRoute;
+  constexpr bool ROUTE = MODE == kRoute || MODE == kRouteTiers;
+  constexpr bool TIERS = MODE == kRouteTiers;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int d = a.d;
@@ -235,6 +247,10 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
     for (int j = 0; j < 8; ++j)
       lg[j] = a.logits[static_cast<int64_t>(tt) * a.E + min(rc * kRouteChunk + 64 * j + lane, a.E - 1)];
     tv = a.table[min(tid, a.E - 1)];
+    if (TIERS) {   // an expert missing from the pool: its host slot, encoded as -2 - h
+      const int hs = a.host_table[min(tid, a.E - 1)];
+      tv = (tv >= 0 && tv < a.n_slots) ? tv : (hs >= 0 && hs < a.host_n_slots ? -2 - hs : -1);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);   // keep the issue order
 
@@ -271,6 +287,7 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
       wave_topk_keys<8>(key, a.k, out, s_scr[wave]);
     }
     if (tid < a.E) s_table[tid] = tv < a.n_slots ? tv : -1;   // out of the pool: a miss
+                                                            // (or its encoded host slot)
   }
   __syncthreads();
   if (ROUTE && nchunk > 1) {   // uniform: rank the 2k survivors of each token
@@ -286,6 +303,8 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
   if (routing) {
     const int e = lane < n ? key_expert(s_top[lane]) : 0;
     sp = lane < n ? s_table[e] : -1;
+    const int gpu_sp = sp < 0 ? -1 : sp;   // the pool's slot (-1: a miss)
+    if (TIERS && sp < -1 && lane % a.k >= a.max_rank) sp = -1;   // a miss left out
     if (static_cast<int>(blockIdx.x) == n_shared) {   // routing outputs: the first routing workgroup
       if (wave < a.T) {
         int id;
@@ -294,11 +313,11 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
         if (lane < a.k) {
           a.o_idx[wave * a.k + lane] = id;
           a.o_w[wave * a.k + lane] = wt;
-          a.o_slot[wave * a.k + lane] = s_table[id];
+          a.o_slot[wave * a.k + lane] = max(s_table[id], -1);
         }
       }
       if (wave == KA_WAVES - 1)
-        wave_miss_lists(lane, n, e, sp, a.o_miss_expert, a.o_miss_pair, a.o_n_miss);
+        wave_miss_lists(lane, n, e, gpu_sp, a.o_miss_expert, a.o_miss_pair, a.o_n_miss);
     }
   }
 
@@ -324,8 +343,10 @@ __global__ __launch_bounds__(KA_THREADS) __attribute__((amdgpu_num_sgpr(72), amd
   int s;
   uint32_t mask;
   uint64_t same;
-  if (!union_member(s_sp[tj & 63], a.T, a.k, a.shared_slot, u, s, mask, same)) return;
-  const uint8_t* __restrict__ base = a.pool + static_cast<int64_t>(s) * a.slot_bytes;
+  if (!union_member(s_sp[tj & 63], a.T, a.k, a.shared_slot, u, s, mask, same, TIERS)) return;
+  const uint8_t* __restrict__ base =
+      TIERS && s < 0 ? a.host_pool + static_cast<int64_t>(-2 - s) * a.slot_bytes
+                     : a.pool + static_cast<int64_t>(s) * a.slot_bytes;
   const uint32_t R = 2u * static_cast<uint32_t>(a.f);                   // G rows
   const uint32_t grow = 2u * SLICE * js + static_cast<uint32_t>(tj & 63);   // this lane's G row
   const int nu = d / 64;
@@ -502,7 +523,10 @@ constexpr int KB_WAVES = 16;
 constexpr int KB_CHUNK = 16;
 static_assert(KB_GROUPS == 2, "the group sums meet in one exchange");
 
-template <bool MISS>
+// CM: kCombinePlain (y = x + terms), kCombineMisses (y += the host tier's
+// terms), kCombineTiers (y = x + the pool's and the host tier's terms).
+enum CombineMode { kCombinePlain = 0, kCombineMisses = 1, kCombineTiers = 2 };
+template <int CM>
 __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
     const float* __restrict__ x, const int32_t* __restrict__ slot, const float* __restrict__ w,
     int T, int k, int d, int nslices, int has_shared, const float* __restrict__ part,
@@ -518,9 +542,12 @@ __global__ __launch_bounds__(KB_WAVES * 64) void decode_combine_kernel(
   const int ti = min(lane, k - 1);
   int sp = slot[t * k + ti];                     // lane i < k: slot of term i
   float wv = w[t * k + ti];                      // lane i < k: weight of term i
-  if (MISS) {
+  constexpr bool MISS = CM == kCombineMisses;
+  if (CM != kCombinePlain) {   // n_slots: the host tier's
     const int hs = host_slot[min(max(idx[t * k + ti], 0), n_experts - 1)];
-    sp = sp < 0 && ti < max_rank && hs < n_slots ? hs : -1;
+    const int hm = ti < max_rank && hs >= 0 && hs < n_slots ? hs : -1;   // a miss that ran
+    // the two-tier layer's slot output is the pool's slot (-1: a miss), in range
+    sp = MISS ? (sp < 0 ? hm : -1) : (sp >= 0 ? sp : hm);
   } else {
     sp = sp < n_slots ? sp : -1;   // a slot outside the pool is a miss, as in the ffn kernel
   }
@@ -587,7 +614,7 @@ hipError_t launch_ffn(const FfnArgs& a, const float* x, hipStream_t s) {
   const int upw = (a.d / 64 + KA_WAVES - 1) / KA_WAVES;
   // the job loop only where a workgroup takes more than one job (routing
   // mode: one routing per workgroup for all its jobs)
-  if constexpr (MODE == kRoute) {
+  if constexpr (MODE == kRoute || MODE == kRouteTiers) {
     if (grid < jobs) {
       if (upw <= 1)
         decode_ffn_kernel<FMT, 1, MODE, true><<<grid, KA_THREADS, 0, s>>>(a, x);
@@ -645,9 +672,21 @@ hipError_t launch_combine_partials(const moe_layer& L, const float* x, int T,
                                    const float* addend = nullptr) {
   const dim3 grid(L.d_model / KB_ROWS, T);
   const size_t lds = static_cast<size_t>(L.top_k + 1) * KB_ROWS * 4;
-  decode_combine_kernel<false><<<grid, KB_WAVES * 64, lds, s>>>(
+  decode_combine_kernel<kCombinePlain><<<grid, KB_WAVES * 64, lds, s>>>(
       x, slot, w, T, L.top_k, L.d_model, L.d_ff / SLICE, L.shared_slot >= 0 ? 1 : 0, part,
       nullptr, nullptr, 1, 0, L.n_slots, y, xnext, addend);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_tiers(const moe_layer& L, const moe_layer& H, const float* x, int T,
+                               const int32_t* idx, const int32_t* slot, const float* w,
+                               const int32_t* host_slot, int max_rank, const float* part,
+                               float* y, hipStream_t s) {
+  const dim3 grid(L.d_model / KB_ROWS, T);
+  const size_t lds = static_cast<size_t>(L.top_k + 1) * KB_ROWS * 4;
+  decode_combine_kernel<kCombineTiers><<<grid, KB_WAVES * 64, lds, s>>>(
+      x, slot, w, T, L.top_k, L.d_model, L.d_ff / SLICE, L.shared_slot >= 0 ? 1 : 0, part, idx,
+      host_slot, L.n_experts, max_rank, H.n_slots, y, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -656,7 +695,7 @@ hipError_t launch_combine_misses(const moe_layer& H, int T, const int32_t* idx,
                                  int max_rank, const float* part, float* y, hipStream_t s) {
   const dim3 grid(H.d_model / KB_ROWS, T);
   const size_t lds = static_cast<size_t>(H.top_k + 1) * KB_ROWS * 4;
-  decode_combine_kernel<true><<<grid, KB_WAVES * 64, lds, s>>>(
+  decode_combine_kernel<kCombineMisses><<<grid, KB_WAVES * 64, lds, s>>>(
       nullptr, slot, w, T, H.top_k, H.d_model, H.d_ff / SLICE, 0, part, idx, host_slot,
       H.n_experts, max_rank, H.n_slots, y, nullptr, nullptr);
   return hipGetLastError();
@@ -695,6 +734,31 @@ hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const 
   const hipError_t e = launch_ffn_fmt<kRoute>(L.fmt, a, x, s);
   if (e != hipSuccess) return e;
   return launch_combine_partials(L, x, T, slot, w, a.part, y, s, xnext, addend);
+}
+
+hipError_t launch_decode_layer_tiers(const moe_layer& L, const moe_layer& H,
+                                     const void* host_pool_dev, const int32_t* host_slot_of_expert,
+                                     int max_rank, const float* x, int T, const float* logits,
+                                     const int32_t* slot_of_expert, int32_t* idx, float* w,
+                                     int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
+                                     int32_t* n_miss, float* y, void* ws, hipStream_t s) {
+  FfnArgs a = ffn_args(L, T, nullptr, ws);
+  a.logits = logits;
+  a.table = slot_of_expert;
+  a.o_idx = idx;
+  a.o_w = w;
+  a.o_slot = slot;
+  a.o_miss_expert = miss_expert;
+  a.o_miss_pair = miss_pair;
+  a.o_n_miss = n_miss;
+  a.max_rank = max_rank;
+  a.host_pool = static_cast<const uint8_t*>(host_pool_dev);
+  a.host_table = host_slot_of_expert;
+  a.host_n_slots = H.n_slots;
+  const hipError_t e = launch_ffn_fmt<kRouteTiers>(L.fmt, a, x, s);
+  if (e != hipSuccess) return e;
+  return launch_combine_tiers(L, H, x, T, idx, slot, w, host_slot_of_expert, max_rank, a.part,
+                              y, s);
 }
 
 hipError_t launch_decode_misses(const moe_layer& H, const void* host_pool_dev, const float* x,

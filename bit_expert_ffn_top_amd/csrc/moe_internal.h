@@ -73,6 +73,15 @@ hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const 
                                float* xnext = nullptr, const float* addend = nullptr);
 // Missed pairs of a decode step computed from a second pool (the host tier,
 // `host_pool_dev` its device-side address) and added into y.
+// The decode layer with the misses read from a second pool (host tier) in the
+// same launch as the hits (moe_decode_layer_tiers).
+hipError_t launch_decode_layer_tiers(const moe_layer& L, const moe_layer& H,
+                                     const void* host_pool_dev, const int32_t* host_slot_of_expert,
+                                     int max_rank, const float* x, int T, const float* logits,
+                                     const int32_t* slot_of_expert, int32_t* idx, float* w,
+                                     int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
+                                     int32_t* n_miss, float* y, void* ws, hipStream_t s);
+
 hipError_t launch_decode_misses(const moe_layer& H, const void* host_pool_dev, const float* x,
                                 int T, const int32_t* idx, const int32_t* slot, const float* w,
                                 const int32_t* host_slot_of_expert, int max_rank, float* y,

@@ -353,6 +353,40 @@ int moe_decode_misses_phases(const moe_layer* H, const float* x, int T,
                              float* y, void* ws, size_t ws_bytes, int phases,
                              hipStream_t stream);
 
+/* One decode / verify layer with both tiers in the same two kernels: the
+ * routing and lookup of moe_decode_layer, then the chosen experts resident in
+ * L's pool read from there and the missed ones read from the host tier H in
+ * the same launch, all terms joined in one sum ("Strataとは？VRAM 12GBのGPUで
+ * …" (vramglass.com), section "その2": the missed experts are computed from
+ * host memory at the same time as the resident ones; "FreeToken vs Strata",
+ * "共通の仕組み": both parts meet before the next layer; "Strata" page,
+ * section "どう見るか": missed experts of low rank may be left out).  The
+ * layer time is that of the larger part, not of the two parts in turn.
+ *   L, x, T, logits, slot_of_expert, idx, w, slot, miss_expert, miss_pair,
+ *   n_miss   as moe_decode_layer; slot (and the miss lists) describe the GPU
+ *            cache only: -1 for a pair not resident there, whether or not
+ *            the host tier computed it.
+ *   H, host_slot_of_expert, max_rank   as moe_decode_misses (same fmt,
+ *            d_model, d_ff, n_experts and top_k as L; H->shared_slot = -1;
+ *            H->pool pinned host or device memory).
+ *   y        fp32 [T][d_model] output:
+ *   y[t] = x[t] + sum_i term(t,i) + FFN_shared(x[t]), term(t,i) =
+ *            w * FFN of GPU slot slot[t*k+i]                if that slot >= 0,
+ *            w * FFN of host slot h = host_slot_of_expert[idx[t*k+i]]
+ *                                       if the pair missed, i < max_rank and
+ *                                       0 <= h < H->n_slots,
+ *            0 otherwise;
+ *            terms in k-slot order, then the shared expert (the same sum as
+ *            moe_decode_layer's when nothing misses, so then the same bits).
+ * Limits as moe_decode_layer.  ws: at least moe_decode_workspace_bytes(L, T)
+ * bytes, 256-byte aligned. */
+int moe_decode_layer_tiers(const moe_layer* L, const moe_layer* H,
+                           const int32_t* host_slot_of_expert, int max_rank, const float* x,
+                           int T, const float* logits, const int32_t* slot_of_expert,
+                           int32_t* idx, float* w, int32_t* slot, int32_t* miss_expert,
+                           int32_t* miss_pair, int32_t* n_miss, float* y, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
 /* Expert-cache admission and eviction.  The cache starts from a table of
  * usage frequencies and is updated as the conversation moves on ("FreeToken
  * vs Strata", comparison table, row "VRAMのエキスパートの入れ替え";

@@ -234,6 +234,42 @@ void misses() {
   EXPECT(phases(MOE_MISSES_JOIN, nullptr, fp<float>(8), fp<float>(1 << 21)), MOE_EALIGN);
 }
 
+void layer_tiers() {
+  moe_layer L = layer();
+  moe_layer H = layer(2048, 768, 512, 10, MOE_FMT_Q2SM, 512, -1);
+  const size_t need = moe_decode_workspace_bytes(&L, 1);
+  auto call = [&](const moe_layer& l, const moe_layer& h, int T, int max_rank, const int32_t* host,
+                  float* yy, void* ws, size_t nb) {
+    return moe_decode_layer_tiers(&l, &h, host, max_rank, fp<float>(), T, fp<float>(1 << 16),
+                                  fp<int32_t>(1 << 17), fp<int32_t>(1 << 18), fp<float>(1 << 19),
+                                  fp<int32_t>(1 << 21), fp<int32_t>(1 << 22), nullptr,
+                                  fp<int32_t>(1 << 23), yy, ws, nb, s0);
+  };
+  float* y = fp<float>(1 << 20);
+  const int32_t* hs = fp<int32_t>(1 << 24);
+  EXPECT(call(L, H, 1, 10, hs, y, fp(), need - 1), MOE_ENOSPC);
+  EXPECT(call(L, H, 1, 10, hs, y, nullptr, need), MOE_EINVAL);
+  EXPECT(call(L, H, 1, 10, hs, y, fp(16), need), MOE_EALIGN);
+  EXPECT(call(L, H, 1, 10, nullptr, y, fp(), need), MOE_EINVAL);
+  EXPECT(call(L, H, 1, 10, fp<int32_t>(4), y, fp(), need), MOE_EALIGN);
+  EXPECT(call(L, H, 1, 11, hs, y, fp(), need), MOE_EINVAL);
+  EXPECT(call(L, H, 1, -1, hs, y, fp(), need), MOE_EINVAL);
+  EXPECT(call(L, H, 5, 10, hs, y, fp(), need), MOE_EINVAL);
+  EXPECT(call(L, H, 1, 10, hs, fp<float>(), fp(), need), MOE_EINVAL);
+  EXPECT(call(L, layer(2048, 768, 512, 10, MOE_FMT_Q2SM, 512, 3), 1, 10, hs, y, fp(), need),
+         MOE_EINVAL);
+  EXPECT(call(L, layer(2048, 768, 512, 8, MOE_FMT_Q2SM, 512, -1), 1, 10, hs, y, fp(), need),
+         MOE_EINVAL);
+  EXPECT(call(L, layer(2048, 768, 256, 10, MOE_FMT_Q2SM, 512, -1), 1, 10, hs, y, fp(), need),
+         MOE_EINVAL);
+  EXPECT(call(L, layer(2048, 768, 512, 10, MOE_FMT_Q3G, 512, -1), 1, 10, hs, y, fp(), need),
+         MOE_EINVAL);
+  moe_layer hb = H;
+  hb.pool = fp(16);
+  EXPECT(call(L, hb, 1, 10, hs, y, fp(), need), MOE_EALIGN);
+  EXPECT(call(layer(2048, 768, 512, 10, 9), H, 1, 10, hs, y, fp(), need), MOE_EFORMAT);
+}
+
 void cache_policy() {
   int32_t* p = fp<int32_t>();
   uint32_t* c = fp<uint32_t>();
@@ -377,6 +413,7 @@ int main() {
   decode();
   prefill_and_combine();
   misses();
+  layer_tiers();
   cache_policy();
   stage();
   stack();

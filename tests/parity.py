@@ -89,3 +89,45 @@ class GpuLayer:
 
     def table_dev(self, dev):
         return torch.tensor(self.table, dtype=torch.int32, device=dev)
+
+
+class HostTier:
+    """Every expert of a layer in pinned host memory at a permuted slot
+    order (only the experts in `fill` are generated; the other slots hold
+    zeros and must never be read for a nonzero term)."""
+
+    def __init__(self, cfg, layer, shape, fmt, fill, absent=(), device_pool=False, seed=0):
+        import bit_expert_ffn_top_amd as bf
+        E = shape.n_experts
+        rng = np.random.default_rng(500 + seed)
+        order = rng.permutation(E)                  # host slot h holds expert order[h]
+        self.host_slot = np.empty(E, np.int32)
+        self.host_slot[order] = np.arange(E, dtype=np.int32)
+        for e in absent:
+            self.host_slot[e] = -1
+        self.fmt, self.shape = fmt, shape
+        sb = synth.slot_bytes(fmt, shape.d_model, shape.d_ff)
+        if device_pool:
+            self.pool = torch.zeros((E, sb), dtype=torch.uint8, device="cuda:0")
+        else:
+            self.pool = torch.zeros((E, sb), dtype=torch.uint8, pin_memory=True)
+        fill = sorted(set(int(e) for e in fill) - set(absent))
+        self._bytes = {}
+        if fill:
+            packed = synth.make_layer_pool(cfg, layer, fill, device="cuda:0", fmt=fmt,
+                                           shape=shape).cpu()
+            for j, e in enumerate(fill):
+                h = int(self.host_slot[e])
+                self.pool[h] = packed[j].to(self.pool.device)
+                self._bytes[h] = packed[j].numpy()
+        self._w = {}
+        self.tier = bf.HostTier(shape.d_model, shape.d_ff, E, shape.top_k, fmt, self.pool)
+
+    def weights_of_host_slot(self, h):
+        if h not in self._w:
+            self._w[h] = oracle.unpack_expert(self._bytes[h], self.fmt, self.shape.d_model,
+                                              self.shape.d_ff)
+        return self._w[h]
+
+    def table_dev(self):
+        return torch.tensor(self.host_slot, dtype=torch.int32, device="cuda:0")

@@ -208,6 +208,35 @@ def test_decode_misses_host_checks():
     assert phases(2, x=None, y=_p(8)) == -2
 
 
+def test_decode_layer_tiers_host_checks():
+    lib = _lib()
+    s = ctypes.c_void_p(0)
+    L = _layer()
+    H = _layer(shared_slot=-1, n_slots=512)
+    need = lib.moe_decode_workspace_bytes(ctypes.byref(L), 1)
+    def call(L=L, H=H, T=1, max_rank=10, ws=need, wsp=_p(), y=_p(1 << 20), host=_p(1 << 24)):
+        return lib.moe_decode_layer_tiers(ctypes.byref(L), ctypes.byref(H), host, max_rank, _p(),
+                                          T, _p(1 << 16), _p(1 << 17), _p(1 << 18), _p(1 << 19),
+                                          _p(1 << 21), _p(1 << 22), None, _p(1 << 23), y, wsp,
+                                          ws, s)
+    assert call(ws=need - 1) == -4
+    assert call(wsp=None) == -1
+    assert call(wsp=_p(16)) == -2
+    assert call(host=None) == -1
+    assert call(host=_p(4)) == -2
+    assert call(max_rank=11) == -1
+    assert call(max_rank=-1) == -1
+    assert call(T=5) == -1
+    assert call(y=_p()) == -1                                                # y aliases x
+    assert call(H=_layer(shared_slot=3, n_slots=512)) == -1                  # shared slot in the tier
+    assert call(H=_layer(shared_slot=-1, n_slots=512, top_k=8)) == -1        # other top_k
+    assert call(H=_layer(shared_slot=-1, n_slots=512, n_experts=256)) == -1  # other E
+    assert call(H=_layer(shared_slot=-1, n_slots=512, fmt=3,
+                         slot_bytes=synth.slot_bytes(3, 2048, 768))) == -1   # other format
+    assert call(H=_layer(shared_slot=-1, n_slots=512, pool=FAKE + 16)) == -2
+    assert call(L=_layer(fmt=9)) == -3
+
+
 def test_cache_policy_host_checks():
     lib = _lib()
     s = ctypes.c_void_p(0)
