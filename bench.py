@@ -628,6 +628,9 @@ def build_host_tiers(torch, bf, synth, shape, dev):
     return tiers, host_table
 
 
+HOST_LINK_GBPS = 63.0   # PCIe 5.0 x16: 64 GB/s per direction less 128b/130b coding
+
+
 def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_graphs, n_missed,
                   tiers, host_table, xs):
     """The expert-cache workload as whole layers: after each layer's GPU
@@ -657,6 +660,22 @@ def run_host_tier(torch, np, bf, synth, shape, pools2, logits2, dev, steps, n_gr
     # at batch 1 every missed pair is a distinct expert read from the host tier
     res["missed_experts_per_token"] = round(misses_per_token, 2)
     res["host_read_MB_per_token"] = round(misses_per_token * sb / 1e6, 1)
+    # misses of k-slot < 5 (the ones the rank limit keeps), same routings
+    kept = 0
+    for g in range(n_graphs):
+        for l in range(N_LAYERS):
+            idx = np.argsort(-logits2[g][l].cpu().numpy(), axis=1, kind="stable")[:, :k]
+            kept += int((pools2[l][1].cpu().numpy()[idx[:, :5]] < 0).sum())
+    kept_per_token = kept / n_graphs
+    res["rank_limit_5_host_read_MB_per_token"] = round(kept_per_token * sb / 1e6, 1)
+    # the host link as the roofline of the one-launch layers: host bytes per token
+    # over the token time, against PCIe 5.0 x16's 63 GB/s of payload per direction
+    link = {}
+    for name, per_tok in (("full_layer_one_launch", misses_per_token),
+                          ("rank_limit_5_one_launch", kept_per_token)):
+        gbps = per_tok * sb / (res[name + "_ms_per_step"] * 1e-3) / 1e9
+        link[name] = {"achieved": round(gbps, 1), "frac": round(gbps / HOST_LINK_GBPS, 3)}
+    res["host_link_roofline"] = dict(bound="host link", peak=HOST_LINK_GBPS, unit="GB/s", **link)
     # effect of the rank limit on each layer's update y - x (graph 0's routing)
     chain_full = DecodeChain(torch, bf, shape, pools2, 1, dev, xs, logits2, tiers=tiers,
                              host_table=host_table)

@@ -492,14 +492,17 @@ def decode_layer_tiers(layer: MoeLayer, tier: HostTier, x, logits, slot_of_exper
     """Route, look up and run one decode layer with the misses read from the
     host tier in the same launch (moe_decode_layer_tiers).
     Returns (y, idx, w, slot, miss_expert, miss_pair, n_miss)."""
-    _dev(_shape(x, (None, layer.d_model), "x"), torch.float32, "x")
+    _shape(x, (None, layer.d_model), "x")
     T = x.shape[0]
     k = layer.top_k
-    _dev(_shape(logits, (T, layer.n_experts), "logits"), torch.float32, "logits")
-    _dev(_shape(slot_of_expert, (layer.n_experts,), "slot_of_expert"), torch.int32,
-         "slot_of_expert")
-    _dev(_shape(host_slot_of_expert, (tier.n_experts,), "host_slot_of_expert"), torch.int32,
-         "host_slot_of_expert")
+    checks = [(x, torch.float32, "x"),
+              (_shape(logits, (T, layer.n_experts), "logits"), torch.float32, "logits"),
+              (_shape(slot_of_expert, (layer.n_experts,), "slot_of_expert"), torch.int32,
+               "slot_of_expert"),
+              (_shape(host_slot_of_expert, (tier.n_experts,), "host_slot_of_expert"),
+               torch.int32, "host_slot_of_expert")]
+    for t, dt, name in checks:   # every shape above first, then the devices and types
+        _dev(t, dt, name)
     dev = x.device
     n = T * k
     idx = torch.empty((T, k), dtype=torch.int32, device=dev) if idx is None else idx

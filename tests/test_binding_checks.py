@@ -58,6 +58,24 @@ def test_decode_misses_shapes():
             ids, w, torch.zeros(8, dtype=torch.int32), torch.zeros((1, 64)))
 
 
+def test_decode_layer_tiers_shapes():
+    L = _layer()
+    tier = bf.HostTier.__new__(bf.HostTier)        # shape fields only: no pool needed here
+    tier.d_model, tier.d_ff, tier.n_experts, tier.top_k = L.d_model, L.d_ff, L.n_experts, L.top_k
+    x = torch.zeros((1, 64))
+    tab = torch.zeros(8, dtype=torch.int32)
+    _raises(r"x: shape \(\*, 64\)", bf.decode_layer_tiers, L, tier, torch.zeros((1, 32)),
+            torch.zeros((1, 8)), tab, tab)
+    _raises(r"logits: shape \(1, 8\)", bf.decode_layer_tiers, L, tier, x, torch.zeros((2, 8)),
+            tab, tab)
+    _raises(r"slot_of_expert: shape \(8,\)", bf.decode_layer_tiers, L, tier, x,
+            torch.zeros((1, 8)), torch.zeros(9, dtype=torch.int32), tab)
+    _raises(r"host_slot_of_expert: shape \(8,\)", bf.decode_layer_tiers, L, tier, x,
+            torch.zeros((1, 8)), tab, torch.zeros(7, dtype=torch.int32))
+    _raises(r"x must be a device tensor", bf.decode_layer_tiers, L, tier, x,
+            torch.zeros((1, 8)), tab, tab)
+
+
 def test_cache_plan_shapes():
     i32 = dict(dtype=torch.int32)
     counts = torch.zeros(8, **i32)
