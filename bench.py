@@ -16,10 +16,15 @@ tensors, resident in HBM before timing starts.  Steps are replayed from HIP
 graphs.
 
 Extra objects on the same line: the decode kernel's roofline (HBM), the
-expert-cache workload (94 of 512 experts resident, about 72% hits), the
-1+3-token verify step, the 8,192-token prefill chunk with its GEMMs' MFMA
-roofline, and the CPU oracle timed on a bounded sample of the decode
-workload on this host.
+expert-cache workload (94 of 512 experts resident, about 72% hits; whole
+layers with the misses read from a pinned host copy, with the host link as
+their roofline), the 1+3-token verify step, the router projection, the
+8,192-token prefill chunk with its GEMMs' MFMA roofline, and the CPU oracle
+timed on a bounded sample of the decode workload on this host.
+
+For profiling, --cache-only, --tiers-only, --prefill-only and --router-only
+run one part alone and print its object; --counters and --counters-verify
+run the short passes the HBM counter summaries are taken from.
 """
 from __future__ import annotations
 
@@ -72,6 +77,9 @@ def parse():
                          "adaptive cache; for profiling); prints their object")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill workload (for profiling); prints its object")
+    ap.add_argument("--tiers-only", action="store_true",
+                    help="run only whole expert-cache layers with every miss read from the "
+                         "host tier in the same launch (for profiling); prints its object")
     ap.add_argument("--router-only", action="store_true",
                     help="run only the router projection (for profiling); prints its object")
     ap.add_argument("--counters", action="store_true",
@@ -367,6 +375,11 @@ def main():
         print(json.dumps({"router": run_router(torch, bf, synth, dev)}), flush=True)
         return
 
+    if args.tiers_only:
+        print(json.dumps({"host_tier_one_launch": run_tiers_only(torch, bf, synth, dev, args)}),
+              flush=True)
+        return
+
     t_gen = time.perf_counter()
     pools = build_pools(torch, synth, 1, lambda l: synth.FMT_Q2SM, dev)
     torch.cuda.synchronize()
@@ -626,6 +639,30 @@ def build_host_tiers(torch, bf, synth, shape, dev):
     log(f"host tiers: {N_LAYERS} x {E} experts pinned ({N_LAYERS * E * sb / 1e9:.1f} GB) "
         f"in {time.perf_counter() - t0:.1f} s")
     return tiers, host_table
+
+
+def run_tiers_only(torch, bf, synth, dev, args):
+    """The expert-cache workload's whole layers with every miss read from
+    the host tier by moe_decode_layer_tiers, and nothing else (so that a
+    profile of this command shows that layer's kernels alone)."""
+    shape = synth.config_shape(2)
+    E, d = shape.n_experts, shape.d_model
+    c2 = synth.WORKLOADS[2]
+    pools2 = build_pools(torch, synth, 2, lambda l: synth.FMT_Q2SM, dev)
+    n_graphs = min(args.graphs, 8)
+    logits2 = [torch.stack([synth.zipf_gumbel_logits(2, l, 1, E, c2["zipf_s"], device=dev, step=g)
+                            for l in range(N_LAYERS)]) for g in range(n_graphs)]
+    xs2 = [synth.make_x(2, l, 1, d, device=dev) for l in range(N_LAYERS)]
+    tiers, host_table = build_host_tiers(torch, bf, synth, shape, dev)
+    chain = DecodeChain(torch, bf, shape, pools2, 1, dev, xs2, logits2, tiers=tiers,
+                        host_table=host_table, one_launch=True)
+    steps = max(20, args.steps // 2)
+    dt, _, graphs = time_graph_steps(torch, chain, steps, 5, n_graphs)
+    del graphs
+    res = {"tok_s": round(steps / dt, 2), "ms_per_step": round(dt * 1e3 / steps, 5),
+           "avg_layer_us": round(dt * 1e6 / (steps * N_LAYERS), 3), "steps": steps}
+    log(f"one-launch host-tier layers: {res}")
+    return res
 
 
 HOST_LINK_GBPS = 63.0   # PCIe 5.0 x16: 64 GB/s per direction less 128b/130b coding
