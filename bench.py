@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=2)
+    ap.add_argument("--decode-only", action="store_true",
+                    help="the decode headline and the verify step only (no other workloads, "
+                         "no CPU baseline)")
     ap.add_argument("--cache-only", action="store_true",
                     help="run only the expert-cache workloads (host tier, staged prefill, "
                          "adaptive cache; for profiling); prints their object")
@@ -463,7 +466,7 @@ def main():
         extra.update(run_extras(torch, np, bf, synth, pools, dev, args))
     result.update(extra)
 
-    if not args.no_cpu:
+    if not args.no_cpu and not args.decode_only:
         result["cpu_baseline"] = cpu_baseline(np, synth, pools, shape)
     print(json.dumps(result), flush=True)
 
@@ -472,6 +475,9 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
     out = {}
     shape = synth.config_shape(1)
     E, k, d, f = shape.n_experts, shape.top_k, shape.d_model, shape.d_ff
+    n_graphs = min(args.graphs, 8)
+    if getattr(args, "decode_only", False):
+        return run_verify(torch, np, bf, synth, shape, pools, dev, args, n_graphs, out)
 
     # ---------------- expert-cache workload ----------------
     t0 = time.perf_counter()
@@ -514,8 +520,19 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
     torch.cuda.empty_cache()
     if cache_only:
         return out
+    run_verify(torch, np, bf, synth, shape, pools, dev, args, n_graphs, out)
 
-    # ---------------- verify step ----------------
+    # ---------------- router projection ----------------
+    out["router"] = run_router(torch, bf, synth, dev)
+
+    # ---------------- prefill chunk ----------------
+    out["prefill"] = run_prefill(torch, np, bf, synth, pools, dev, args)
+    return out
+
+
+def run_verify(torch, np, bf, synth, shape, pools, dev, args, n_graphs, out):
+    """The verify step (workload 3) timed into out["verify"]."""
+    k, d, f = shape.top_k, shape.d_model, shape.d_ff
     t0 = time.perf_counter()
     chain3, pools3, logits3 = verify_chain(torch, bf, synth, shape, pools, dev, n_graphs)
     steps3 = max(20, args.steps // 2)
@@ -546,12 +563,6 @@ def run_extras(torch, np, bf, synth, pools, dev, args, cache_only=False):
     log(f"verify: {sps:.1f} steps/s, union {mean_u:.2f} ({time.perf_counter() - t0:.1f} s)")
     del pools3, chain3, logits3
     torch.cuda.empty_cache()
-
-    # ---------------- router projection ----------------
-    out["router"] = run_router(torch, bf, synth, dev)
-
-    # ---------------- prefill chunk ----------------
-    out["prefill"] = run_prefill(torch, np, bf, synth, pools, dev, args)
     return out
 
 

@@ -251,3 +251,36 @@ def test_stack_routing_edge_cases(E, k):
     out = _run(layers, x, logits, tables, adds)
     _check_against_oracle(layers, x, logits, adds, out, tabs)
     assert list(out["idx"][0][0].cpu().numpy()) == list(range(k))
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_stack_full_size_equals_one_layer_calls(T):
+    """At the model's shape, 8 stacked layers (Q2SM and Q3G in turn) in one
+    call give the bits of 8 one-layer calls chained here with the same fp32
+    additions, with the routing outputs given per layer or not at all (the
+    workspace's stand-ins then serve every layer)."""
+    import bit_expert_ffn_top_amd as bf
+    dev = need_gpu()
+    shape = synth.config_shape(1)
+    nl = 8
+    fmts = [(synth.FMT_Q2SM, synth.FMT_Q3G)[l % 2] for l in range(nl)]
+    x, logits, adds = _inputs(1, shape, T, nl, dev, sigma=1.5, step=11)
+    only = [set(oracle.route_topk(logits[l].cpu().numpy(), shape.top_k)[0].reshape(-1).tolist())
+            for l in range(nl)]
+    layers, tabs = _layers(1, shape, fmts, 1.0, dev, only=only)
+    tables = [torch.tensor(t, dtype=torch.int32, device=dev) for t in tabs]
+    full = _run(layers, x, logits, tables, adds)
+    objs = [L.layer_obj for L in layers]
+    bare = bf.decode_stack(objs, x, logits, tables, addends=adds)   # no routing outputs
+    torch.cuda.synchronize()
+    assert torch.equal(bare["y"], full["y"])
+    xl = x
+    for l in range(nl):
+        one = _run([layers[l]], xl, [logits[l]], [tables[l]], [adds[l]])
+        assert torch.equal(one["y"][0], full["y"][l]), l
+        assert torch.equal(one["idx"][0], full["idx"][l]), l
+        assert torch.equal(one["w"][0], full["w"][l]), l
+        if l + 1 < nl:
+            xl = (one["y"][0] + adds[l + 1]).contiguous()
+    _check_against_oracle(layers[:2], x, logits[:2], adds[:2],
+                          {k: v[:2] for k, v in full.items() if k != "ws"}, tabs[:2])
