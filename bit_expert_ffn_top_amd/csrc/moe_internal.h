@@ -71,8 +71,6 @@ hipError_t launch_decode_layer(const moe_layer& L, const float* x, int T, const 
                                int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
                                int32_t* n_miss, float* y, void* ws, hipStream_t s,
                                float* xnext = nullptr, const float* addend = nullptr);
-// Missed pairs of a decode step computed from a second pool (the host tier,
-// `host_pool_dev` its device-side address) and added into y.
 // The decode layer with the misses read from a second pool (host tier) in the
 // same launch as the hits (moe_decode_layer_tiers).
 hipError_t launch_decode_layer_tiers(const moe_layer& L, const moe_layer& H,
@@ -82,6 +80,9 @@ hipError_t launch_decode_layer_tiers(const moe_layer& L, const moe_layer& H,
                                      int32_t* slot, int32_t* miss_expert, int32_t* miss_pair,
                                      int32_t* n_miss, float* y, void* ws, hipStream_t s);
 
+// Missed pairs of a decode step computed from a second pool (the host tier,
+// `host_pool_dev` its device-side address) and added into y; `phases` selects
+// the read (their products into the workspace) and the join (y += them).
 hipError_t launch_decode_misses(const moe_layer& H, const void* host_pool_dev, const float* x,
                                 int T, const int32_t* idx, const int32_t* slot, const float* w,
                                 const int32_t* host_slot_of_expert, int max_rank, float* y,
