@@ -227,3 +227,34 @@ def test_combine_parity():
             ref = oracle.combine(xx.double().numpy(), rows.double().numpy(), pos,
                                  w.double().numpy(), None if s is None else s.double().numpy())
             np.testing.assert_allclose(y.cpu().double().numpy(), ref, rtol=1e-5, atol=1e-5)
+
+
+def test_prefill_skewed_groups():
+    """Degenerate routing: one expert chosen first by every token (a group of
+    600 rows: three 256-row tiles, the last ragged), one chosen by half of
+    them (300 rows: two tiles), one never chosen (an empty group), and the
+    rest spread; grouping exact, rows and y within the bar."""
+    dev = need_gpu()
+    shape = synth.LayerShape(16, 3, 256, 128, True)
+    L = GpuLayer(4, 4, shape, synth.FMT_Q2SM, dev)
+    T = 600
+    x = synth.make_x(4, 4, T, shape.d_model, dtype=torch.bfloat16)
+    logits = synth.make_logits(4, 4, T, shape.n_experts, 1.0)
+    logits[:, 3] += 20.0                      # every token's first choice
+    logits[: T // 2, 5] += 10.0               # second choice of half the tokens
+    logits[:, 7] -= 50.0                      # never chosen
+    out_pairs, pair_pos, offs, out_sh, y, idx, slot, w = _prefill(L, x, logits, shape.top_k, dev)
+    ridx, rw = oracle.route_topk(logits.numpy(), shape.top_k)
+    np.testing.assert_array_equal(idx, ridx)
+    roffs, rpos, _ = _oracle_groups(ridx, slot, shape.n_experts)
+    np.testing.assert_array_equal(offs, roffs)
+    np.testing.assert_array_equal(pair_pos, rpos)
+    sizes = np.diff(roffs)
+    assert sizes[3] == T and sizes[5] >= T // 2 and sizes[7] == 0
+    xd = x.double().numpy()
+    ro, rsh, ry = oracle.prefill_layer(xd, ridx, rw, L.weights_of_expert,
+                                       L.weights_of_slot(L.shared_slot), shape.n_experts)
+    n = int(roffs[-1])
+    check_close(out_pairs.numpy()[:n], ro[:n], what="out_pairs")
+    check_close(out_sh.numpy(), rsh, what="out_shared")
+    check_close(y.numpy(), ry, xd)
