@@ -58,7 +58,7 @@ def test_decode_small(name, shape, fmt, T, shared):
 
 
 @pytest.mark.parametrize("fmt", [synth.FMT_Q2SM, synth.FMT_Q3G])
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_decode_full_layer(fmt, T):
     """The decode layer at full size: E=512, top-10 + shared, d=2048, d_ff=768,
     all experts resident under a random slot permutation (only the chosen

@@ -77,7 +77,8 @@ def test_decode_layer_small(name, shape, fmt, T, shared):
     _compare(L, x, logits)
 
 
-@pytest.mark.parametrize("fmt,T", [(synth.FMT_Q2SM, 1), (synth.FMT_Q3G, 4)])
+@pytest.mark.parametrize("fmt,T", [(synth.FMT_Q2SM, 1), (synth.FMT_Q3G, 4), (synth.FMT_Q2S, 3),
+                                   (synth.FMT_Q2SM, 2)])
 def test_decode_layer_full_size(fmt, T):
     """E=512, top-10 + shared, d=2048, d_ff=768 (only the chosen experts'
     slots are filled; no other slot is read)."""

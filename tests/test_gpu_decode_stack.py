@@ -102,6 +102,7 @@ def test_stack_small_vs_oracle(name, shape, T, fmts, frac):
 
 
 @pytest.mark.parametrize("T,fmts", [(1, (synth.FMT_Q2SM, synth.FMT_Q3G, synth.FMT_Q2SM)),
+                                    (3, (synth.FMT_Q2S, synth.FMT_Q2SM)),
                                     (4, (synth.FMT_Q2SM, synth.FMT_Q3G))])
 def test_stack_full_size(T, fmts):
     """E=512, top-10 + shared, d=2048, d_ff=768, every expert resident under a
