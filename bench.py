@@ -23,8 +23,10 @@ their roofline), the 1+3-token verify step, the router projection, the
 timed on a bounded sample of the decode workload on this host.
 
 For profiling, --cache-only, --tiers-only, --prefill-only and --router-only
-run one part alone and print its object; --counters and --counters-verify
-run the short passes the HBM counter summaries are taken from.
+run one part alone and print its object, and --decode-only prints the
+headline line with only the verify object beside it; --counters and
+--counters-verify run the short passes the HBM counter summaries are taken
+from.
 """
 from __future__ import annotations
 
