@@ -285,3 +285,30 @@ def test_stack_full_size_equals_one_layer_calls(T):
             xl = (one["y"][0] + adds[l + 1]).contiguous()
     _check_against_oracle(layers[:2], x, logits[:2], adds[:2],
                           {k: v[:2] for k, v in full.items() if k != "ws"}, tabs[:2])
+
+
+def test_stack_cache_full_size_t4():
+    """The expert-cache workload's shape through a stack at T = 4: 94 of 512
+    experts + the shared one resident per layer (the seeded residency),
+    Zipf(1.1) routing; every layer's routing outputs and miss lists exact,
+    y (the resident part) within the bar."""
+    dev = need_gpu()
+    shape = synth.config_shape(2)
+    c = synth.WORKLOADS[2]
+    T, nl = 4, 3
+    layers, tabs = [], []
+    for l in range(nl):
+        _, _, slot_expert = synth.make_slot_table(2, l)
+        resident = [e for e in slot_expert if e < shape.n_experts]
+        L = GpuLayer(2, l, shape, (synth.FMT_Q2SM, synth.FMT_Q3G)[l % 2], dev, resident=resident)
+        layers.append(L)
+        tabs.append(L.table)
+    tables = [torch.tensor(t, dtype=torch.int32, device=dev) for t in tabs]
+    x = synth.make_x(2, 0, T, shape.d_model).to(dev)
+    logits = [synth.zipf_gumbel_logits(2, l, T, shape.n_experts, c["zipf_s"], step=5).to(dev)
+              for l in range(nl)]
+    adds = [0.5 * synth.make_x(2, 200 + l, T, shape.d_model).to(dev) for l in range(nl)]
+    out = _run(layers, x, logits, tables, adds)
+    nm = out["n_miss"].cpu().numpy()
+    assert (nm[:, 1] > 0).all() and (nm[:, 1] < T * shape.top_k).all()   # hits and misses mixed
+    _check_against_oracle(layers, x, logits, adds, out, tabs)
