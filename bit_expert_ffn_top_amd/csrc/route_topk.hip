@@ -1,10 +1,9 @@
 // Router top-k, one wavefront per token: lane l holds the keys of experts
 // 64j + l (the 64-bit keys of the shared routing building blocks: value desc,
-// index asc, -0 as +0, NaN as -inf; all distinct), and k rounds each take the
-// wavefront's largest remaining key, so choice r is the key of rank r, as the
-// fused decode layer's selection (bound, candidates, their ranks) finds it.
-// The softmax over the k chosen logits is the shared one, so both give
-// identical bits.
+// index asc, -0 as +0, NaN as -inf; all distinct), and the fused decode
+// layer's selection (a bound from the lane maxima, the candidates at or above
+// it ranked among themselves) gives choice r = the key of rank r.  The softmax
+// over the k chosen logits is the shared one, so both give identical bits.
 #include "moe_internal.h"
 #include "route_device.h"
 
@@ -13,13 +12,12 @@ namespace {
 
 constexpr int kTokensPerBlock = 4;   // one wavefront each
 
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
 template <int M>   // keys per lane: E <= 64 * M
 __global__ __launch_bounds__(64 * kTokensPerBlock) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ idx,
     float* __restrict__ w) {
   __shared__ uint64_t top[kTokensPerBlock][MOE_MAX_TOPK];
+  __shared__ uint64_t scratch[kTokensPerBlock][128];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokensPerBlock + wave;
@@ -31,19 +29,7 @@ __global__ __launch_bounds__(64 * kTokensPerBlock) void route_topk_kernel(
     const int e = 64 * j + lane;
     key[j] = route_key(lg[min(e, E - 1)], e, e < E);
   }
-  uint64_t mine = 0;   // lane r < k: the key of rank r
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int j = 1; j < M; ++j) best = max_u64(best, key[j]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) best = max_u64(best, __shfl_xor(best, off, 64));
-    if (lane == r) mine = best;
-#pragma unroll
-    for (int j = 0; j < M; ++j) key[j] = key[j] == best ? 0 : key[j];   // keys are never 0
-  }
-  top[wave][lane] = mine;
-  __builtin_amdgcn_wave_barrier();
+  wave_topk_keys<M>(key, k, top[wave], scratch[wave]);
   int id;
   float wt;
   topk_softmax_lane(top[wave], k, lane, id, wt);
