@@ -216,31 +216,61 @@ __global__ __launch_bounds__(64) void group_scatter_kernel(
     const int32_t* __restrict__ table, int T, int k, int E, bool select_hits, int n_slots,
     const int32_t* __restrict__ chunk_start, const int32_t* __restrict__ starts,
     int32_t* __restrict__ perm, int32_t* __restrict__ pos, int32_t* __restrict__ group_slot) {
+  static_assert(MOE_MAX_TOPK <= 64, "a token's pairs in one step of the wavefront");
+  constexpr int kChunkPairs = kGroupChunkTokens * MOE_MAX_TOPK;
+  constexpr int kPerLane = kChunkPairs / 64;
   __shared__ int32_t cursor[kMaxE];
+  __shared__ int32_t s_start[kMaxE];     // each group's first position
+  __shared__ int32_t s_e[kChunkPairs];   // the chunk's experts and slots, in pair order
+  __shared__ int32_t s_s[kChunkPairs];
   const int chunk = blockIdx.x;
   const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64)
-    cursor[e] = starts[e] + chunk_start[static_cast<int64_t>(chunk) * E + e];
-  __syncthreads();
+  for (int e = lane; e < E; e += 64) {
+    const int st = starts[e];
+    s_start[e] = st;
+    cursor[e] = st + chunk_start[static_cast<int64_t>(chunk) * E + e];
+  }
   const int t0 = chunk * kGroupChunkTokens;
   const int t1 = min(T, t0 + kGroupChunkTokens);
-  for (int t = t0; t < t1; ++t) {
-    for (int i0 = 0; i0 < k; i0 += 64) {
-      const int i = i0 + lane;
-      if (i < k) {
-        const int p = t * k + i;
-        const int e = idx[p];
-        const int s = slot_of_pair ? slot_of_pair[p] : table[e];
-        int at = -1;
-        if (selected(s, select_hits, n_slots)) {
-          at = atomicAdd(&cursor[e], 1);
-          if (perm) perm[at] = p;
-          if (group_slot && at == starts[e]) group_slot[e] = s;   // the group's first pair
-        }
-        if (pos) pos[p] = at;
-      }
-      __syncthreads();
+  const int n = (t1 - t0) * k;                       // pairs of this chunk
+  const int64_t p0 = static_cast<int64_t>(t0) * k;
+  // every expert id and slot of the chunk requested at once (two rounds when
+  // the slots come from the table), then the ordered pass reads LDS only
+  int ev[kPerLane];
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) {
+    const int q = lane + 64 * j;
+    ev[j] = q < n ? idx[p0 + q] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) {
+    const int q = lane + 64 * j;
+    if (q < n) {
+      s_e[q] = ev[j];
+      s_s[q] = slot_of_pair ? slot_of_pair[p0 + q] : table[ev[j]];
     }
+  }
+  __syncthreads();
+  // Tokens in order (k <= 64: one token per step of the wavefront).  The
+  // workgroup is one wavefront, whose LDS accesses take effect in program
+  // order, so a later token's cursor increment follows an earlier one's
+  // without a barrier (a barrier here would also wait for every store).
+  for (int t = t0; t < t1; ++t) {
+    const int i = lane;
+    if (i < k) {
+      const int q = (t - t0) * k + i;
+      const int p = t * k + i;
+      const int e = s_e[q];
+      const int s = s_s[q];
+      int at = -1;
+      if (selected(s, select_hits, n_slots)) {
+        at = atomicAdd(&cursor[e], 1);
+        if (perm) perm[at] = p;
+        if (group_slot && at == s_start[e]) group_slot[e] = s;   // the group's first pair
+      }
+      if (pos) pos[p] = at;
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
